@@ -1,0 +1,255 @@
+"""Benchmark of the per-rank ZeRO-1/2 mixed-precision shard step on one MI355X.
+
+Workload: the Llama-3-8B shard (psi = 8.03e9 params over N = 8 ranks, so this
+rank owns 1,003,750,000 params), 8 fp16 replica gradient chunks in HBM,
+loss scale 65536, AdamW at t = 1000 with non-zero fp32 m and v.  Inputs are
+seeded synthetic draws made on the device before timing starts.
+
+One timed step is the whole per-rank path: zero the device flag and norm,
+overflow check (sum, mean, unscale, inf/NaN flag, squared norm), read the
+flag back, update the dynamic loss scale on the host, and run the fused
+update (moments, fp32 master, fp16 params) when the step is clean.
+
+Prints one JSON line.  `value` is params/s of the whole step.  `roofline`
+rates the fused update kernel, the dominant one, by its algorithmic bytes
+(2N + 24 + 2 per param) over its average duration measured with HIP events
+on the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+PMC_SUMMARY = os.path.join(PROFILE_DIR, "shard_step_kernel_llama3_8b_shard_pmc.txt")
+METRIC = "optimizer-shard params/s and achieved HBM GB/s (% of peak), 1 MI355X"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_shard")
+    ap.add_argument("--cpu-sample-slices", type=int, default=96,
+                    help="CPU baseline sample: this many slices of 2^22 params")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB fp32 copy kernel (counter calibration)")
+    ap.add_argument("--no-flatten", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def read_traffic(digest: str, n: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not m or m.group(1) != digest:
+        return None
+    vals = {}
+    for key in ("fetch_bytes_per_param", "write_bytes_per_param"):
+        mm = re.search(rf"^{key}:\s*([0-9.eE+-]+)", text, re.M)
+        if not mm:
+            return None
+        vals[key] = float(mm.group(1))
+    return (vals["fetch_bytes_per_param"] + vals["write_bytes_per_param"]) * n
+
+
+def cpu_baseline(dev_shard, w, slices: int):
+    """The CPU oracle as it stands, on the first `slices` x 2^22 params of the
+    shard (host copies of the device inputs), over a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle.zero_step as ozs
+
+    piece = 1 << 22
+    total = min(slices * piece, w.n)
+    host = dict(chunks=[c[:total].cpu().numpy() for c in dev_shard["chunks"]],
+                master=dev_shard["master"][:total].cpu().numpy(),
+                m=dev_shard["m"][:total].cpu().numpy(), v=dev_shard["v"][:total].cpu().numpy(),
+                p16=dev_shard["p16"][:total].cpu().numpy())
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+
+    def run(k):
+        sl = slice(k * piece, min((k + 1) * piece, total))
+        return ozs.shard_step([c[sl] for c in host["chunks"]], host["master"][sl],
+                              host["m"][sl], host["v"][sl], host["p16"][sl], w.hyper,
+                              w.loss_scale)
+
+    count = (total + piece - 1) // piece
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        results = list(ex.map(run, range(count)))
+    dt = time.perf_counter() - t0
+    assert not any(r.overflow for r in results)
+    return {"value": total / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"first {total} params of the {w.name} shard ({count} slices of 2^22, "
+                      f"N={w.n_replicas} replicas), full step incl. overflow check"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the shard step has no cross-GPU traffic here, "
+              f"so --gpus {args.gpus} is not supported (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sharded_mixed_precision_step_amd as zs
+    import workloads as wl
+    from sharded_mixed_precision_step_amd import _build
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    n, N = w.n, w.n_replicas
+    log(f"bench: workload={w.name} n={n} N={N} steps={args.steps} warmup={args.warmup}")
+    t0 = time.perf_counter()
+    d = wl.device_shard(w, dev)
+    torch.cuda.synchronize()
+    log(f"bench: inputs drawn on device in {time.perf_counter() - t0:.1f} s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, w, args.cpu_sample_slices)
+        log(f"bench: cpu oracle {cpu['value']:.3e} params/s on {cpu['cores']} threads "
+            f"({cpu['seconds']:.1f} s)")
+
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    sq = torch.zeros(1, dtype=torch.float64, device=dev)
+    scaler = zs.LossScaler.create(scale=w.loss_scale)
+    hp = zs.adamw_params(w.hyper)
+    stream = torch.cuda.current_stream()
+    k1_events, k2_events = [], []
+    skipped = 0
+
+    def step(record: bool):
+        nonlocal skipped
+        flag.zero_()
+        sq.zero_()
+        scale = scaler.scale
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+        zs.zero_overflow_check(d["chunks"], scale, flag, sq, stream=stream)
+        if record:
+            e[1].record(stream)
+        overflow = int(flag.item())
+        if zs.zero_update_loss_scale(scaler, overflow):
+            skipped += 1
+            return
+        if record:
+            e[2].record(stream)
+        zs.zero_shard_step(d["chunks"], scale, d["master"], d["m"], d["v"], d["p16"], hp,
+                           stream=stream)
+        if record:
+            e[3].record(stream)
+            k2_events.append((e[0], e[1]))
+            k1_events.append((e[2], e[3]))
+        hp.step += 1
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    k1_ms = sum(a.elapsed_time(b) for a, b in k1_events) / max(len(k1_events), 1)
+    k2_ms = sum(a.elapsed_time(b) for a, b in k2_events) / max(len(k2_events), 1)
+    log(f"bench: {ms_per_step:.3f} ms/step, fused step {k1_ms:.3f} ms, check {k2_ms:.3f} ms, "
+        f"skipped {skipped}")
+
+    k1_bytes = w.bytes_per_param_step() * n
+    k2_bytes = 2 * N * n
+    k1_gbps = k1_bytes / (k1_ms * 1e-3) / 1e9
+    traffic = read_traffic(_build.sources_digest(), n)
+    extra = {
+        "fused_step_ms": k1_ms, "fused_step_params_per_s": n / (k1_ms * 1e-3),
+        "fused_step_gbps": k1_gbps, "fused_step_pct_peak": 100 * k1_gbps / HBM_PEAK_GBPS,
+        "check_ms": k2_ms, "check_gbps": k2_bytes / (k2_ms * 1e-3) / 1e9,
+        "step_gbps": (k1_bytes + k2_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "skipped_steps": skipped,
+    }
+
+    if not args.no_flatten:
+        extra.update(bench_flatten(zs, wl, dev, stream))
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    out = {
+        "metric": METRIC,
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded device draws; fp16 grads, fp32 state)",
+        "config": {"workload": w.name, "shard_params": n, "replicas": N,
+                   "loss_scale": w.loss_scale, "adam_step": w.hyper.step,
+                   "bytes_per_param_fused_step": w.bytes_per_param_step(),
+                   "bytes_per_param_check": 2 * N},
+        "roofline": {"bound": "hbm", "achieved": k1_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": k1_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_flatten(zs, wl, dev, stream, reps: int = 10):
+    """Bucket flatten of the largest ZeRO-2 bucket (one 4096 x 14336 grad)."""
+    import torch
+    numel = wl.ZERO2_HIDDEN * wl.ZERO2_FFN
+    src = torch.empty(numel, dtype=torch.float16, device=dev)
+    wl.device_fill_normal(src, wl.seed_of(wl.ZERO2_WID, 0), 1e-4 * 65536.0)
+    pad = wl.ZERO2_ALIGN * wl.ZERO2_REPLICAS
+    L = (numel + pad - 1) // pad * pad
+    bucket = torch.empty(L, dtype=torch.float16, device=dev)
+    zs.zero_bucket_flatten([src], bucket, wl.ZERO2_ALIGN, pad, stream=stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        zs.zero_bucket_flatten([src], bucket, wl.ZERO2_ALIGN, pad, stream=stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    return {"flatten_ms": ms, "flatten_gbps": (2 * numel + 2 * L) / (ms * 1e-3) / 1e9}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * zero_step.h -- C ABI of the per-rank ZeRO-1/2 mixed-precision shard step
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * One rank owns 1/N of the flat parameter space.  After backward, the N
+ * ranks' fp16 gradients for that shard are reduced onto it as a mean, and the
+ * owner updates its fp32 optimizer state and fp32 master weights and writes
+ * its fp16 parameters (ZeRO notes, rkmt.cn/news/44736, section
+ * "Deepspeed ZeRO-1", steps 同步 (sync) and 更新 (update); section
+ * "Deepspeed ZeRO-2" updates each shard the same way after bucketed sync).
+ * Here the N replica gradient chunks are N arrays in local device memory, and
+ * the library performs the reduction arithmetic (a sum in fixed order, then
+ * the mean), the unscale, the overflow check and the Adam/AdamW update.
+ *
+ * Conventions for every call:
+ *  - Array pointers are DEVICE pointers owned by the caller; host pointers
+ *    are marked HOST.  The library never allocates, frees or keeps them.
+ *  - Device work is enqueued asynchronously on `stream` (a hipStream_t passed
+ *    as void*; NULL means the default stream); a call returns once enqueued.
+ *  - Arguments are validated completely before anything is enqueued: a
+ *    non-zero return means no device work was started by that call.
+ *  - An asynchronous kernel fault surfaces at the caller's next stream
+ *    synchronisation, or as ZERO_EHIP from a later call.
+ *  - n == 0 (or n_tensors == 0) is a valid no-op apart from output offsets;
+ *    array pointers are then not read and may be NULL (scalars are still
+ *    validated).
+ *  - Calls are thread-safe; zero_last_error_string() is per thread.
+ */
+#ifndef ZERO_STEP_H
+#define ZERO_STEP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_OK 0
+#define ZERO_EINVAL (-1)     /* bad value: null pointer, n < 0, n_chunks out of
+                                [1, ZERO_MAX_CHUNKS], loss_scale not finite and
+                                > 0, bad hyperparameters, overlapping outputs */
+#define ZERO_EALIGN (-2)     /* a pointer lacks the alignment stated below     */
+#define ZERO_ERANGE (-3)     /* bucket capacity below the padded bucket length */
+#define ZERO_EHIP (-4)       /* the HIP runtime reported an error              */
+#define ZERO_MAX_CHUNKS 64   /* largest N (replica gradient chunks)            */
+
+/* Adam / AdamW hyperparameters of one update (fp32, as the step uses them).
+ * The optimizer is Adam with bias correction (Kingma & Ba, Adam, Alg. 1), eps
+ * added after the square root; decoupled_wd = 1 applies weight decay as
+ * p <- p - lr*wd*p before the Adam term (Loshchilov & Hutter, AdamW, Alg. 2),
+ * decoupled_wd = 0 adds wd*p to the gradient instead (L2 Adam).
+ * Valid ranges: lr >= 0, 0 <= beta1, beta2 < 1, eps >= 0, weight_decay >= 0,
+ * all finite; step >= 1. */
+typedef struct zero_adamw_params {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+    int64_t step;            /* 1-based index t of THIS update; the caller
+                                advances it only after a step that was applied */
+    int32_t decoupled_wd;    /* 1 = AdamW, 0 = L2 Adam                          */
+    int32_t bias_correction; /* 1 = divide by 1 - beta^t, 0 = do not            */
+} zero_adamw_params;
+
+/* Dynamic loss-scale state, owned and stored by the caller (HOST memory). */
+typedef struct zero_loss_scaler {
+    float scale;             /* S, finite and > 0                               */
+    float growth_factor;     /* >= 1, e.g. 2                                    */
+    float backoff_factor;    /* in (0, 1], e.g. 0.5                             */
+    float min_scale;         /* > 0, floor of S                                 */
+    float max_scale;         /* >= min_scale, ceiling of S                      */
+    int32_t growth_interval; /* >= 1: clean steps in a row before S grows       */
+    int32_t good_steps;      /* clean steps since the last overflow or growth  */
+    int64_t skipped_steps;   /* total skipped steps                             */
+} zero_loss_scaler;
+
+/*
+ * zero_overflow_check -- overflow flag and squared norm of the unscaled mean
+ * gradient, without touching any optimizer state.
+ *
+ * For each j < n: s = chunk_0[j] + chunk_1[j] + ... + chunk_{N-1}[j] summed
+ * in fp32 in that order (the sum a ring scatter-reduce leaves on the owner,
+ * DP/DDP/FSDP walkthrough, pswp.cn/web/84187, section "DDP"), mean = s / N
+ * (ZeRO-1 sync: the owner holds the mean), g = mean / loss_scale (ZeRO-1
+ * update: convert to fp32, then scale).  If any g is +-inf or NaN, 1 is
+ * stored to *d_overflow; if d_sqnorm is not NULL, sum_j g_j^2 (each square
+ * exact in fp64, summed in fp64 in no fixed order) is ADDED to *d_sqnorm.
+ * Nothing else is written, so the caller zeroes both at the start of a step
+ * and several buckets of one step may accumulate into them.
+ *
+ *   grad_chunks  HOST array of n_chunks DEVICE pointers, each to n fp16
+ *                (IEEE binary16) values, 16-byte aligned
+ *   n_chunks     N, 1..ZERO_MAX_CHUNKS
+ *   n            elements per chunk, >= 0
+ *   loss_scale   S, finite and > 0
+ *   d_overflow   DEVICE int32, not NULL
+ *   d_sqnorm     DEVICE fp64 or NULL, 8-byte aligned
+ * Returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN or ZERO_EHIP.
+ */
+int zero_overflow_check(const void* const* grad_chunks, int32_t n_chunks,
+                        int64_t n, float loss_scale, int32_t* d_overflow,
+                        double* d_sqnorm, void* stream);
+
+/*
+ * zero_shard_step -- the fused update of one shard (or one bucket's shard).
+ *
+ * Computes g exactly as zero_overflow_check does, then for each j, in the
+ * order of the ZeRO-1 update step (moments, then fp32 master, then fp16
+ * params; ZeRO notes, rkmt.cn/news/44736, section "Deepspeed ZeRO-1"):
+ *   (L2 mode only) g <- g + wd*p
+ *   m  <- beta1*m + (1-beta1)*g            v <- beta2*v + ((1-beta2)*g)*g
+ *   m^ = m / (1 - beta1^t)                 v^ = v / (1 - beta2^t)
+ *   u  = m^ / (sqrt(v^) + eps)
+ *   p  <- (p - (lr*wd)*p) - lr*u           (AdamW; L2 mode: p <- p - lr*u)
+ *   param_fp16 <- p rounded to nearest-even binary16
+ * each operation one IEEE fp32 operation, 1 - beta^t evaluated in fp64 from
+ * the fp32 beta and rounded to fp32.  master, exp_avg and exp_avg_sq are
+ * updated in place.  If d_overflow / d_sqnorm are not NULL they accumulate
+ * the flag and squared norm as in zero_overflow_check.  The step itself does
+ * not skip: a caller that must leave the state untouched on overflow runs
+ * zero_overflow_check first and calls this only on a clean step.
+ *
+ *   grad_chunks  as for zero_overflow_check
+ *   master, exp_avg, exp_avg_sq
+ *                DEVICE fp32[n] each, 16-byte aligned, read and written
+ *   param_fp16   DEVICE fp16[n], 16-byte aligned, written only
+ *   hp           HOST, hyperparameters of this update
+ *   d_overflow   DEVICE int32 or NULL;  d_sqnorm DEVICE fp64 or NULL
+ * The four state arrays must not overlap each other or any chunk.
+ * Returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN or ZERO_EHIP.
+ */
+int zero_shard_step(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                    float loss_scale, float* master, float* exp_avg,
+                    float* exp_avg_sq, void* param_fp16,
+                    const zero_adamw_params* hp, int32_t* d_overflow,
+                    double* d_sqnorm, void* stream);
+
+/*
+ * zero_bucket_flatten -- pack whole fp16 gradient tensors into one bucket.
+ *
+ * Several parameters' gradients are grouped into a bucket and reduced as one
+ * unit (DP/DDP/FSDP walkthrough, pswp.cn/web/84187, section "DDP", bucket
+ * paragraph; ZeRO notes, section "Deepspeed ZeRO-2", sync step).  Tensor k is
+ * copied bit for bit to bucket[off_k .. off_k + numels[k]), where off_0 = 0
+ * and off_{k+1} = round_up(off_k + numels[k], align); the bucket length is
+ * L = round_up(off_last + numels[last], pad_multiple) (pad_multiple 0 or 1:
+ * no extra padding).  Every element of [0, L) not covered by a tensor is set
+ * to +0.  With pad_multiple = N * align the bucket splits into N equal,
+ * aligned shards.
+ *
+ *   tensors       HOST array of n_tensors DEVICE pointers to fp16 data, each
+ *                 2-byte aligned (views are fine); NULL only if its numel is 0
+ *   numels        HOST int64[n_tensors], each >= 0
+ *   n_tensors     >= 0
+ *   align         >= 1 (elements)
+ *   pad_multiple  >= 0 (elements)
+ *   bucket        DEVICE fp16, 16-byte aligned, bucket_capacity elements
+ *   offsets_out   HOST int64[n_tensors + 1]: off_0..off_{n-1}, then L
+ * Sources must not overlap the bucket.  Returns ZERO_OK, ZERO_EINVAL,
+ * ZERO_EALIGN, ZERO_ERANGE (capacity < L; offsets_out is still filled) or
+ * ZERO_EHIP.
+ */
+int zero_bucket_flatten(const void* const* tensors, const int64_t* numels,
+                        int32_t n_tensors, int64_t align, int64_t pad_multiple,
+                        void* bucket, int64_t bucket_capacity,
+                        int64_t* offsets_out, void* stream);
+
+/*
+ * zero_update_loss_scale -- host-only, synchronous dynamic loss scaling.
+ *
+ * The pages name the scaling step only (ZeRO-1 update: "scale"); this is the
+ * usual dynamic scheme.  Given the overflow flag the caller has read back
+ * for the step: on overflow the step is skipped (*skip_out = 1), S becomes
+ * max(S * backoff_factor, min_scale) and good_steps restarts at 0; on a clean
+ * step (*skip_out = 0) good_steps grows by one and, on reaching
+ * growth_interval, S becomes min(S * growth_factor, max_scale) and good_steps
+ * restarts.  All scale arithmetic is fp32.
+ *
+ *   s          HOST state, updated in place
+ *   overflow   0 = clean, anything else = overflow
+ *   skip_out   HOST int32, not NULL
+ * Returns ZERO_OK or ZERO_EINVAL (state left unchanged).
+ */
+int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_out);
+
+/* Text of the last error reported by a call on this thread ("" if none). */
+const char* zero_last_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_STEP_H */

@@ -1,0 +1,215 @@
+"""Python binding of libzerostep.so, the MI355X (gfx950) ZeRO-1/2 shard step.
+
+Argument marshalling only: tensors become raw device pointers, the current
+torch stream becomes a hipStream_t, and every call goes straight to the C ABI
+declared in include/zero_step.h.  All arithmetic of the step runs in the HIP
+kernels; nothing here computes on data.  If the library is missing the import
+fails loudly: there is no fallback path.
+
+torch is imported before the library is loaded so that the process holds a
+single HIP runtime (torch's libamdhip64.so.7 satisfies the library's
+dependency of the same soname) and torch's stream handles are valid for it.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch  # noqa: F401  (loads the HIP runtime first; see module docstring)
+
+from . import _build
+
+LIB_PATH = _build.LIB
+
+ZERO_OK = 0
+ZERO_EINVAL = -1
+ZERO_EALIGN = -2
+ZERO_ERANGE = -3
+ZERO_EHIP = -4
+ZERO_MAX_CHUNKS = 64
+
+EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_bucket_flatten",
+            "zero_update_loss_scale", "zero_last_error_string")
+
+
+class ZeroStepError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class AdamWParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64),
+                ("decoupled_wd", ctypes.c_int32), ("bias_correction", ctypes.c_int32)]
+
+
+class LossScaler(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("growth_factor", ctypes.c_float),
+                ("backoff_factor", ctypes.c_float), ("min_scale", ctypes.c_float),
+                ("max_scale", ctypes.c_float), ("growth_interval", ctypes.c_int32),
+                ("good_steps", ctypes.c_int32), ("skipped_steps", ctypes.c_int64)]
+
+    @classmethod
+    def create(cls, scale=65536.0, growth_factor=2.0, backoff_factor=0.5,
+               min_scale=1.0, max_scale=float(2 ** 24), growth_interval=1000):
+        return cls(scale, growth_factor, backoff_factor, min_scale, max_scale,
+                   growth_interval, 0, 0)
+
+
+def adamw_params(hyper) -> AdamWParams:
+    """AdamWParams from any object with lr, beta1, beta2, eps, weight_decay,
+    step, decoupled_wd and bias_correction attributes."""
+    return AdamWParams(hyper.lr, hyper.beta1, hyper.beta2, hyper.eps,
+                       hyper.weight_decay, int(hyper.step), int(bool(hyper.decoupled_wd)),
+                       int(bool(getattr(hyper, "bias_correction", True))))
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    lib.zero_overflow_check.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp]
+    lib.zero_shard_step.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp, vp,
+                                    ctypes.POINTER(AdamWParams), vp, vp, vp]
+    lib.zero_bucket_flatten.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), i32, i64, i64,
+                                        vp, i64, ctypes.POINTER(ctypes.c_int64), vp]
+    lib.zero_update_loss_scale.argtypes = [ctypes.POINTER(LossScaler), i32,
+                                           ctypes.POINTER(ctypes.c_int32)]
+    lib.zero_last_error_string.argtypes = []
+    lib.zero_last_error_string.restype = ctypes.c_char_p
+    for name in EXPORTED[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != ZERO_OK:
+        raise ZeroStepError(rc, lib.zero_last_error_string().decode())
+
+
+def _ptr_array(ptrs: Sequence[int]):
+    arr = (ctypes.c_void_p * max(len(ptrs), 1))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _opt(t: Optional[torch.Tensor], dtype: torch.dtype, name: str) -> Optional[int]:
+    return None if t is None else _dev(t, dtype, name)
+
+
+def zero_overflow_check(grad_chunks: Sequence[torch.Tensor], loss_scale: float,
+                        d_overflow: torch.Tensor, d_sqnorm: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """OR the non-finite flag of g = (sum chunks / N) / loss_scale into
+    d_overflow (int32[1]) and add sum g^2 to d_sqnorm (float64[1])."""
+    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+    n = grad_chunks[0].numel() if grad_chunks else 0
+    for i, c in enumerate(grad_chunks):
+        if c.numel() != n:
+            raise ValueError(f"grad_chunks[{i}] has {c.numel()} elements, expected {n}")
+    _check(lib.zero_overflow_check(_ptr_array(ptrs), len(ptrs), n, float(loss_scale),
+                                   _dev(d_overflow, torch.int32, "d_overflow"),
+                                   _opt(d_sqnorm, torch.float64, "d_sqnorm"), _stream(stream)))
+
+
+def zero_shard_step(grad_chunks: Sequence[torch.Tensor], loss_scale: float,
+                    master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                    param_fp16: torch.Tensor, hp: AdamWParams,
+                    d_overflow: Optional[torch.Tensor] = None,
+                    d_sqnorm: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Fused Adam/AdamW update of one shard in place (see zero_step.h)."""
+    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+    n = master.numel()
+    for name, t in (("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq),
+                    ("param_fp16", param_fp16), *[(f"grad_chunks[{i}]", c)
+                                                  for i, c in enumerate(grad_chunks)]):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    if not isinstance(hp, AdamWParams):
+        hp = adamw_params(hp)
+    _check(lib.zero_shard_step(
+        _ptr_array(ptrs), len(ptrs), n, float(loss_scale),
+        _dev(master, torch.float32, "master"), _dev(exp_avg, torch.float32, "exp_avg"),
+        _dev(exp_avg_sq, torch.float32, "exp_avg_sq"),
+        _dev(param_fp16, torch.float16, "param_fp16"), ctypes.byref(hp),
+        _opt(d_overflow, torch.int32, "d_overflow"), _opt(d_sqnorm, torch.float64, "d_sqnorm"),
+        _stream(stream)))
+
+
+def zero_bucket_flatten(tensors: Sequence[torch.Tensor], bucket: torch.Tensor,
+                        align: int = 256, pad_multiple: int = 0, stream=None) -> list:
+    """Pack fp16 tensors into ``bucket``; returns the offsets and padded length."""
+    ptrs, numels = [], []
+    for i, t in enumerate(tensors):
+        ptrs.append(_dev(t, torch.float16, f"tensors[{i}]") if t.numel() else 0)
+        numels.append(t.numel())
+    nt = len(ptrs)
+    numel_arr = (ctypes.c_int64 * max(nt, 1))(*numels)
+    offs = (ctypes.c_int64 * (nt + 1))()
+    _check(lib.zero_bucket_flatten(_ptr_array(ptrs), numel_arr, nt, int(align), int(pad_multiple),
+                                   _dev(bucket, torch.float16, "bucket"), bucket.numel(), offs,
+                                   _stream(stream)))
+    return list(offs)
+
+
+def zero_update_loss_scale(scaler: LossScaler, overflow: int) -> bool:
+    """Advance the dynamic loss scale after a step; True means skip the step."""
+    skip = ctypes.c_int32(0)
+    _check(lib.zero_update_loss_scale(ctypes.byref(scaler), int(overflow), ctypes.byref(skip)))
+    return bool(skip.value)
+
+
+@dataclasses.dataclass
+class ShardStepResult:
+    overflow: bool
+    skipped: bool
+    sqnorm: float
+
+
+def checked_step(grad_chunks, master, exp_avg, exp_avg_sq, param_fp16, hp: AdamWParams,
+                 scaler: LossScaler, d_overflow: torch.Tensor, d_sqnorm: torch.Tensor,
+                 stream=None) -> ShardStepResult:
+    """One clean-or-skipped step as a rank runs it: check, read the flag back,
+    update the loss scale, then update the shard only if the step is clean.
+    d_overflow and d_sqnorm are caller-owned device scalars (zeroed here);
+    hp.step is advanced on a clean step."""
+    d_overflow.zero_()
+    d_sqnorm.zero_()
+    scale = scaler.scale
+    zero_overflow_check(grad_chunks, scale, d_overflow, d_sqnorm, stream=stream)
+    flag = int(d_overflow.item())          # device -> host: the skip decision
+    skip = zero_update_loss_scale(scaler, flag)
+    if not skip:
+        zero_shard_step(grad_chunks, scale, master, exp_avg, exp_avg_sq, param_fp16, hp,
+                        stream=stream)
+        hp.step += 1
+    return ShardStepResult(bool(flag), skip, float(d_sqnorm.item()))

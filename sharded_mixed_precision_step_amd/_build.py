@@ -1,0 +1,78 @@
+"""Build of libzerostep.so: the gfx950 kernels and the C-ABI host layer.
+
+hipcc cross-compiles for gfx950 on any host, so this runs without a GPU.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+INCLUDE = os.path.join(ROOT, "include")
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libzerostep.so")
+SOURCES = [os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_abi.cpp")]
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # every fp32 operation separately rounded, as the step is defined
+    "-ffp-contract=off",
+    # no packed fp32 arithmetic in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def sources_digest() -> str:
+    """SHA-256 over the library's sources and header."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(SOURCES + [os.path.join(CSRC, "zero_internal.h"),
+                               os.path.join(INCLUDE, "zero_step.h")]):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 into libzerostep.so (atomically)."""
+    fd, tmp = tempfile.mkstemp(prefix=".libzerostep.", suffix=".so.tmp", dir=HERE)
+    os.close(fd)
+    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+        if verbose and res.stderr.strip():
+            print(res.stderr, flush=True)
+        os.replace(tmp, LIB)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return LIB
+
+
+def ensure_built() -> str:
+    """Build only if no library is present."""
+    if not os.path.exists(LIB):
+        build()
+    return LIB

@@ -1,0 +1,262 @@
+// C-ABI host layer: argument validation, per-step scalars, launches, errors,
+// and the host-only dynamic loss-scale state machine.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "zero_internal.h"
+#include "zero_step.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_error[0] = '\0';
+    return ZERO_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(ZERO_EHIP, "%s: HIP error %d (%s)", where, static_cast<int>(e),
+                hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool finite_f(float x) { return isfinite(x) != 0; }
+
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + static_cast<uintptr_t>(nb) &&
+           y < x + static_cast<uintptr_t>(na);
+}
+
+bool is_pow2(float x) {
+    int e = 0;
+    return x > 0.0f && frexpf(x, &e) == 0.5f;
+}
+
+int check_chunks(const void* const* grad_chunks, int32_t n_chunks, int64_t n, float loss_scale,
+                 zero::ChunkTable* table, zero::GradScalars* gs) {
+    if (!grad_chunks) return fail(ZERO_EINVAL, "grad_chunks is NULL");
+    if (n_chunks < 1 || n_chunks > ZERO_MAX_CHUNKS)
+        return fail(ZERO_EINVAL, "n_chunks = %d outside [1, %d]", n_chunks, ZERO_MAX_CHUNKS);
+    if (n < 0) return fail(ZERO_EINVAL, "n = %lld < 0", static_cast<long long>(n));
+    if (!finite_f(loss_scale) || !(loss_scale > 0.0f))
+        return fail(ZERO_EINVAL, "loss_scale = %g is not finite and > 0",
+                    static_cast<double>(loss_scale));
+    memset(table, 0, sizeof *table);
+    if (n == 0) return ZERO_OK;  // nothing is read: empty (NULL) chunks are fine
+    for (int32_t c = 0; c < n_chunks; ++c) {
+        if (!grad_chunks[c]) return fail(ZERO_EINVAL, "grad_chunks[%d] is NULL", c);
+        if (!aligned(grad_chunks[c], 16))
+            return fail(ZERO_EALIGN, "grad_chunks[%d] is not 16-byte aligned", c);
+        table->p[c] = static_cast<const uint16_t*>(grad_chunks[c]);
+    }
+    gs->n_f = static_cast<float>(n_chunks);
+    gs->inv_n = 1.0f / gs->n_f;
+    gs->mean_by_mul = is_pow2(gs->n_f) ? 1 : 0;
+    gs->s = loss_scale;
+    gs->inv_s = 1.0f / loss_scale;
+    gs->unscale_by_mul = (is_pow2(loss_scale) && finite_f(gs->inv_s)) ? 1 : 0;
+    return ZERO_OK;
+}
+
+int check_flag_ptrs(const int32_t* d_overflow, const double* d_sqnorm) {
+    if (d_overflow && !aligned(d_overflow, 4))
+        return fail(ZERO_EALIGN, "d_overflow is not 4-byte aligned");
+    if (d_sqnorm && !aligned(d_sqnorm, 8)) return fail(ZERO_EALIGN, "d_sqnorm is not 8-byte aligned");
+    return ZERO_OK;
+}
+
+int adam_scalars(const zero_adamw_params* hp, zero::AdamScalars* as) {
+    if (!hp) return fail(ZERO_EINVAL, "hp is NULL");
+    const float vals[5] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+    for (float x : vals)
+        if (!finite_f(x)) return fail(ZERO_EINVAL, "a hyperparameter is not finite");
+    if (hp->lr < 0.0f) return fail(ZERO_EINVAL, "lr < 0");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f)) return fail(ZERO_EINVAL, "beta1 outside [0, 1)");
+    if (!(hp->beta2 >= 0.0f && hp->beta2 < 1.0f)) return fail(ZERO_EINVAL, "beta2 outside [0, 1)");
+    if (hp->eps < 0.0f) return fail(ZERO_EINVAL, "eps < 0");
+    if (hp->weight_decay < 0.0f) return fail(ZERO_EINVAL, "weight_decay < 0");
+    if (hp->step < 1) return fail(ZERO_EINVAL, "step = %lld < 1", static_cast<long long>(hp->step));
+    as->beta1 = hp->beta1;
+    as->beta2 = hp->beta2;
+    as->c1 = 1.0f - hp->beta1;
+    as->c2 = 1.0f - hp->beta2;
+    if (hp->bias_correction) {
+        const double t = static_cast<double>(hp->step);
+        as->bc1 = static_cast<float>(1.0 - pow(static_cast<double>(hp->beta1), t));
+        // beta <= 1 - 2^-24 keeps 1 - beta^t >= 2^-24 > 0 for every t >= 1
+        as->bc2 = static_cast<float>(1.0 - pow(static_cast<double>(hp->beta2), t));
+    } else {
+        as->bc1 = 1.0f;
+        as->bc2 = 1.0f;
+    }
+    as->eps = hp->eps;
+    as->lr = hp->lr;
+    as->wd = hp->weight_decay;
+    as->lrwd = hp->lr * hp->weight_decay;
+    as->decoupled = hp->decoupled_wd ? 1 : 0;
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zero_last_error_string(void) { return g_error; }
+
+int zero_overflow_check(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                        float loss_scale, int32_t* d_overflow, double* d_sqnorm, void* stream) {
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    int rc = check_chunks(grad_chunks, n_chunks, n, loss_scale, &table, &gs);
+    if (rc) return rc;
+    if (!d_overflow) return fail(ZERO_EINVAL, "d_overflow is NULL");
+    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
+    if (n == 0) return ok();
+    const hipError_t e = zero::launch_overflow_check(table, n_chunks, n, gs, d_overflow, d_sqnorm,
+                                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "zero_overflow_check launch");
+}
+
+int zero_shard_step(const void* const* grad_chunks, int32_t n_chunks, int64_t n, float loss_scale,
+                    float* master, float* exp_avg, float* exp_avg_sq, void* param_fp16,
+                    const zero_adamw_params* hp, int32_t* d_overflow, double* d_sqnorm,
+                    void* stream) {
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    zero::AdamScalars as;
+    int rc = check_chunks(grad_chunks, n_chunks, n, loss_scale, &table, &gs);
+    if (rc) return rc;
+    if ((rc = adam_scalars(hp, &as))) return rc;
+    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
+    if (n == 0) return ok();  // nothing is read or written
+    if (!master || !exp_avg || !exp_avg_sq || !param_fp16)
+        return fail(ZERO_EINVAL, "a state pointer (master, exp_avg, exp_avg_sq, param_fp16) is NULL");
+    if (!aligned(master, 16) || !aligned(exp_avg, 16) || !aligned(exp_avg_sq, 16) ||
+        !aligned(param_fp16, 16))
+        return fail(ZERO_EALIGN, "a state pointer is not 16-byte aligned");
+    const void* state[4] = {master, exp_avg, exp_avg_sq, param_fp16};
+    const int64_t bytes[4] = {4 * n, 4 * n, 4 * n, 2 * n};
+    static const char* names[4] = {"master", "exp_avg", "exp_avg_sq", "param_fp16"};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(state[a], bytes[a], state[b], bytes[b]))
+                return fail(ZERO_EINVAL, "%s overlaps %s", names[a], names[b]);
+        for (int32_t c = 0; c < n_chunks; ++c)
+            if (overlap(state[a], bytes[a], grad_chunks[c], 2 * n))
+                return fail(ZERO_EINVAL, "%s overlaps grad_chunks[%d]", names[a], c);
+    }
+    const hipError_t e = zero::launch_shard_step(
+        table, n_chunks, n, gs, as, master, exp_avg, exp_avg_sq, static_cast<uint16_t*>(param_fp16),
+        d_overflow, d_sqnorm, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "zero_shard_step launch");
+}
+
+int zero_bucket_flatten(const void* const* tensors, const int64_t* numels, int32_t n_tensors,
+                        int64_t align, int64_t pad_multiple, void* bucket, int64_t bucket_capacity,
+                        int64_t* offsets_out, void* stream) {
+    if (n_tensors < 0) return fail(ZERO_EINVAL, "n_tensors < 0");
+    if (n_tensors > 0 && (!tensors || !numels))
+        return fail(ZERO_EINVAL, "tensors or numels is NULL");
+    if (!offsets_out) return fail(ZERO_EINVAL, "offsets_out is NULL");
+    if (align < 1) return fail(ZERO_EINVAL, "align < 1");
+    if (pad_multiple < 0) return fail(ZERO_EINVAL, "pad_multiple < 0");
+    if (bucket_capacity < 0) return fail(ZERO_EINVAL, "bucket_capacity < 0");
+    const int64_t kLimit = INT64_MAX / 4;
+    int64_t end = 0;
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        if (numels[k] < 0) return fail(ZERO_EINVAL, "numels[%d] < 0", k);
+        if (numels[k] > 0 && !tensors[k]) return fail(ZERO_EINVAL, "tensors[%d] is NULL", k);
+        if (numels[k] > 0 && !aligned(tensors[k], 2))
+            return fail(ZERO_EALIGN, "tensors[%d] is not 2-byte aligned", k);
+        const int64_t start = (end + align - 1) / align * align;
+        if (start > kLimit || numels[k] > kLimit - start)
+            return fail(ZERO_EINVAL, "bucket length overflows");
+        offsets_out[k] = start;
+        end = start + numels[k];
+    }
+    const int64_t total = pad_multiple > 1 ? (end + pad_multiple - 1) / pad_multiple * pad_multiple : end;
+    offsets_out[n_tensors] = total;
+    if (total > 0 && !bucket) return fail(ZERO_EINVAL, "bucket is NULL");
+    if (total > 0 && !aligned(bucket, 16)) return fail(ZERO_EALIGN, "bucket is not 16-byte aligned");
+    if (total > bucket_capacity)
+        return fail(ZERO_ERANGE, "bucket needs %lld elements, capacity is %lld",
+                    static_cast<long long>(total), static_cast<long long>(bucket_capacity));
+    for (int32_t k = 0; k < n_tensors; ++k)
+        if (overlap(tensors[k], 2 * numels[k], bucket, 2 * total))
+            return fail(ZERO_EINVAL, "tensors[%d] overlaps the bucket", k);
+    if (total == 0) return ok();
+    // Slots: tensor k owns [off_k, off_{k+1}); the last slot runs to the padded end.
+    // A bucket with no tensors (all numels 0 and total 0) returned above.
+    zero::FlattenTable table;
+    memset(&table, 0, sizeof table);
+    int count = 0;
+    int64_t max_slot = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        const int64_t next = k + 1 < n_tensors ? offsets_out[k + 1] : total;
+        zero::FlattenDesc& d = table.d[count];
+        d.src = static_cast<const uint16_t*>(tensors[k]);
+        d.numel = numels[k];
+        d.dst_off = offsets_out[k];
+        d.slot_len = next - offsets_out[k];
+        d.vec = (d.dst_off % zero::kPack == 0 && d.slot_len % zero::kPack == 0) ? 1 : 0;
+        if (d.slot_len > max_slot) max_slot = d.slot_len;
+        if (d.slot_len > 0) ++count;
+        if (count == zero::kFlattenBatch || (k + 1 == n_tensors && count > 0)) {
+            const hipError_t e = zero::launch_bucket_flatten(
+                table, count, max_slot, static_cast<uint16_t*>(bucket), st);
+            if (e != hipSuccess) return hip_fail(e, "zero_bucket_flatten launch");
+            memset(&table, 0, sizeof table);
+            count = 0;
+            max_slot = 0;
+        }
+    }
+    return ok();
+}
+
+int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_out) {
+    if (!s || !skip_out) return fail(ZERO_EINVAL, "scaler or skip_out is NULL");
+    if (!finite_f(s->scale) || !(s->scale > 0.0f)) return fail(ZERO_EINVAL, "scale not finite and > 0");
+    if (!finite_f(s->growth_factor) || !(s->growth_factor >= 1.0f))
+        return fail(ZERO_EINVAL, "growth_factor < 1");
+    if (!(s->backoff_factor > 0.0f && s->backoff_factor <= 1.0f))
+        return fail(ZERO_EINVAL, "backoff_factor outside (0, 1]");
+    if (!finite_f(s->min_scale) || !(s->min_scale > 0.0f)) return fail(ZERO_EINVAL, "min_scale <= 0");
+    if (!finite_f(s->max_scale) || !(s->max_scale >= s->min_scale))
+        return fail(ZERO_EINVAL, "max_scale < min_scale");
+    if (s->growth_interval < 1) return fail(ZERO_EINVAL, "growth_interval < 1");
+    if (s->good_steps < 0) return fail(ZERO_EINVAL, "good_steps < 0");
+    if (overflow) {
+        const float backed = s->scale * s->backoff_factor;
+        s->scale = backed > s->min_scale ? backed : s->min_scale;
+        s->good_steps = 0;
+        s->skipped_steps += 1;
+        *skip_out = 1;
+        return ok();
+    }
+    s->good_steps += 1;
+    if (s->good_steps >= s->growth_interval) {
+        const float grown = s->scale * s->growth_factor;
+        s->scale = grown < s->max_scale ? grown : s->max_scale;
+        s->good_steps = 0;
+    }
+    *skip_out = 0;
+    return ok();
+}
+
+}  // extern "C"

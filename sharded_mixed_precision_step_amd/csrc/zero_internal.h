@@ -1,0 +1,74 @@
+// Internal interface between the C-ABI host layer (zero_abi.cpp) and the
+// gfx950 kernels (zero_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_step.h"
+
+namespace zero {
+
+constexpr int kBlock = 256;        // threads per workgroup: four 64-wide waves
+constexpr int kPack = 8;           // params per thread per iteration: 16 B of fp16
+constexpr int kFlattenBatch = 32;  // tensors per flatten launch (kernel-argument table)
+
+// Replica gradient chunks, passed by value in the kernel arguments.
+struct ChunkTable {
+    const uint16_t* p[ZERO_MAX_CHUNKS];
+};
+
+// Scalars of the mean (s / N) and the unscale (mean / S).  When N (or S) is a
+// power of two whose reciprocal is a finite fp32 value, multiplying by the
+// reciprocal rounds the same exact quotient and so gives the same bits as the
+// division; otherwise the kernel divides.
+struct GradScalars {
+    float n_f;
+    float inv_n;
+    float s;
+    float inv_s;
+    int32_t mean_by_mul;
+    int32_t unscale_by_mul;
+};
+
+// Per-update Adam scalars, computed once on the host in fp32 (bias
+// corrections in fp64, then rounded).
+struct AdamScalars {
+    float beta1, beta2;
+    float c1, c2;      // 1 - beta1, 1 - beta2 (exact fp32 subtractions)
+    float bc1, bc2;    // 1 - beta^t, or 1 without bias correction
+    float eps;
+    float lr;
+    float wd;
+    float lrwd;        // lr * wd
+    int32_t decoupled;
+};
+
+struct FlattenDesc {
+    const uint16_t* src;  // fp16 bits, 2-byte aligned
+    int64_t numel;        // elements of the tensor
+    int64_t dst_off;      // slot start in the bucket (elements)
+    int64_t slot_len;     // slot length: tensor plus the zero gap after it
+    int32_t vec;          // dst_off and slot_len are multiples of 8
+    int32_t pad_;
+};
+
+struct FlattenTable {
+    FlattenDesc d[kFlattenBatch];
+};
+
+hipError_t launch_overflow_check(const ChunkTable& chunks, int n_chunks, int64_t n,
+                                 const GradScalars& gs, int32_t* d_overflow,
+                                 double* d_sqnorm, hipStream_t stream);
+
+hipError_t launch_shard_step(const ChunkTable& chunks, int n_chunks, int64_t n,
+                             const GradScalars& gs, const AdamScalars& as,
+                             float* master, float* exp_avg, float* exp_avg_sq,
+                             uint16_t* param_fp16, int32_t* d_overflow,
+                             double* d_sqnorm, hipStream_t stream);
+
+hipError_t launch_bucket_flatten(const FlattenTable& table, int count,
+                                 int64_t max_slot_len, uint16_t* bucket,
+                                 hipStream_t stream);
+
+}  // namespace zero

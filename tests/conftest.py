@@ -21,3 +21,9 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_sessionstart(session):
+    # Tests load the built library; build it only when none is present.
+    from sharded_mixed_precision_step_amd import _build
+    _build.ensure_built()

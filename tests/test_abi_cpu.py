@@ -1,0 +1,170 @@
+"""The C ABI on the host: the library loads, exports what the header
+declares, rejects bad arguments before any launch, and its host-only loss
+scaler walks the same states as the oracle's.  No device work runs here:
+every call below either fails validation or is host-only."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.loss_scale as ols
+import sharded_mixed_precision_step_amd as zs
+
+pytestmark = pytest.mark.cpu
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "zero_step.h")
+
+A = 0x7f0000001000          # a 16-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(zs.EXPORTED)
+    lib = ctypes.CDLL(zs.LIB_PATH)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_single_hip_runtime_in_process():
+    maps = [ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln]
+    assert len(set(maps)) == 1, set(maps)
+
+
+def _ptrs(*p):
+    return zs._ptr_array(list(p))
+
+
+def _check(*args):
+    return zs.lib.zero_overflow_check(*args)
+
+
+def _step(chunks, n_chunks, n, scale, master, m, v, p16, hp, flag=None, sq=None):
+    return zs.lib.zero_shard_step(chunks, n_chunks, n, scale, master, m, v, p16,
+                                  ctypes.byref(hp) if hp is not None else None, flag, sq, None)
+
+
+def _hp(**kw):
+    d = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1,
+             decoupled_wd=1, bias_correction=1)
+    d.update(kw)
+    return zs.AdamWParams(**d)
+
+
+def _last():
+    return zs.lib.zero_last_error_string().decode()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 3, 10, 1024.0, A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, A, A), 0, 10, 1024.0, A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(*[A] * 65), 65, 10, 1024.0, A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, A, A), 3, -1, 1024.0, A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, A, A), 3, 10, 0.0, A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, A, A), 3, 10, float("inf"), A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, A, A), 3, 10, float("nan"), A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, A, A), 3, 10, -2.0, A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, 0, A), 3, 10, 1024.0, A, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, A + 2, A), 3, 10, 1024.0, A, None, None), zs.ZERO_EALIGN),
+    ((_ptrs(A, A, A), 3, 10, 1024.0, None, None, None), zs.ZERO_EINVAL),
+    ((_ptrs(A, A, A), 3, 10, 1024.0, A + 2, None, None), zs.ZERO_EALIGN),
+    ((_ptrs(A, A, A), 3, 10, 1024.0, A, A + 4, None), zs.ZERO_EALIGN),
+])
+def test_overflow_check_rejects(args, code):
+    assert _check(*args) == code
+    assert _last()
+
+
+def test_zero_length_is_a_noop():
+    assert _check(_ptrs(A, A, A), 3, 0, 1024.0, A, None, None) == zs.ZERO_OK
+    assert _last() == ""
+    assert _step(_ptrs(A, A), 2, 0, 1.0, A, A + 4096, A + 8192, A + 12288, _hp()) == zs.ZERO_OK
+    # with n == 0 no array is read, so empty (NULL) arrays are accepted ...
+    assert _check(_ptrs(0, 0), 2, 0, 4.0, A, None, None) == zs.ZERO_OK
+    assert _step(_ptrs(0), 1, 0, 1.0, None, None, None, None, _hp()) == zs.ZERO_OK
+    # ... but scalars are still checked
+    assert _step(_ptrs(0), 1, 0, 1.0, None, None, None, None, _hp(step=0)) == zs.ZERO_EINVAL
+    assert _check(_ptrs(0, 0), 2, 0, -4.0, A, None, None) == zs.ZERO_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(lr=-1e-3), dict(beta1=1.0), dict(beta1=-0.1), dict(beta2=1.0), dict(eps=-1.0),
+    dict(weight_decay=-0.01), dict(step=0), dict(lr=float("nan")), dict(eps=float("inf")),
+])
+def test_shard_step_rejects_hyperparameters(kw):
+    B = A + (1 << 20)
+    rc = _step(_ptrs(A, A), 2, 16, 1024.0, B, B + 4096, B + 8192, B + 12288, _hp(**kw))
+    assert rc == zs.ZERO_EINVAL, (kw, _last())
+
+
+def test_shard_step_rejects_bad_state():
+    B = A + (1 << 20)
+    n = 1000
+    good = (B, B + 4 * n, B + 8 * n, B + 12 * n)
+    assert _step(_ptrs(A), 1, n, 1.0, *good[:3], None, _hp()) == zs.ZERO_EINVAL
+    assert _step(_ptrs(A), 1, n, 1.0, good[0] + 8, *good[1:], _hp()) == zs.ZERO_EALIGN
+    assert _step(_ptrs(A), 1, n, 1.0, good[0], good[0] + 16, *good[2:], _hp()) == zs.ZERO_EINVAL
+    assert "overlaps" in _last()
+    # a chunk overlapping the master weights
+    assert _step(_ptrs(B + 16), 1, n, 1.0, *good, _hp()) == zs.ZERO_EINVAL
+    assert _step(_ptrs(A), 1, n, 1.0, *good, None) == zs.ZERO_EINVAL
+    assert _step(_ptrs(A), 1, n, 1.0, *good, _hp(), A + 2) == zs.ZERO_EALIGN
+
+
+def _flatten(ptrs, numels, align, pad, bucket, cap):
+    nt = len(numels)
+    offs = (ctypes.c_int64 * (nt + 1))()
+    rc = zs.lib.zero_bucket_flatten(_ptrs(*ptrs) if ptrs else None,
+                                    (ctypes.c_int64 * max(nt, 1))(*numels), nt, align, pad,
+                                    bucket, cap, offs, None)
+    return rc, list(offs)
+
+
+def test_flatten_validation_and_layout():
+    B = A + (1 << 24)
+    assert _flatten([], [], 256, 512, B, 0) == (zs.ZERO_OK, [0])
+    assert _flatten([A, A + 4096], [0, 0], 256, 512, B, 0) == (zs.ZERO_OK, [0, 0, 0])
+    rc, offs = _flatten([A, A + 4096, A + 8192], [5, 300, 1], 256, 512, B, 1000)
+    assert rc == zs.ZERO_ERANGE and offs == [0, 256, 768, 1024]
+    assert _flatten([A], [5], 256, 512, B + 8, 4096)[0] == zs.ZERO_EALIGN
+    assert _flatten([A + 1], [5], 256, 512, B, 4096)[0] == zs.ZERO_EALIGN
+    assert _flatten([A], [-5], 256, 512, B, 4096)[0] == zs.ZERO_EINVAL
+    assert _flatten([0], [5], 256, 512, B, 4096)[0] == zs.ZERO_EINVAL
+    assert _flatten([A], [5], 0, 512, B, 4096)[0] == zs.ZERO_EINVAL
+    assert _flatten([B + 64], [5], 256, 512, B, 4096)[0] == zs.ZERO_EINVAL   # source inside bucket
+
+
+def test_scaler_matches_oracle_on_forced_sequences():
+    rng = np.random.default_rng(11)
+    for interval in (1, 3, 1000):
+        for trial in range(20):
+            flags = rng.random(60) < rng.choice([0.05, 0.3, 0.8])
+            c = zs.LossScaler.create(scale=65536.0, growth_interval=interval,
+                                     min_scale=4.0, max_scale=2.0 ** 18)
+            o = ols.ScalerState(scale=65536.0, growth_interval=interval, min_scale=4.0,
+                                max_scale=2.0 ** 18)
+            for f in flags:
+                assert zs.zero_update_loss_scale(c, int(f)) == ols.update_loss_scale(o, bool(f))
+                assert (c.scale, c.good_steps, c.skipped_steps) == (o.scale, o.good_steps,
+                                                                    o.skipped_steps)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("scale", 0.0), ("scale", float("inf")), ("growth_factor", 0.5), ("backoff_factor", 0.0),
+    ("backoff_factor", 1.5), ("min_scale", 0.0), ("max_scale", 0.5), ("growth_interval", 0),
+])
+def test_scaler_rejects(field, value):
+    s = zs.LossScaler.create()
+    setattr(s, field, value)
+    before = bytes(s)
+    with pytest.raises(zs.ZeroStepError) as e:
+        zs.zero_update_loss_scale(s, 1)
+    assert e.value.code == zs.ZERO_EINVAL and bytes(s) == before
