@@ -25,5 +25,5 @@ def golden_dir():
 
 def pytest_sessionstart(session):
     # Tests load the built library; build it only when none is present.
-    from sharded_mixed_precision_step_amd import _build
-    _build.ensure_built()
+    import __graft_entry__
+    __graft_entry__._build_module().ensure_built()
