@@ -41,8 +41,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b_shard")
-    ap.add_argument("--cpu-sample-slices", type=int, default=96,
-                    help="CPU baseline sample: this many slices of 2^22 params")
+    ap.add_argument("--cpu-sample-slices", type=int, default=0,
+                    help="CPU baseline sample: this many slices of 2^22 params "
+                         "(0: the whole shard)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration)")
@@ -60,7 +61,7 @@ def read_traffic(digest: str, n: int):
     if not os.path.exists(PMC_SUMMARY):
         return None
     text = open(PMC_SUMMARY).read()
-    m = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]+)", text, re.M)
+    m = re.search(r"^kernel_digest_sha256:\s*([0-9a-f]+)", text, re.M)
     if not m or m.group(1) != digest:
         return None
     vals = {}
@@ -80,7 +81,7 @@ def cpu_baseline(dev_shard, w, slices: int):
     import oracle.zero_step as ozs
 
     piece = 1 << 22
-    total = min(slices * piece, w.n)
+    total = min(slices * piece, w.n) if slices > 0 else w.n
     host = dict(chunks=[c[:total].cpu().numpy() for c in dev_shard["chunks"]],
                 master=dev_shard["master"][:total].cpu().numpy(),
                 m=dev_shard["m"][:total].cpu().numpy(), v=dev_shard["v"][:total].cpu().numpy(),
@@ -101,8 +102,9 @@ def cpu_baseline(dev_shard, w, slices: int):
     assert not any(r.overflow for r in results)
     return {"value": total / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
             "seconds": dt,
-            "sample": f"first {total} params of the {w.name} shard ({count} slices of 2^22, "
-                      f"N={w.n_replicas} replicas), full step incl. overflow check"}
+            "sample": (f"{'whole' if total == w.n else 'first ' + str(total) + ' params of the'} "
+                       f"{w.name} shard ({total} params, {count} slices of 2^22, "
+                       f"N={w.n_replicas} replicas): overflow check and AdamW update")}
 
 
 def main():
@@ -186,7 +188,7 @@ def main():
     k1_bytes = w.bytes_per_param_step() * n
     k2_bytes = 2 * N * n
     k1_gbps = k1_bytes / (k1_ms * 1e-3) / 1e9
-    traffic = read_traffic(_build.sources_digest(), n)
+    traffic = read_traffic(_build.kernel_digest(), n)
     extra = {
         "fused_step_ms": k1_ms, "fused_step_params_per_s": n / (k1_ms * 1e-3),
         "fused_step_gbps": k1_gbps, "fused_step_pct_peak": 100 * k1_gbps / HBM_PEAK_GBPS,
@@ -197,6 +199,7 @@ def main():
 
     if not args.no_flatten:
         extra.update(bench_flatten(zs, wl, dev, stream))
+    extra.update(copy_ceiling(dev, stream))
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -229,6 +232,27 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def copy_ceiling(dev, stream, reps: int = 5):
+    """A plain 4 GiB elementwise copy (torch's vectorized elementwise kernel,
+    dst = -src): the bandwidth a two-array stream reaches on this device
+    (read + write bytes over time)."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.neg(src, out=dst)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    nbytes = 2 * src.numel() * 4
+    del src, dst
+    return {"copy_ceiling_gbps": nbytes / (ms * 1e-3) / 1e9}
 
 
 def bench_flatten(zs, wl, dev, stream, reps: int = 10):

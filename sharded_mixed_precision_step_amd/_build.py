@@ -39,12 +39,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def sources_digest() -> str:
-    """SHA-256 over the library's sources and header."""
+def kernel_digest() -> str:
+    """SHA-256 over the sources that fix the kernels' code and launch shapes
+    (the device source and the internal header).  Hardware counters taken on
+    one digest do not describe kernels built from another."""
     import hashlib
     h = hashlib.sha256()
-    for p in sorted(SOURCES + [os.path.join(CSRC, "zero_internal.h"),
-                               os.path.join(INCLUDE, "zero_step.h")]):
+    for p in (os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_internal.h")):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())

@@ -10,7 +10,10 @@
 namespace zero {
 
 constexpr int kBlock = 256;        // threads per workgroup: four 64-wide waves
-constexpr int kPack = 8;           // params per thread per iteration: 16 B of fp16
+constexpr int kPack = 8;           // params per 16-byte fp16 vector ("pack")
+constexpr int kWaveSpan = 2;       // packs per lane in a step tile
+constexpr int kTilePacks = kBlock * kWaveSpan;  // packs per step tile (one block)
+constexpr int kCheckBlocksPerCU = 6;            // resident blocks of the check kernel
 constexpr int kFlattenBatch = 32;  // tensors per flatten launch (kernel-argument table)
 
 // Replica gradient chunks, passed by value in the kernel arguments.

@@ -11,16 +11,20 @@
 // (not stored), scale, fp32 moments, fp32 master weights, fp16 params.
 //
 // All three are memory-bound streams (well under 1 flop per byte), so the
-// design goal is HBM bandwidth: every thread moves 16-byte vectors (8 fp16
-// gradients per chunk, 2 x 16 B of each fp32 state array, 8 fp16 params) in a
-// grid-stride loop over a grid sized to the resident capacity of the chip, so
-// each 64-wide wave issues fully coalesced 1 KiB requests per array.  The
-// overflow flag and the squared norm are reduced per wave with lane shuffles,
-// across the block's four waves in LDS, and published with one atomic each
-// per block.  Every fp32 operation is a separate IEEE operation (the file is
-// built without floating-point contraction, division and square root are the
-// correctly rounded forms), so results match the plain per-operation
-// definition bit for bit.
+// design goal is HBM bandwidth.  Every access is a 16-byte vector (8 fp16
+// gradients of one chunk, 4 fp32 of one state array, 8 fp16 params), so each
+// 64-wide wave instruction moves 1 KiB of one array, fully coalesced.  The
+// fused step runs one block per 4096-param tile (a one-shot grid); the check
+// runs a grid-stride loop over a resident grid with streaming loads.  Both
+// launch shapes were chosen by measurement on MI355X: with the N + 7 arrays
+// the step touches, one-shot tiles sustain the most bandwidth, while the
+// read-only check does best as a resident loop.  The overflow flag and the
+// squared norm are reduced per wave with lane shuffles, across the block's
+// four waves in LDS, and published with one atomic each per block.  Every
+// fp32 operation is a separate IEEE operation (the file is built without
+// floating-point contraction, division and square root are the correctly
+// rounded forms), so results match the plain per-operation definition bit
+// for bit.
 #include "zero_internal.h"
 
 namespace zero {
@@ -100,6 +104,16 @@ __device__ __forceinline__ void publish(bool bad, double sq, int32_t* d_overflow
 }
 
 template <int NC>
+__device__ __forceinline__ float replica_sum1(const ChunkTable& chunks, int n_chunks,
+                                              int64_t j) {
+    float s = load_widen1(chunks.p[0], j);
+    const int nc = NC > 0 ? NC : n_chunks;
+    for (int c = 1; c < nc; ++c) s += load_widen1(chunks.p[c], j);
+    return s;
+}
+
+// Sum of the N replicas' pack `pack`, widened, in replica order 0..N-1.
+template <int NC>
 __device__ __forceinline__ f8 replica_sum8(const ChunkTable& chunks, int n_chunks,
                                            int64_t pack) {
     f8 s = load_widen8(chunks.p[0], pack);
@@ -112,15 +126,76 @@ __device__ __forceinline__ f8 replica_sum8(const ChunkTable& chunks, int n_chunk
     return s;
 }
 
-template <int NC>
-__device__ __forceinline__ float replica_sum1(const ChunkTable& chunks, int n_chunks,
-                                              int64_t j) {
-    float s = load_widen1(chunks.p[0], j);
-    const int nc = NC > 0 ? NC : n_chunks;
-    for (int c = 1; c < nc; ++c) s += load_widen1(chunks.p[c], j);
-    return s;
+// One step tile: kTilePacks consecutive packs.  Wave w of the block owns the
+// kWaveSpan * 64 packs starting at w * kWaveSpan * 64, lane l the packs
+// l, l + 64, ...: every vector instruction of a wave reads or writes 1 KiB
+// of one array contiguously, and each wave sweeps 2 KiB of fp16 (4 KiB of
+// fp32) per array.  All loads of the tile are issued before the arithmetic.
+// FULL: every pack of the tile exists (all tiles but possibly the last).
+template <int NC, bool REDUCE, bool FULL>
+__device__ __forceinline__ void step_tile(const ChunkTable& chunks, int n_chunks, int64_t packs,
+                                          int64_t first, const GradScalars& gs,
+                                          const AdamScalars& as, float* __restrict__ master,
+                                          float* __restrict__ exp_avg,
+                                          float* __restrict__ exp_avg_sq,
+                                          uint16_t* __restrict__ param_fp16, bool& bad,
+                                          double& sq) {
+    f8 s[kWaveSpan];
+    f4 p[kWaveSpan][2], m[kWaveSpan][2], v[kWaveSpan][2];
+#pragma unroll
+    for (int u = 0; u < kWaveSpan; ++u) {
+        const int64_t i = first + u * 64;
+        if (FULL || i < packs) {
+            s[u] = replica_sum8<NC>(chunks, n_chunks, i);
+            const f4* pm = reinterpret_cast<const f4*>(master) + 2 * i;
+            const f4* mm = reinterpret_cast<const f4*>(exp_avg) + 2 * i;
+            const f4* vm = reinterpret_cast<const f4*>(exp_avg_sq) + 2 * i;
+            p[u][0] = pm[0];
+            p[u][1] = pm[1];
+            m[u][0] = mm[0];
+            m[u][1] = mm[1];
+            v[u][0] = vm[0];
+            v[u][1] = vm[1];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kWaveSpan; ++u) {
+        const int64_t i = first + u * 64;
+        if (!FULL && i >= packs) continue;
+        float pe[kPack] = {p[u][0].x, p[u][0].y, p[u][0].z, p[u][0].w,
+                           p[u][1].x, p[u][1].y, p[u][1].z, p[u][1].w};
+        float me[kPack] = {m[u][0].x, m[u][0].y, m[u][0].z, m[u][0].w,
+                           m[u][1].x, m[u][1].y, m[u][1].z, m[u][1].w};
+        float ve[kPack] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                           v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+        u16x8 out;
+#pragma unroll
+        for (int e = 0; e < kPack; ++e) {
+            const float g = unscaled_mean(s[u][e], gs);
+            if constexpr (REDUCE) {
+                bad |= nonfinite(g);
+                sq += static_cast<double>(g) * static_cast<double>(g);
+            }
+            adam_update(g, pe[e], me[e], ve[e], as);
+            out[e] = to_fp16_bits(pe[e]);
+        }
+        f4* pm = reinterpret_cast<f4*>(master) + 2 * i;
+        f4* mm = reinterpret_cast<f4*>(exp_avg) + 2 * i;
+        f4* vm = reinterpret_cast<f4*>(exp_avg_sq) + 2 * i;
+        pm[0] = f4{pe[0], pe[1], pe[2], pe[3]};
+        pm[1] = f4{pe[4], pe[5], pe[6], pe[7]};
+        mm[0] = f4{me[0], me[1], me[2], me[3]};
+        mm[1] = f4{me[4], me[5], me[6], me[7]};
+        vm[0] = f4{ve[0], ve[1], ve[2], ve[3]};
+        vm[1] = f4{ve[4], ve[5], ve[6], ve[7]};
+        *reinterpret_cast<u16x8*>(param_fp16 + i * kPack) = out;
+    }
 }
 
+// The fused step.  One block per tile (a one-shot grid, not a grid-stride
+// loop): on MI355X a stream over this many arrays (N chunks, three state
+// arrays read and written, the fp16 params) sustains more HBM bandwidth when
+// blocks retire after one tile than when resident blocks loop.
 template <int NC, bool REDUCE>
 __global__ __launch_bounds__(kBlock) void shard_step_kernel(
     ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs, AdamScalars as,
@@ -128,38 +203,18 @@ __global__ __launch_bounds__(kBlock) void shard_step_kernel(
     float* __restrict__ exp_avg_sq, uint16_t* __restrict__ param_fp16,
     int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
     const int64_t packs = n / kPack;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kTilePacks;
+    const int64_t first = tile0 + wave * (kWaveSpan * 64) + lane;
     bool bad = false;
     double sq = 0.0;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < packs;
-         i += stride) {
-        const f8 s = replica_sum8<NC>(chunks, n_chunks, i);
-        f4* pm = reinterpret_cast<f4*>(master) + 2 * i;
-        f4* mm = reinterpret_cast<f4*>(exp_avg) + 2 * i;
-        f4* vm = reinterpret_cast<f4*>(exp_avg_sq) + 2 * i;
-        const f4 p0 = pm[0], p1 = pm[1], m0 = mm[0], m1 = mm[1], v0 = vm[0], v1 = vm[1];
-        float p[kPack] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        float m[kPack] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        float v[kPack] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        u16x8 out;
-#pragma unroll
-        for (int e = 0; e < kPack; ++e) {
-            const float g = unscaled_mean(s[e], gs);
-            if constexpr (REDUCE) {
-                bad |= nonfinite(g);
-                sq += static_cast<double>(g) * static_cast<double>(g);
-            }
-            adam_update(g, p[e], m[e], v[e], as);
-            out[e] = to_fp16_bits(p[e]);
-        }
-        pm[0] = f4{p[0], p[1], p[2], p[3]};
-        pm[1] = f4{p[4], p[5], p[6], p[7]};
-        mm[0] = f4{m[0], m[1], m[2], m[3]};
-        mm[1] = f4{m[4], m[5], m[6], m[7]};
-        vm[0] = f4{v[0], v[1], v[2], v[3]};
-        vm[1] = f4{v[4], v[5], v[6], v[7]};
-        *reinterpret_cast<u16x8*>(param_fp16 + i * kPack) = out;
-    }
+    if (tile0 + kTilePacks <= packs)
+        step_tile<NC, REDUCE, true>(chunks, n_chunks, packs, first, gs, as, master, exp_avg,
+                                    exp_avg_sq, param_fp16, bad, sq);
+    else
+        step_tile<NC, REDUCE, false>(chunks, n_chunks, packs, first, gs, as, master, exp_avg,
+                                     exp_avg_sq, param_fp16, bad, sq);
     // The last n % 8 params: one per thread of the last block.
     if (blockIdx.x == gridDim.x - 1) {
         const int64_t j = packs * kPack + threadIdx.x;
@@ -180,17 +235,27 @@ __global__ __launch_bounds__(kBlock) void shard_step_kernel(
     if constexpr (REDUCE) publish(bad, sq, d_overflow, d_sqnorm);
 }
 
+__device__ __forceinline__ f8 load_widen8_nt(const uint16_t* base, int64_t pack) {
+    const h8 h = __builtin_nontemporal_load(reinterpret_cast<const h8*>(base + pack * kPack));
+    return __builtin_convertvector(h, f8);
+}
+
+// The check reads only the chunks, once: a grid-stride loop over a grid of
+// kCheckBlocksPerCU blocks per CU, with non-temporal (streaming) loads.
 template <int NC>
 __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs,
     int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
     const int64_t packs = n / kPack;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    const int nc = NC > 0 ? NC : n_chunks;
     bool bad = false;
     double sq = 0.0;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < packs;
          i += stride) {
-        const f8 s = replica_sum8<NC>(chunks, n_chunks, i);
+        f8 s = load_widen8_nt(chunks.p[0], i);
+#pragma unroll
+        for (int c = 1; c < nc; ++c) s += load_widen8_nt(chunks.p[c], i);
 #pragma unroll
         for (int e = 0; e < kPack; ++e) {
             const float g = unscaled_mean(s[e], gs);
@@ -237,8 +302,7 @@ __global__ __launch_bounds__(kBlock) void bucket_flatten_kernel(FlattenTable tab
 }
 
 // ---------------------------------------------------------------------------
-// Launch sizing: a grid-stride loop wants exactly as many blocks as the chip
-// holds at once (more would leave a tail of late blocks, fewer idle CUs).
+// Launch sizing.
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxDevices = 64;
@@ -256,29 +320,24 @@ int device_cus(int dev) {
     return v;
 }
 
-template <typename Kernel>
-int resident_blocks(Kernel kernel) {
-    static int cache[kMaxDevices] = {};
+int current_cus() {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-    if (v == 0) {
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
-                                                         kBlock, 0) != hipSuccess ||
-            per_cu <= 0)
-            per_cu = 1;
-        v = per_cu * device_cus(dev);
-        __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
-    }
-    return v;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    return device_cus(dev);
 }
 
-int64_t grid_for(int64_t n, int resident) {
-    const int64_t packs = n / kPack;
-    int64_t want = (packs + kBlock - 1) / kBlock;
-    if (want < 1) want = 1;  // a grid of one block still runs the tail
-    return want < resident ? want : resident;
+// Step: one block per tile; a grid of one block still runs the tail.
+int64_t step_grid(int64_t n) {
+    const int64_t tiles = (n / kPack + kTilePacks - 1) / kTilePacks;
+    return tiles < 1 ? 1 : tiles;
+}
+
+// Check: a resident grid (grid-stride loop), no larger than the packs need.
+int64_t check_grid(int64_t n) {
+    const int64_t want = (n / kPack + kBlock - 1) / kBlock;
+    const int64_t resident = static_cast<int64_t>(kCheckBlocksPerCU) * current_cus();
+    const int64_t g = want < resident ? want : resident;
+    return g < 1 ? 1 : g;
 }
 
 template <int NC, bool REDUCE>
@@ -286,21 +345,19 @@ hipError_t step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const Gr
                      const AdamScalars& as, float* master, float* exp_avg, float* exp_avg_sq,
                      uint16_t* param_fp16, int32_t* d_overflow, double* d_sqnorm,
                      hipStream_t stream) {
-    auto kernel = shard_step_kernel<NC, REDUCE>;
-    const int64_t grid = grid_for(n, resident_blocks(kernel));
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, chunks,
-                       n_chunks, n, gs, as, master, exp_avg, exp_avg_sq, param_fp16, d_overflow,
-                       d_sqnorm);
+    const int64_t grid = step_grid(n);
+    hipLaunchKernelGGL((shard_step_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, as, master, exp_avg,
+                       exp_avg_sq, param_fp16, d_overflow, d_sqnorm);
     return hipGetLastError();
 }
 
 template <int NC>
 hipError_t check_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
                       int32_t* d_overflow, double* d_sqnorm, hipStream_t stream) {
-    auto kernel = overflow_check_kernel<NC>;
-    const int64_t grid = grid_for(n, resident_blocks(kernel));
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, stream, chunks,
-                       n_chunks, n, gs, d_overflow, d_sqnorm);
+    const int64_t grid = check_grid(n);
+    hipLaunchKernelGGL(overflow_check_kernel<NC>, dim3(static_cast<unsigned>(grid)), dim3(kBlock),
+                       0, stream, chunks, n_chunks, n, gs, d_overflow, d_sqnorm);
     return hipGetLastError();
 }
 
@@ -354,9 +411,7 @@ hipError_t launch_overflow_check(const ChunkTable& chunks, int n_chunks, int64_t
 hipError_t launch_bucket_flatten(const FlattenTable& table, int count, int64_t max_slot_len,
                                  uint16_t* bucket, hipStream_t stream) {
     if (count <= 0 || max_slot_len <= 0) return hipSuccess;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    const int64_t cap = static_cast<int64_t>(device_cus(dev)) * 8;
+    const int64_t cap = static_cast<int64_t>(current_cus()) * 8;
     int64_t gx = (max_slot_len / kPack + kBlock) / kBlock;
     if (gx > cap) gx = cap;
     if (gx < 1) gx = 1;
