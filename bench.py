@@ -5,10 +5,13 @@ rank owns 1,003,750,000 params), 8 fp16 replica gradient chunks in HBM,
 loss scale 65536, AdamW at t = 1000 with non-zero fp32 m and v.  Inputs are
 seeded synthetic draws made on the device before timing starts.
 
-One timed step is the whole per-rank path: zero the device flag and norm,
-overflow check (sum, mean, unscale, inf/NaN flag, squared norm), read the
-flag back, update the dynamic loss scale on the host, and run the fused
-update (moments, fp32 master, fp16 params) when the step is clean.
+One timed step is the whole per-rank path in its single-pass form: zero the
+device flag and norm; run the fused update (replica sum, mean, unscale,
+inf/NaN flag, squared norm, moments, fp32 master, fp16 params) from the
+current copy of the state into the other copy; read the flag back; update
+the dynamic loss scale on the host; and commit the written copy if the step
+is clean.  The two-pass form (overflow check, then the in-place update) is
+timed afterwards on the same state and reported under "extra".
 
 Prints one JSON line.  `value` is params/s of the whole step.  `roofline`
 rates the fused update kernel, the dominant one, by its algorithmic bytes
@@ -48,6 +51,9 @@ def parse_args():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration)")
     ap.add_argument("--no-flatten", action="store_true")
+    ap.add_argument("--two-pass-steps", type=int, default=10,
+                    help="steps of the two-pass path (check, then in-place step), "
+                         "timed after the main loop for comparison")
     return ap.parse_args()
 
 
@@ -143,32 +149,31 @@ def main():
     scaler = zs.LossScaler.create(scale=w.loss_scale)
     hp = zs.adamw_params(w.hyper)
     stream = torch.cuda.current_stream()
-    k1_events, k2_events = [], []
+    shard = zs.DoubleBufferedShard(d["master"], d["m"], d["v"], d["p16"])
+    fused_events = []
     skipped = 0
 
     def step(record: bool):
+        """The single-pass step: fused out-of-place update with the flag and
+        squared norm, flag read-back, loss-scale update, commit if clean."""
         nonlocal skipped
         flag.zero_()
         sq.zero_()
         scale = scaler.scale
+        m_in, a_in, v_in, _ = shard.current
+        m_out, a_out, v_out, p_out = shard.other
         if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
-        zs.zero_overflow_check(d["chunks"], scale, flag, sq, stream=stream)
+        zs.zero_shard_step_out(d["chunks"], scale, m_in, a_in, v_in, m_out, a_out, v_out, p_out,
+                               hp, flag, sq, stream=stream)
         if record:
             e[1].record(stream)
-        overflow = int(flag.item())
-        if zs.zero_update_loss_scale(scaler, overflow):
+            fused_events.append(e)
+        if zs.zero_update_loss_scale(scaler, int(flag.item())):
             skipped += 1
             return
-        if record:
-            e[2].record(stream)
-        zs.zero_shard_step(d["chunks"], scale, d["master"], d["m"], d["v"], d["p16"], hp,
-                           stream=stream)
-        if record:
-            e[3].record(stream)
-            k2_events.append((e[0], e[1]))
-            k1_events.append((e[2], e[3]))
+        shard.cur = 1 - shard.cur
         hp.step += 1
 
     for _ in range(args.warmup):
@@ -180,22 +185,25 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    k1_ms = sum(a.elapsed_time(b) for a, b in k1_events) / max(len(k1_events), 1)
-    k2_ms = sum(a.elapsed_time(b) for a, b in k2_events) / max(len(k2_events), 1)
-    log(f"bench: {ms_per_step:.3f} ms/step, fused step {k1_ms:.3f} ms, check {k2_ms:.3f} ms, "
+    k1_ms = sum(a.elapsed_time(b) for a, b in fused_events) / max(len(fused_events), 1)
+    log(f"bench: single-pass {ms_per_step:.3f} ms/step, fused step {k1_ms:.3f} ms, "
         f"skipped {skipped}")
+    two = two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, args.two_pass_steps)
+    log(f"bench: two-pass {two['two_pass_ms_per_step']:.3f} ms/step, check "
+        f"{two['check_ms']:.3f} ms, in-place step {two['inplace_step_ms']:.3f} ms")
 
     k1_bytes = w.bytes_per_param_step() * n
-    k2_bytes = 2 * N * n
     k1_gbps = k1_bytes / (k1_ms * 1e-3) / 1e9
     traffic = read_traffic(_build.kernel_digest(), n)
     extra = {
+        "path": "single pass: zero_shard_step_out with flag and squared norm, "
+                "flag read-back, zero_update_loss_scale, commit by buffer swap",
         "fused_step_ms": k1_ms, "fused_step_params_per_s": n / (k1_ms * 1e-3),
         "fused_step_gbps": k1_gbps, "fused_step_pct_peak": 100 * k1_gbps / HBM_PEAK_GBPS,
-        "check_ms": k2_ms, "check_gbps": k2_bytes / (k2_ms * 1e-3) / 1e9,
-        "step_gbps": (k1_bytes + k2_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "step_gbps": k1_bytes / (ms_per_step * 1e-3) / 1e9,
         "skipped_steps": skipped,
     }
+    extra.update(two)
 
     if not args.no_flatten:
         extra.update(bench_flatten(zs, wl, dev, stream))
@@ -223,8 +231,7 @@ def main():
         "data": "synthetic (seeded device draws; fp16 grads, fp32 state)",
         "config": {"workload": w.name, "shard_params": n, "replicas": N,
                    "loss_scale": w.loss_scale, "adam_step": w.hyper.step,
-                   "bytes_per_param_fused_step": w.bytes_per_param_step(),
-                   "bytes_per_param_check": 2 * N},
+                   "bytes_per_param_fused_step": w.bytes_per_param_step()},
         "roofline": {"bound": "hbm", "achieved": k1_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": k1_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic},
@@ -232,6 +239,44 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
+    """The two-pass step on the same state, for comparison: overflow check,
+    flag read-back, loss-scale update, in-place fused update if clean."""
+    import torch
+    n, N = w.n, w.n_replicas
+    master, m, v, p16 = shard.current
+    ev_check, ev_step = [], []
+    t0 = None
+    for k in range(steps + 1):           # the first step is an untimed warm-up
+        if k == 1:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        flag.zero_()
+        sq.zero_()
+        scale = scaler.scale
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        zs.zero_overflow_check(d["chunks"], scale, flag, sq, stream=stream)
+        e[1].record(stream)
+        if zs.zero_update_loss_scale(scaler, int(flag.item())):
+            continue
+        e[2].record(stream)
+        zs.zero_shard_step(d["chunks"], scale, master, m, v, p16, hp, stream=stream)
+        e[3].record(stream)
+        hp.step += 1
+        if k >= 1:
+            ev_check.append((e[0], e[1]))
+            ev_step.append((e[2], e[3]))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    check_ms = sum(a.elapsed_time(b) for a, b in ev_check) / max(len(ev_check), 1)
+    step_ms = sum(a.elapsed_time(b) for a, b in ev_step) / max(len(ev_step), 1)
+    return {"two_pass_ms_per_step": ms, "two_pass_params_per_s": n / (ms * 1e-3),
+            "check_ms": check_ms, "check_gbps": 2 * N * n / (check_ms * 1e-3) / 1e9,
+            "inplace_step_ms": step_ms,
+            "inplace_step_gbps": w.bytes_per_param_step() * n / (step_ms * 1e-3) / 1e9}
 
 
 def copy_ceiling(dev, stream, reps: int = 5):

@@ -137,6 +137,46 @@ int zero_shard_step(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
                     double* d_sqnorm, void* stream);
 
 /*
+ * zero_shard_step_out -- the fused update, reading one copy of the state and
+ * writing the next, so that a step can be committed or dropped after the fact.
+ *
+ * The arithmetic, element by element, is exactly that of zero_shard_step:
+ * the new master, moments and fp16 params of element j are computed from
+ * master_in[j], exp_avg_in[j], exp_avg_sq_in[j] and the replica chunks, and
+ * stored to master_out[j], exp_avg_out[j], exp_avg_sq_out[j] and
+ * param_fp16_out[j].  The *_in arrays are only read.  With d_overflow (and
+ * d_sqnorm) given, the same pass also ORs the non-finite flag of g into
+ * *d_overflow and adds sum g^2 to *d_sqnorm, as zero_overflow_check does.
+ *
+ * This is the single-pass form of a ZeRO step whose update is skipped on
+ * overflow: the skip decision is global, so no in-place pass can know it
+ * before writing.  Writing to a second copy of the state instead lets the
+ * caller read the flag afterwards and either adopt the *_out arrays (clean
+ * step) or keep the untouched *_in arrays and its previous fp16 params
+ * (overflow).  The step then reads the gradients once (2N + 26 bytes per
+ * param in all) instead of twice (check, then step: 4N + 26).
+ *
+ *   grad_chunks     as for zero_overflow_check
+ *   master_in, exp_avg_in, exp_avg_sq_in
+ *                   DEVICE fp32[n] each, 16-byte aligned, read only
+ *   master_out, exp_avg_out, exp_avg_sq_out
+ *                   DEVICE fp32[n] each, 16-byte aligned, written only
+ *   param_fp16_out  DEVICE fp16[n], 16-byte aligned, written only
+ *   hp              HOST, hyperparameters of this update
+ *   d_overflow      DEVICE int32 or NULL;  d_sqnorm DEVICE fp64 or NULL
+ * Each *_out array may be the same pointer as its *_in array (that element is
+ * then updated in place, as zero_shard_step does); apart from that, no output
+ * may share a byte with any input, another output or a gradient chunk.
+ * Returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN or ZERO_EHIP.
+ */
+int zero_shard_step_out(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                        float loss_scale, const float* master_in, const float* exp_avg_in,
+                        const float* exp_avg_sq_in, float* master_out, float* exp_avg_out,
+                        float* exp_avg_sq_out, void* param_fp16_out,
+                        const zero_adamw_params* hp, int32_t* d_overflow, double* d_sqnorm,
+                        void* stream);
+
+/*
  * zero_bucket_flatten -- pack whole fp16 gradient tensors into one bucket.
  *
  * Several parameters' gradients are grouped into a bucket and reduced as one

@@ -30,8 +30,8 @@ ZERO_ERANGE = -3
 ZERO_EHIP = -4
 ZERO_MAX_CHUNKS = 64
 
-EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_bucket_flatten",
-            "zero_update_loss_scale", "zero_last_error_string")
+EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
+            "zero_bucket_flatten", "zero_update_loss_scale", "zero_last_error_string")
 
 
 class ZeroStepError(RuntimeError):
@@ -78,6 +78,8 @@ def _load() -> ctypes.CDLL:
     lib.zero_overflow_check.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp]
     lib.zero_shard_step.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp, vp,
                                     ctypes.POINTER(AdamWParams), vp, vp, vp]
+    lib.zero_shard_step_out.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.POINTER(AdamWParams), vp, vp, vp]
     lib.zero_bucket_flatten.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), i32, i64, i64,
                                         vp, i64, ctypes.POINTER(ctypes.c_int64), vp]
     lib.zero_update_loss_scale.argtypes = [ctypes.POINTER(LossScaler), i32,
@@ -165,6 +167,37 @@ def zero_shard_step(grad_chunks: Sequence[torch.Tensor], loss_scale: float,
         _stream(stream)))
 
 
+def zero_shard_step_out(grad_chunks: Sequence[torch.Tensor], loss_scale: float,
+                        master_in: torch.Tensor, exp_avg_in: torch.Tensor,
+                        exp_avg_sq_in: torch.Tensor, master_out: torch.Tensor,
+                        exp_avg_out: torch.Tensor, exp_avg_sq_out: torch.Tensor,
+                        param_fp16_out: torch.Tensor, hp: AdamWParams,
+                        d_overflow: Optional[torch.Tensor] = None,
+                        d_sqnorm: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Fused update from the *_in state into the *_out state (see zero_step.h)."""
+    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+    n = master_in.numel()
+    named = [("exp_avg_in", exp_avg_in), ("exp_avg_sq_in", exp_avg_sq_in),
+             ("master_out", master_out), ("exp_avg_out", exp_avg_out),
+             ("exp_avg_sq_out", exp_avg_sq_out), ("param_fp16_out", param_fp16_out)]
+    named += [(f"grad_chunks[{i}]", c) for i, c in enumerate(grad_chunks)]
+    for name, t in named:
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    if not isinstance(hp, AdamWParams):
+        hp = adamw_params(hp)
+    _check(lib.zero_shard_step_out(
+        _ptr_array(ptrs), len(ptrs), n, float(loss_scale),
+        _dev(master_in, torch.float32, "master_in"), _dev(exp_avg_in, torch.float32, "exp_avg_in"),
+        _dev(exp_avg_sq_in, torch.float32, "exp_avg_sq_in"),
+        _dev(master_out, torch.float32, "master_out"),
+        _dev(exp_avg_out, torch.float32, "exp_avg_out"),
+        _dev(exp_avg_sq_out, torch.float32, "exp_avg_sq_out"),
+        _dev(param_fp16_out, torch.float16, "param_fp16_out"), ctypes.byref(hp),
+        _opt(d_overflow, torch.int32, "d_overflow"), _opt(d_sqnorm, torch.float64, "d_sqnorm"),
+        _stream(stream)))
+
+
 def zero_bucket_flatten(tensors: Sequence[torch.Tensor], bucket: torch.Tensor,
                         align: int = 256, pad_multiple: int = 0, stream=None) -> list:
     """Pack fp16 tensors into ``bucket``; returns the offsets and padded length."""
@@ -211,5 +244,48 @@ def checked_step(grad_chunks, master, exp_avg, exp_avg_sq, param_fp16, hp: AdamW
     if not skip:
         zero_shard_step(grad_chunks, scale, master, exp_avg, exp_avg_sq, param_fp16, hp,
                         stream=stream)
+        hp.step += 1
+    return ShardStepResult(bool(flag), skip, float(d_sqnorm.item()))
+
+
+class DoubleBufferedShard:
+    """Two copies of a shard's state (fp32 master, m, v and fp16 params) for
+    the single-pass step: a step reads copy ``cur`` and writes the other, and
+    is committed by making the other copy current.  Memory is owned by the
+    caller's tensors; this object only tracks which copy is current."""
+
+    def __init__(self, master, exp_avg, exp_avg_sq, param_fp16, spare=None):
+        if spare is None:
+            spare = tuple(torch.empty_like(t) for t in (master, exp_avg, exp_avg_sq, param_fp16))
+        self.copies = [(master, exp_avg, exp_avg_sq, param_fp16), tuple(spare)]
+        self.cur = 0
+
+    @property
+    def current(self):
+        return self.copies[self.cur]
+
+    @property
+    def other(self):
+        return self.copies[1 - self.cur]
+
+
+def committed_step(grad_chunks, shard: DoubleBufferedShard, hp: AdamWParams,
+                   scaler: LossScaler, d_overflow: torch.Tensor, d_sqnorm: torch.Tensor,
+                   stream=None) -> ShardStepResult:
+    """One clean-or-skipped step in a single pass over the gradients: the
+    fused out-of-place update (with the flag and squared norm), the flag read
+    back, the loss-scale update, and the commit (the written copy becomes
+    current) only if the step is clean.  hp.step is advanced on a clean step."""
+    d_overflow.zero_()
+    d_sqnorm.zero_()
+    scale = scaler.scale
+    m_in, a_in, v_in, _ = shard.current
+    m_out, a_out, v_out, p_out = shard.other
+    zero_shard_step_out(grad_chunks, scale, m_in, a_in, v_in, m_out, a_out, v_out, p_out, hp,
+                        d_overflow, d_sqnorm, stream=stream)
+    flag = int(d_overflow.item())          # device -> host: the skip decision
+    skip = zero_update_loss_scale(scaler, flag)
+    if not skip:
+        shard.cur = 1 - shard.cur
         hp.step += 1
     return ShardStepResult(bool(flag), skip, float(d_sqnorm.item()))

@@ -112,6 +112,57 @@ int adam_scalars(const zero_adamw_params* hp, zero::AdamScalars* as) {
     return ZERO_OK;
 }
 
+// Validation and launch shared by the in-place and the out-of-place step.
+// Output k may equal input k exactly (in place); otherwise no output may
+// share a byte with any input, another output or a gradient chunk.
+int shard_step_common(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                      float loss_scale, const float* master_in, const float* exp_avg_in,
+                      const float* exp_avg_sq_in, float* master_out, float* exp_avg_out,
+                      float* exp_avg_sq_out, void* param_fp16_out, const zero_adamw_params* hp,
+                      int32_t* d_overflow, double* d_sqnorm, void* stream, const char* who) {
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    zero::AdamScalars as;
+    int rc = check_chunks(grad_chunks, n_chunks, n, loss_scale, &table, &gs);
+    if (rc) return rc;
+    if ((rc = adam_scalars(hp, &as))) return rc;
+    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
+    if (n == 0) return ok();  // nothing is read or written
+    const void* in[3] = {master_in, exp_avg_in, exp_avg_sq_in};
+    const void* out[4] = {master_out, exp_avg_out, exp_avg_sq_out, param_fp16_out};
+    static const char* in_names[3] = {"master_in", "exp_avg_in", "exp_avg_sq_in"};
+    static const char* out_names[4] = {"master_out", "exp_avg_out", "exp_avg_sq_out",
+                                       "param_fp16_out"};
+    const int64_t out_bytes[4] = {4 * n, 4 * n, 4 * n, 2 * n};
+    for (int a = 0; a < 3; ++a) {
+        if (!in[a]) return fail(ZERO_EINVAL, "%s: %s is NULL", who, in_names[a]);
+        if (!aligned(in[a], 16))
+            return fail(ZERO_EALIGN, "%s: %s is not 16-byte aligned", who, in_names[a]);
+    }
+    for (int a = 0; a < 4; ++a) {
+        if (!out[a]) return fail(ZERO_EINVAL, "%s: %s is NULL", who, out_names[a]);
+        if (!aligned(out[a], 16))
+            return fail(ZERO_EALIGN, "%s: %s is not 16-byte aligned", who, out_names[a]);
+    }
+    for (int a = 0; a < 4; ++a) {
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(out[a], out_bytes[a], out[b], out_bytes[b]))
+                return fail(ZERO_EINVAL, "%s: %s overlaps %s", who, out_names[a], out_names[b]);
+        for (int b = 0; b < 3; ++b)
+            if (!(a == b && out[a] == in[b]) && overlap(out[a], out_bytes[a], in[b], 4 * n))
+                return fail(ZERO_EINVAL, "%s: %s overlaps %s", who, out_names[a], in_names[b]);
+        for (int32_t c = 0; c < n_chunks; ++c)
+            if (overlap(out[a], out_bytes[a], grad_chunks[c], 2 * n))
+                return fail(ZERO_EINVAL, "%s: %s overlaps grad_chunks[%d]", who, out_names[a], c);
+    }
+    const zero::ShardState st = {master_in,  exp_avg_in,     exp_avg_sq_in,
+                                 master_out, exp_avg_out,    exp_avg_sq_out,
+                                 static_cast<uint16_t*>(param_fp16_out)};
+    const hipError_t e = zero::launch_shard_step(table, n_chunks, n, gs, as, st, d_overflow,
+                                                 d_sqnorm, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,34 +187,20 @@ int zero_shard_step(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
                     float* master, float* exp_avg, float* exp_avg_sq, void* param_fp16,
                     const zero_adamw_params* hp, int32_t* d_overflow, double* d_sqnorm,
                     void* stream) {
-    zero::ChunkTable table;
-    zero::GradScalars gs;
-    zero::AdamScalars as;
-    int rc = check_chunks(grad_chunks, n_chunks, n, loss_scale, &table, &gs);
-    if (rc) return rc;
-    if ((rc = adam_scalars(hp, &as))) return rc;
-    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
-    if (n == 0) return ok();  // nothing is read or written
-    if (!master || !exp_avg || !exp_avg_sq || !param_fp16)
-        return fail(ZERO_EINVAL, "a state pointer (master, exp_avg, exp_avg_sq, param_fp16) is NULL");
-    if (!aligned(master, 16) || !aligned(exp_avg, 16) || !aligned(exp_avg_sq, 16) ||
-        !aligned(param_fp16, 16))
-        return fail(ZERO_EALIGN, "a state pointer is not 16-byte aligned");
-    const void* state[4] = {master, exp_avg, exp_avg_sq, param_fp16};
-    const int64_t bytes[4] = {4 * n, 4 * n, 4 * n, 2 * n};
-    static const char* names[4] = {"master", "exp_avg", "exp_avg_sq", "param_fp16"};
-    for (int a = 0; a < 4; ++a) {
-        for (int b = a + 1; b < 4; ++b)
-            if (overlap(state[a], bytes[a], state[b], bytes[b]))
-                return fail(ZERO_EINVAL, "%s overlaps %s", names[a], names[b]);
-        for (int32_t c = 0; c < n_chunks; ++c)
-            if (overlap(state[a], bytes[a], grad_chunks[c], 2 * n))
-                return fail(ZERO_EINVAL, "%s overlaps grad_chunks[%d]", names[a], c);
-    }
-    const hipError_t e = zero::launch_shard_step(
-        table, n_chunks, n, gs, as, master, exp_avg, exp_avg_sq, static_cast<uint16_t*>(param_fp16),
-        d_overflow, d_sqnorm, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ok() : hip_fail(e, "zero_shard_step launch");
+    return shard_step_common(grad_chunks, n_chunks, n, loss_scale, master, exp_avg, exp_avg_sq,
+                             master, exp_avg, exp_avg_sq, param_fp16, hp, d_overflow, d_sqnorm,
+                             stream, "zero_shard_step");
+}
+
+int zero_shard_step_out(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                        float loss_scale, const float* master_in, const float* exp_avg_in,
+                        const float* exp_avg_sq_in, float* master_out, float* exp_avg_out,
+                        float* exp_avg_sq_out, void* param_fp16_out, const zero_adamw_params* hp,
+                        int32_t* d_overflow, double* d_sqnorm, void* stream) {
+    return shard_step_common(grad_chunks, n_chunks, n, loss_scale, master_in, exp_avg_in,
+                             exp_avg_sq_in, master_out, exp_avg_out, exp_avg_sq_out,
+                             param_fp16_out, hp, d_overflow, d_sqnorm, stream,
+                             "zero_shard_step_out");
 }
 
 int zero_bucket_flatten(const void* const* tensors, const int64_t* numels, int32_t n_tensors,

@@ -47,6 +47,18 @@ struct AdamScalars {
     int32_t decoupled;
 };
 
+// The shard's optimizer state as one step reads and writes it.  In place:
+// each *_out equals its *_in.  Out of place: the *_in arrays are only read.
+struct ShardState {
+    const float* master_in;
+    const float* exp_avg_in;
+    const float* exp_avg_sq_in;
+    float* master_out;
+    float* exp_avg_out;
+    float* exp_avg_sq_out;
+    uint16_t* param_fp16_out;
+};
+
 struct FlattenDesc {
     const uint16_t* src;  // fp16 bits, 2-byte aligned
     int64_t numel;        // elements of the tensor
@@ -66,8 +78,7 @@ hipError_t launch_overflow_check(const ChunkTable& chunks, int n_chunks, int64_t
 
 hipError_t launch_shard_step(const ChunkTable& chunks, int n_chunks, int64_t n,
                              const GradScalars& gs, const AdamScalars& as,
-                             float* master, float* exp_avg, float* exp_avg_sq,
-                             uint16_t* param_fp16, int32_t* d_overflow,
+                             const ShardState& st, int32_t* d_overflow,
                              double* d_sqnorm, hipStream_t stream);
 
 hipError_t launch_bucket_flatten(const FlattenTable& table, int count,

@@ -130,15 +130,14 @@ __device__ __forceinline__ f8 replica_sum8(const ChunkTable& chunks, int n_chunk
 // kWaveSpan * 64 packs starting at w * kWaveSpan * 64, lane l the packs
 // l, l + 64, ...: every vector instruction of a wave reads or writes 1 KiB
 // of one array contiguously, and each wave sweeps 2 KiB of fp16 (4 KiB of
-// fp32) per array.  All loads of the tile are issued before the arithmetic.
+// fp32) per array.  All loads of the tile are issued before the arithmetic,
+// and each element is read (from the *_in arrays) before it is written (to
+// the *_out arrays), so in-place (in == out) and out-of-place both hold.
 // FULL: every pack of the tile exists (all tiles but possibly the last).
 template <int NC, bool REDUCE, bool FULL>
 __device__ __forceinline__ void step_tile(const ChunkTable& chunks, int n_chunks, int64_t packs,
                                           int64_t first, const GradScalars& gs,
-                                          const AdamScalars& as, float* __restrict__ master,
-                                          float* __restrict__ exp_avg,
-                                          float* __restrict__ exp_avg_sq,
-                                          uint16_t* __restrict__ param_fp16, bool& bad,
+                                          const AdamScalars& as, const ShardState& st, bool& bad,
                                           double& sq) {
     f8 s[kWaveSpan];
     f4 p[kWaveSpan][2], m[kWaveSpan][2], v[kWaveSpan][2];
@@ -147,9 +146,9 @@ __device__ __forceinline__ void step_tile(const ChunkTable& chunks, int n_chunks
         const int64_t i = first + u * 64;
         if (FULL || i < packs) {
             s[u] = replica_sum8<NC>(chunks, n_chunks, i);
-            const f4* pm = reinterpret_cast<const f4*>(master) + 2 * i;
-            const f4* mm = reinterpret_cast<const f4*>(exp_avg) + 2 * i;
-            const f4* vm = reinterpret_cast<const f4*>(exp_avg_sq) + 2 * i;
+            const f4* pm = reinterpret_cast<const f4*>(st.master_in) + 2 * i;
+            const f4* mm = reinterpret_cast<const f4*>(st.exp_avg_in) + 2 * i;
+            const f4* vm = reinterpret_cast<const f4*>(st.exp_avg_sq_in) + 2 * i;
             p[u][0] = pm[0];
             p[u][1] = pm[1];
             m[u][0] = mm[0];
@@ -179,16 +178,16 @@ __device__ __forceinline__ void step_tile(const ChunkTable& chunks, int n_chunks
             adam_update(g, pe[e], me[e], ve[e], as);
             out[e] = to_fp16_bits(pe[e]);
         }
-        f4* pm = reinterpret_cast<f4*>(master) + 2 * i;
-        f4* mm = reinterpret_cast<f4*>(exp_avg) + 2 * i;
-        f4* vm = reinterpret_cast<f4*>(exp_avg_sq) + 2 * i;
+        f4* pm = reinterpret_cast<f4*>(st.master_out) + 2 * i;
+        f4* mm = reinterpret_cast<f4*>(st.exp_avg_out) + 2 * i;
+        f4* vm = reinterpret_cast<f4*>(st.exp_avg_sq_out) + 2 * i;
         pm[0] = f4{pe[0], pe[1], pe[2], pe[3]};
         pm[1] = f4{pe[4], pe[5], pe[6], pe[7]};
         mm[0] = f4{me[0], me[1], me[2], me[3]};
         mm[1] = f4{me[4], me[5], me[6], me[7]};
         vm[0] = f4{ve[0], ve[1], ve[2], ve[3]};
         vm[1] = f4{ve[4], ve[5], ve[6], ve[7]};
-        *reinterpret_cast<u16x8*>(param_fp16 + i * kPack) = out;
+        *reinterpret_cast<u16x8*>(st.param_fp16_out + i * kPack) = out;
     }
 }
 
@@ -198,9 +197,7 @@ __device__ __forceinline__ void step_tile(const ChunkTable& chunks, int n_chunks
 // blocks retire after one tile than when resident blocks loop.
 template <int NC, bool REDUCE>
 __global__ __launch_bounds__(kBlock) void shard_step_kernel(
-    ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs, AdamScalars as,
-    float* __restrict__ master, float* __restrict__ exp_avg,
-    float* __restrict__ exp_avg_sq, uint16_t* __restrict__ param_fp16,
+    ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs, AdamScalars as, ShardState st,
     int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
     const int64_t packs = n / kPack;
     const int lane = threadIdx.x & 63;
@@ -210,11 +207,9 @@ __global__ __launch_bounds__(kBlock) void shard_step_kernel(
     bool bad = false;
     double sq = 0.0;
     if (tile0 + kTilePacks <= packs)
-        step_tile<NC, REDUCE, true>(chunks, n_chunks, packs, first, gs, as, master, exp_avg,
-                                    exp_avg_sq, param_fp16, bad, sq);
+        step_tile<NC, REDUCE, true>(chunks, n_chunks, packs, first, gs, as, st, bad, sq);
     else
-        step_tile<NC, REDUCE, false>(chunks, n_chunks, packs, first, gs, as, master, exp_avg,
-                                     exp_avg_sq, param_fp16, bad, sq);
+        step_tile<NC, REDUCE, false>(chunks, n_chunks, packs, first, gs, as, st, bad, sq);
     // The last n % 8 params: one per thread of the last block.
     if (blockIdx.x == gridDim.x - 1) {
         const int64_t j = packs * kPack + threadIdx.x;
@@ -224,12 +219,12 @@ __global__ __launch_bounds__(kBlock) void shard_step_kernel(
                 bad |= nonfinite(g);
                 sq += static_cast<double>(g) * static_cast<double>(g);
             }
-            float p = master[j], m = exp_avg[j], v = exp_avg_sq[j];
+            float p = st.master_in[j], m = st.exp_avg_in[j], v = st.exp_avg_sq_in[j];
             adam_update(g, p, m, v, as);
-            master[j] = p;
-            exp_avg[j] = m;
-            exp_avg_sq[j] = v;
-            param_fp16[j] = to_fp16_bits(p);
+            st.master_out[j] = p;
+            st.exp_avg_out[j] = m;
+            st.exp_avg_sq_out[j] = v;
+            st.param_fp16_out[j] = to_fp16_bits(p);
         }
     }
     if constexpr (REDUCE) publish(bad, sq, d_overflow, d_sqnorm);
@@ -342,13 +337,12 @@ int64_t check_grid(int64_t n) {
 
 template <int NC, bool REDUCE>
 hipError_t step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
-                     const AdamScalars& as, float* master, float* exp_avg, float* exp_avg_sq,
-                     uint16_t* param_fp16, int32_t* d_overflow, double* d_sqnorm,
-                     hipStream_t stream) {
+                     const AdamScalars& as, const ShardState& st, int32_t* d_overflow,
+                     double* d_sqnorm, hipStream_t stream) {
     const int64_t grid = step_grid(n);
     hipLaunchKernelGGL((shard_step_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, as, master, exp_avg,
-                       exp_avg_sq, param_fp16, d_overflow, d_sqnorm);
+                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, as, st, d_overflow,
+                       d_sqnorm);
     return hipGetLastError();
 }
 
@@ -369,27 +363,22 @@ hipError_t check_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const G
 }  // namespace
 
 hipError_t launch_shard_step(const ChunkTable& chunks, int n_chunks, int64_t n,
-                             const GradScalars& gs, const AdamScalars& as, float* master,
-                             float* exp_avg, float* exp_avg_sq, uint16_t* param_fp16,
+                             const GradScalars& gs, const AdamScalars& as, const ShardState& st,
                              int32_t* d_overflow, double* d_sqnorm, hipStream_t stream) {
     const bool reduce = d_overflow != nullptr || d_sqnorm != nullptr;
-#define ZERO_CASE(K)                                                                         \
-    case K:                                                                                  \
-        return reduce ? step_impl<K, true>(chunks, n_chunks, n, gs, as, master, exp_avg,     \
-                                           exp_avg_sq, param_fp16, d_overflow, d_sqnorm,     \
-                                           stream)                                           \
-                      : step_impl<K, false>(chunks, n_chunks, n, gs, as, master, exp_avg,    \
-                                            exp_avg_sq, param_fp16, d_overflow, d_sqnorm,    \
-                                            stream);
+#define ZERO_CASE(K)                                                                          \
+    case K:                                                                                   \
+        return reduce ? step_impl<K, true>(chunks, n_chunks, n, gs, as, st, d_overflow,       \
+                                           d_sqnorm, stream)                                  \
+                      : step_impl<K, false>(chunks, n_chunks, n, gs, as, st, d_overflow,      \
+                                            d_sqnorm, stream);
     switch (n_chunks) {
         ZERO_FOR_EACH_N(ZERO_CASE)
         default:
-            return reduce ? step_impl<0, true>(chunks, n_chunks, n, gs, as, master, exp_avg,
-                                               exp_avg_sq, param_fp16, d_overflow, d_sqnorm,
-                                               stream)
-                          : step_impl<0, false>(chunks, n_chunks, n, gs, as, master, exp_avg,
-                                                exp_avg_sq, param_fp16, d_overflow, d_sqnorm,
-                                                stream);
+            return reduce ? step_impl<0, true>(chunks, n_chunks, n, gs, as, st, d_overflow,
+                                               d_sqnorm, stream)
+                          : step_impl<0, false>(chunks, n_chunks, n, gs, as, st, d_overflow,
+                                                d_sqnorm, stream);
     }
 #undef ZERO_CASE
 }

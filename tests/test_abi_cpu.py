@@ -119,6 +119,43 @@ def test_shard_step_rejects_bad_state():
     assert _step(_ptrs(A), 1, n, 1.0, *good, _hp(), A + 2) == zs.ZERO_EALIGN
 
 
+def _step_out(chunks, n_chunks, n, ins, outs, hp, flag=None, sq=None):
+    return zs.lib.zero_shard_step_out(chunks, n_chunks, n, 1.0, *ins, *outs,
+                                      ctypes.byref(hp) if hp is not None else None, flag, sq,
+                                      None)
+
+
+def test_shard_step_out_rejects_bad_state():
+    """Out-of-place step: every output must be 16-byte aligned and may equal
+    its own input exactly, but may share no byte with any other input, any
+    other output or a gradient chunk."""
+    B = A + (1 << 20)
+    n = 1000
+    ins = (B, B + 4 * n, B + 8 * n)
+    C = B + (1 << 20)
+    outs = (C, C + 4 * n, C + 8 * n, C + 12 * n)
+    ch = _ptrs(A)
+    # missing or misaligned arrays
+    assert _step_out(ch, 1, n, (None,) + ins[1:], outs, _hp()) == zs.ZERO_EINVAL
+    assert _step_out(ch, 1, n, ins, outs[:3] + (None,), _hp()) == zs.ZERO_EINVAL
+    assert _step_out(ch, 1, n, (ins[0] + 4,) + ins[1:], outs, _hp()) == zs.ZERO_EALIGN
+    assert _step_out(ch, 1, n, ins, (outs[0] + 8,) + outs[1:], _hp()) == zs.ZERO_EALIGN
+    # an output inside another input, shifted inside its own input, or on a chunk
+    assert _step_out(ch, 1, n, ins, (ins[1],) + outs[1:], _hp()) == zs.ZERO_EINVAL
+    assert "overlaps" in _last()
+    assert _step_out(ch, 1, n, ins, (ins[0] + 16,) + outs[1:], _hp()) == zs.ZERO_EINVAL
+    assert _step_out(ch, 1, n, ins, outs[:3] + (ins[2] + 32,), _hp()) == zs.ZERO_EINVAL
+    assert _step_out(_ptrs(C + 4 * n + 64), 1, n, ins, outs, _hp()) == zs.ZERO_EINVAL
+    # two outputs on each other
+    assert _step_out(ch, 1, n, ins, (outs[0], outs[0] + 16) + outs[2:], _hp()) == zs.ZERO_EINVAL
+    # bad hyperparameters and flag alignment
+    assert _step_out(ch, 1, n, ins, outs, _hp(step=0)) == zs.ZERO_EINVAL
+    assert _step_out(ch, 1, n, ins, outs, None) == zs.ZERO_EINVAL
+    assert _step_out(ch, 1, n, ins, outs, _hp(), A + 2) == zs.ZERO_EALIGN
+    # n == 0 is a no-op whatever the pointers
+    assert _step_out(_ptrs(0), 1, 0, (None, None, None), (None,) * 4, _hp()) == zs.ZERO_OK
+
+
 def _flatten(ptrs, numels, align, pad, bucket, cap):
     nt = len(numels)
     offs = (ctypes.c_int64 * (nt + 1))()
