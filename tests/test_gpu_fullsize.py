@@ -1,0 +1,220 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (the single-pass step; also the two-pass check-then-step), compared
+with the CPU oracle element by element wherever the oracle can follow in
+seconds on the host's cores, and by properties that hold at any size
+elsewhere.
+
+* Llama-3-8B shard (1,003,750,000 params, N = 8): every element, both paths.
+* Overflow (125,468,750 params, 100,375 injected inf/NaN): the step is
+  skipped, the scale halves, the state stays bit-identical; then a clean
+  step at the halved scale matches the oracle everywhere.
+* ZeRO-2 bucketed (160 buckets, 973,111,296 params on one rank): every
+  bucket flattened for 8 replicas and stepped; buckets 0, 3, 4 and 159
+  (both bucket shapes, first and last) checked in full against the oracle's
+  flatten and step, the rest by the fp16 writeback property.
+* 70B-class shard (4,412,500,000 params, N = 16) streamed in 23 buckets
+  through two chunk buffers: buckets 0, 11 and 22 checked in full, the rest
+  by the fp16 writeback property.
+"""
+import gc
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.flatten as ofl
+import oracle.zero_step as ozs
+import sharded_mixed_precision_step_amd as zs
+import workloads as wl
+from fullsize_util import (compare_with_expected, compare_with_oracle, oracle_check_only,
+                           rel_close, threads)
+from gpu_util import device, flags
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(autouse=True)
+def _free_device_memory():
+    yield
+    gc.collect()
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def _bits(t):
+    return t.view(torch.uint8)
+
+
+def _assert_writeback_property(master, p16, label, piece=1 << 24):
+    """p16 == fp16 round-to-nearest-even of master, and master finite, at
+    every element: the last step of the update, at any size."""
+    n = master.numel()
+
+    def work(k):
+        a, b = k * piece, min(n, (k + 1) * piece)
+        mh = master[a:b].cpu().numpy()
+        ph = p16[a:b].cpu().numpy()
+        assert np.isfinite(mh).all(), f"{label}: non-finite master in [{a}:{b}]"
+        assert np.array_equal(mh.astype(np.float16).view(np.uint16), ph.view(np.uint16)), \
+            f"{label}: p16 is not the rounded master in [{a}:{b}]"
+
+    with ThreadPoolExecutor(threads()) as ex:
+        list(ex.map(work, range((n + piece - 1) // piece)))
+
+
+def test_llama3_8b_shard_full():
+    dev = device()
+    w = wl.LLAMA3_8B_SHARD
+    print(f"case: full {w.name} n={w.n} N={w.n_replicas}", flush=True)
+    d = wl.device_shard(w, dev)
+    cur = (d["master"], d["m"], d["v"], d["p16"])
+    out = tuple(torch.empty_like(t) for t in cur)
+    hp = zs.adamw_params(w.hyper)
+    fl, sq = flags(dev)
+    zs.zero_shard_step_out(d["chunks"], w.loss_scale, *cur[:3], *out, hp, fl, sq)
+    torch.cuda.synchronize()
+    print("case: full llama3_8b_shard, single-pass step vs oracle", flush=True)
+    overflow, want_sq, expected = compare_with_oracle(d["chunks"], cur, out, w.hyper,
+                                                      w.loss_scale, label="single-pass ",
+                                                      keep_expected=True)
+    assert not overflow and int(fl.item()) == 0
+    assert rel_close(float(sq.item()), want_sq), (float(sq.item()), want_sq)
+    del out
+    fl2, sq2 = flags(dev)
+    zs.zero_overflow_check(d["chunks"], w.loss_scale, fl2, sq2)
+    zs.zero_shard_step(d["chunks"], w.loss_scale, *cur, hp)
+    torch.cuda.synchronize()
+    print("case: full llama3_8b_shard, two-pass step vs oracle", flush=True)
+    assert int(fl2.item()) == 0 and rel_close(float(sq2.item()), want_sq)
+    compare_with_expected(cur, expected, label="two-pass ")
+
+
+def test_overflow_workload_full():
+    dev = device()
+    w = wl.OVERFLOW
+    print(f"case: full {w.name} n={w.n} N={w.n_replicas} inject={w.n_inject}", flush=True)
+    d = wl.device_shard(w, dev)
+    wl.device_inject(d["chunks"], wl.injection_sites(w))
+    shard = zs.DoubleBufferedShard(d["master"], d["m"], d["v"], d["p16"])
+    snap = [t.clone() for t in shard.current]
+    scaler = zs.LossScaler.create(scale=w.loss_scale)
+    hp = zs.adamw_params(w.hyper)
+    fl, sq = flags(dev)
+    r = zs.committed_step(d["chunks"], shard, hp, scaler, fl, sq)
+    torch.cuda.synchronize()
+    want_flag, _ = oracle_check_only(d["chunks"], w.loss_scale)
+    assert want_flag and r.overflow and r.skipped
+    assert scaler.scale == w.loss_scale / 2 and hp.step == w.hyper.step and shard.cur == 0
+    for a, b in zip(snap, shard.current):
+        assert torch.equal(_bits(a), _bits(b))
+    fl2, _ = flags(dev)
+    zs.zero_overflow_check(d["chunks"], w.loss_scale, fl2, None)
+    torch.cuda.synchronize()
+    assert int(fl2.item()) == 1
+    # the retry: clean gradients drawn at the halved scale, same t
+    S2 = scaler.scale
+    wl.device_chunks(w, dev, offset_seed=1, loss_scale=S2, out=d["chunks"])
+    state_in = shard.current
+    r2 = zs.committed_step(d["chunks"], shard, hp, scaler, fl, sq)
+    torch.cuda.synchronize()
+    assert not r2.overflow and not r2.skipped and hp.step == w.hyper.step + 1
+    print("case: full overflow workload, clean retry vs oracle", flush=True)
+    overflow, want_sq, _ = compare_with_oracle(d["chunks"], state_in, shard.current, w.hyper,
+                                               S2, label="retry ")
+    assert not overflow and rel_close(r2.sqnorm, want_sq)
+
+
+ZERO2_SAMPLED = (0, 3, 4, 159)
+
+
+def test_zero2_bucketed_full():
+    dev = device()
+    w = wl.ZERO2
+    N, r, S = w.n_replicas, wl.ZERO2_RANK, w.loss_scale
+    align, pad = wl.ZERO2_ALIGN, wl.ZERO2_ALIGN * w.n_replicas
+    sizes = [int(np.prod(s)) for _, s in wl.zero2_tensors()]
+    plan = wl.zero2_bucket_plan()
+    layouts = [ofl.bucket_layout([sizes[k] for k in idx], align, pad) for idx in plan]
+    assert len(plan) == 160 and sum(lay[-1] for lay in layouts) // N == w.n
+    print(f"case: full {w.name} buckets={len(plan)} rank={r} n={w.n}", flush=True)
+    st = wl.device_state(w, dev)
+    cur = (st["master"], st["m"], st["v"], st["p16"])
+    out = tuple(torch.empty_like(t) for t in cur)
+    lmax = max(lay[-1] for lay in layouts)
+    buckets = [torch.empty(lmax, dtype=torch.float16, device=dev) for _ in range(N)]
+    hp = zs.adamw_params(w.hyper)
+    fl, sq = flags(dev)
+    off = 0
+    for b, idx in enumerate(plan):
+        L = layouts[b][-1]
+        sl = L // N
+        reps = [[wl.zero2_device_tensor(i, k, dev) for k in idx] for i in range(N)]
+        for i in range(N):
+            offs = zs.zero_bucket_flatten(reps[i], buckets[i], align=align, pad_multiple=pad)
+            assert offs == layouts[b], (b, offs, layouts[b])
+        chunks = [bk[r * sl:(r + 1) * sl] for bk in buckets]
+        s_in = tuple(t[off:off + sl] for t in cur)
+        s_out = tuple(t[off:off + sl] for t in out)
+        zs.zero_shard_step_out(chunks, S, *s_in[:3], *s_out, hp, fl, sq)
+        if b in ZERO2_SAMPLED:
+            fb, sb = flags(dev)
+            zs.zero_overflow_check(chunks, S, fb, sb)
+            torch.cuda.synchronize()
+            print(f"case: zero2 bucket {b} (L={L}) flatten and step vs oracle", flush=True)
+            want_b = [ofl.flatten([t.cpu().numpy() for t in reps[i]], align, pad)[0]
+                      for i in range(N)]
+            for i in range(N):
+                got = buckets[i][:L].cpu().numpy()
+                assert np.array_equal(got.view(np.uint16), want_b[i].view(np.uint16)), (b, i)
+            want = ozs.shard_step([wb[r * sl:(r + 1) * sl] for wb in want_b],
+                                  *[t.cpu().numpy() for t in s_in], w.hyper, S)
+            assert not want.overflow and int(fb.item()) == 0
+            assert rel_close(float(sb.item()), want.sqnorm)
+            for name, t, ref in zip(("master", "m", "v"), s_out[:3], (want.master, want.m, want.v)):
+                assert np.array_equal(t.cpu().numpy().view(np.uint32), ref.view(np.uint32)), (b, name)
+            assert np.array_equal(s_out[3].cpu().numpy().view(np.uint16), want.p16.view(np.uint16))
+        del reps
+        off += sl
+    torch.cuda.synchronize()
+    assert off == w.n and int(fl.item()) == 0
+    _assert_writeback_property(out[0], out[3], "zero2")
+
+
+LLAMA70B_SAMPLED = (0, 11, 22)
+
+
+def test_llama70b_shard_streamed():
+    dev = device()
+    w = wl.LLAMA70B_SHARD
+    N, S = w.n_replicas, w.loss_scale
+    assert sum(w.buckets) == w.n
+    print(f"case: full {w.name} n={w.n} N={N} buckets={len(w.buckets)}", flush=True)
+    st = wl.device_state(w, dev)
+    cur = (st["master"], st["m"], st["v"], st["p16"])
+    out = tuple(torch.empty_like(t) for t in cur)
+    bmax = max(w.buckets)
+    bufs = [[torch.empty(bmax, dtype=torch.float16, device=dev) for _ in range(N)]
+            for _ in range(2)]
+    hp = zs.adamw_params(w.hyper)
+    fl, sq = flags(dev)
+    off = 0
+    for b, nb in enumerate(w.buckets):
+        chunks = [c[:nb] for c in bufs[b % 2]]
+        wl.device_chunks(w, dev, n=nb, offset_seed=100 + b, out=chunks)
+        s_in = tuple(t[off:off + nb] for t in cur)
+        s_out = tuple(t[off:off + nb] for t in out)
+        zs.zero_shard_step_out(chunks, S, *s_in[:3], *s_out, hp, fl, sq)
+        if b in LLAMA70B_SAMPLED:
+            fb, sb = flags(dev)
+            zs.zero_overflow_check(chunks, S, fb, sb)
+            torch.cuda.synchronize()
+            print(f"case: llama70b bucket {b} (n={nb}) step vs oracle", flush=True)
+            overflow, want_sq, _ = compare_with_oracle(chunks, s_in, s_out, w.hyper, S,
+                                                       label=f"bucket {b} ")
+            assert not overflow and int(fb.item()) == 0 and rel_close(float(sb.item()), want_sq)
+        off += nb
+    torch.cuda.synchronize()
+    assert int(fl.item()) == 0
+    _assert_writeback_property(out[0], out[3], "llama70b")

@@ -103,6 +103,7 @@ LLAMA70B_SHARD = ShardWorkload(
     buckets=tuple([200_000_000] * 22 + [12_500_000]))
 
 WORKLOADS = {w.name: w for w in (TINY, LLAMA3_8B_SHARD, OVERFLOW, LLAMA70B_SHARD)}
+# (the ZeRO-2 bucketed workload, ZERO2, is defined below with its bucket plan)
 
 
 # ---------------------------------------------------------------------------
@@ -160,6 +161,31 @@ def zero2_bucket_plan(cap: int = ZERO2_BUCKET_CAP, align: int = ZERO2_ALIGN
     if cur:
         buckets.append(cur)
     return buckets
+
+
+ZERO2_GRAD_SIGMA = 1e-4
+ZERO2_LOSS_SCALE = 65536.0
+ZERO2_RANK = 3          # the rank whose shard the bucketed workload updates
+
+
+# One rank's shard of the bucketed workload: slice ZERO2_RANK of every bucket.
+# The 160 buckets are 96 of 58,720,256 elements (one MLP gradient each) and
+# 64 of 33,558,528 (three attention-side gradients each) once tensor starts
+# are aligned to 256 and lengths to 256 * 8, so the shard holds
+# (96 * 58,720,256 + 64 * 33,558,528) / 8 = 973,111,296 params.
+ZERO2 = ShardWorkload(
+    name="zero2_bucketed", wid=ZERO2_WID, n=973_111_296, n_replicas=ZERO2_REPLICAS,
+    grad_sigma=ZERO2_GRAD_SIGMA, loss_scale=ZERO2_LOSS_SCALE, hyper=AdamWHyper(step=1000),
+    m_sigma=1e-4, v_sigma=1e-8)
+
+
+def zero2_device_tensor(replica: int, k: int, device):
+    """Replica ``replica``'s fp16 gradient of tensor ``k`` (flat), loss-scaled."""
+    torch = _torch()
+    numel = int(np.prod(zero2_tensors()[k][1]))
+    t = torch.empty(numel, dtype=torch.float16, device=device)
+    return device_fill_normal(t, seed_of(ZERO2_WID, 100 + replica, ARRAY_GRAD, k),
+                              ZERO2_GRAD_SIGMA * ZERO2_LOSS_SCALE)
 
 
 # ---------------------------------------------------------------------------
@@ -261,18 +287,11 @@ def device_fill_normal(out, seed: int, sigma: float, absolute: bool = False):
     return out
 
 
-def device_shard(w: ShardWorkload, device, n: int | None = None,
-                 offset_seed: int = 0, stagger_bytes: int = 0):
-    """Device tensors for workload ``w``: N fp16 chunks, fp32 master/m/v and
-    the fp16 params.  All are separate allocations (16-byte aligned)."""
+def device_state(w: ShardWorkload, device, n: int | None = None, offset_seed: int = 0):
+    """Device fp32 master, m, v and the fp16 params for workload ``w``."""
     torch = _torch()
     n = w.n if n is None else n
     key = (w.wid, offset_seed)
-    chunks = []
-    for i in range(w.n_replicas):
-        c = torch.empty(n, dtype=torch.float16, device=device)
-        device_fill_normal(c, seed_of(*key, ARRAY_GRAD, i), w.grad_sigma * w.loss_scale)
-        chunks.append(c)
     master = torch.empty(n, dtype=torch.float32, device=device)
     device_fill_normal(master, seed_of(*key, ARRAY_MASTER), w.master_sigma)
     m = torch.zeros(n, dtype=torch.float32, device=device)
@@ -282,7 +301,30 @@ def device_shard(w: ShardWorkload, device, n: int | None = None,
     if w.v_sigma:
         device_fill_normal(v, seed_of(*key, ARRAY_V), w.v_sigma, absolute=True)
     p16 = master.to(torch.float16)
-    return dict(chunks=chunks, master=master, m=m, v=v, p16=p16)
+    return dict(master=master, m=m, v=v, p16=p16)
+
+
+def device_chunks(w: ShardWorkload, device, n: int | None = None, offset_seed: int = 0,
+                  loss_scale: float | None = None, out=None):
+    """The N replica gradient chunks of ``w`` (fp16(N(0, sigma) * S)), drawn
+    into ``out`` (a list of N device fp16 tensors) if given."""
+    torch = _torch()
+    n = w.n if n is None else n
+    S = w.loss_scale if loss_scale is None else loss_scale
+    key = (w.wid, offset_seed)
+    if out is None:
+        out = [torch.empty(n, dtype=torch.float16, device=device) for _ in range(w.n_replicas)]
+    for i, c in enumerate(out):
+        device_fill_normal(c[:n], seed_of(*key, ARRAY_GRAD, i), w.grad_sigma * S)
+    return out
+
+
+def device_shard(w: ShardWorkload, device, n: int | None = None, offset_seed: int = 0):
+    """Device tensors for workload ``w``: N fp16 chunks, fp32 master/m/v and
+    the fp16 params.  All are separate allocations (16-byte aligned)."""
+    d = device_state(w, device, n=n, offset_seed=offset_seed)
+    d["chunks"] = device_chunks(w, device, n=n, offset_seed=offset_seed)
+    return d
 
 
 def device_inject(chunks: Sequence, sites) -> None:
