@@ -176,6 +176,49 @@ int zero_shard_step_out(const void* const* grad_chunks, int32_t n_chunks, int64_
                         const zero_adamw_params* hp, int32_t* d_overflow, double* d_sqnorm,
                         void* stream);
 
+/* One bucket's slice of a rank's shard (ZeRO-2: the part of a gradient bucket
+ * this rank owns).  HOST struct. */
+typedef struct zero_bucket_slice {
+    const void* const* grad_chunks; /* HOST array of n_chunks DEVICE pointers, each
+                                       to n fp16 values, 16-byte aligned        */
+    int64_t n;                      /* params in the slice, >= 0                */
+    int64_t offset;                 /* first state element of the slice, a
+                                       multiple of 8                            */
+} zero_bucket_slice;
+
+/*
+ * zero_shard_step_buckets -- the fused update over many bucket slices.
+ *
+ * ZeRO-2 hands gradients to their owner bucket by bucket (ZeRO notes,
+ * rkmt.cn/news/44736, section "Deepspeed ZeRO-2", sync step: each finished
+ * bucket is sent to the rank that owns that part and freed).  This call
+ * performs, for every slice k, exactly what zero_shard_step_out does for
+ * slice k's n params: its chunks against state elements
+ * [offset_k, offset_k + n_k) of the *_in arrays, written to the same elements
+ * of the *_out arrays, with the flag and squared norm of all slices
+ * accumulated into *d_overflow / *d_sqnorm.  The work is enqueued as a few
+ * launches (up to 32 slices, and up to 256 chunk pointers, per launch), not
+ * one launch per bucket.  State elements outside every slice are not touched.
+ *
+ *   slices         HOST array of n_slices slices; slices must not share a
+ *                  state element; a slice with n == 0 is skipped
+ *   n_chunks       N, 1..ZERO_MAX_CHUNKS, the same for every slice
+ *   loss_scale     S, finite and > 0
+ *   n_state        elements of each state array, >= every offset + n
+ *   *_in, *_out    as for zero_shard_step_out, each of n_state elements
+ *   hp, d_overflow, d_sqnorm, stream   as for zero_shard_step_out
+ * Validation covers every slice before anything is enqueued.  Returns ZERO_OK,
+ * ZERO_EINVAL, ZERO_EALIGN (a chunk not 16-byte aligned, an offset not a
+ * multiple of 8) or ZERO_EHIP (a launch failed; earlier launches of the call
+ * may have been enqueued).
+ */
+int zero_shard_step_buckets(const zero_bucket_slice* slices, int32_t n_slices, int32_t n_chunks,
+                            float loss_scale, int64_t n_state, const float* master_in,
+                            const float* exp_avg_in, const float* exp_avg_sq_in,
+                            float* master_out, float* exp_avg_out, float* exp_avg_sq_out,
+                            void* param_fp16_out, const zero_adamw_params* hp,
+                            int32_t* d_overflow, double* d_sqnorm, void* stream);
+
 /*
  * zero_bucket_flatten -- pack whole fp16 gradient tensors into one bucket.
  *

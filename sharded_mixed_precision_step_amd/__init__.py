@@ -31,7 +31,8 @@ ZERO_EHIP = -4
 ZERO_MAX_CHUNKS = 64
 
 EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
-            "zero_bucket_flatten", "zero_update_loss_scale", "zero_last_error_string")
+            "zero_shard_step_buckets", "zero_bucket_flatten", "zero_update_loss_scale",
+            "zero_last_error_string")
 
 
 class ZeroStepError(RuntimeError):
@@ -60,6 +61,11 @@ class LossScaler(ctypes.Structure):
                    growth_interval, 0, 0)
 
 
+class BucketSliceC(ctypes.Structure):
+    _fields_ = [("grad_chunks", ctypes.POINTER(ctypes.c_void_p)), ("n", ctypes.c_int64),
+                ("offset", ctypes.c_int64)]
+
+
 def adamw_params(hyper) -> AdamWParams:
     """AdamWParams from any object with lr, beta1, beta2, eps, weight_decay,
     step, decoupled_wd and bias_correction attributes."""
@@ -80,6 +86,9 @@ def _load() -> ctypes.CDLL:
                                     ctypes.POINTER(AdamWParams), vp, vp, vp]
     lib.zero_shard_step_out.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                          ctypes.POINTER(AdamWParams), vp, vp, vp]
+    lib.zero_shard_step_buckets.argtypes = [ctypes.POINTER(BucketSliceC), i32, i32,
+                                             ctypes.c_float, i64, vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.POINTER(AdamWParams), vp, vp, vp]
     lib.zero_bucket_flatten.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), i32, i64, i64,
                                         vp, i64, ctypes.POINTER(ctypes.c_int64), vp]
     lib.zero_update_loss_scale.argtypes = [ctypes.POINTER(LossScaler), i32,
@@ -188,6 +197,69 @@ def zero_shard_step_out(grad_chunks: Sequence[torch.Tensor], loss_scale: float,
         hp = adamw_params(hp)
     _check(lib.zero_shard_step_out(
         _ptr_array(ptrs), len(ptrs), n, float(loss_scale),
+        _dev(master_in, torch.float32, "master_in"), _dev(exp_avg_in, torch.float32, "exp_avg_in"),
+        _dev(exp_avg_sq_in, torch.float32, "exp_avg_sq_in"),
+        _dev(master_out, torch.float32, "master_out"),
+        _dev(exp_avg_out, torch.float32, "exp_avg_out"),
+        _dev(exp_avg_sq_out, torch.float32, "exp_avg_sq_out"),
+        _dev(param_fp16_out, torch.float16, "param_fp16_out"), ctypes.byref(hp),
+        _opt(d_overflow, torch.int32, "d_overflow"), _opt(d_sqnorm, torch.float64, "d_sqnorm"),
+        _stream(stream)))
+
+
+class BucketSlices:
+    """A table of bucket slices for zero_shard_step_buckets, marshalled once.
+
+    ``slices`` is a sequence of (chunks, offset): the N replica gradient
+    chunks of one bucket's slice (fp16 device tensors of equal length) and the
+    slice's first element in the shard's state arrays.  The tensors are
+    referenced, so their memory stays valid while the table exists; their
+    contents may change between steps (bucket buffers are reused)."""
+
+    def __init__(self, slices):
+        self.tensors = []
+        self.ptr_arrays = []
+        self.n_chunks = None
+        self.table = (BucketSliceC * max(len(slices), 1))()
+        for k, (chunks, offset) in enumerate(slices):
+            if self.n_chunks is None:
+                self.n_chunks = len(chunks)
+            elif len(chunks) != self.n_chunks:
+                raise ValueError(f"slice {k} has {len(chunks)} chunks, expected {self.n_chunks}")
+            n = chunks[0].numel()
+            ptrs = []
+            for i, c in enumerate(chunks):
+                if c.numel() != n:
+                    raise ValueError(f"slice {k} chunk {i} has {c.numel()} elements, expected {n}")
+                ptrs.append(_dev(c, torch.float16, f"slice {k} chunk {i}"))
+            arr = _ptr_array(ptrs)
+            self.ptr_arrays.append(arr)
+            self.tensors.append(list(chunks))
+            self.table[k].grad_chunks = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+            self.table[k].n = n
+            self.table[k].offset = int(offset)
+        self.count = len(slices)
+        if self.n_chunks is None:
+            self.n_chunks = 1
+
+
+def zero_shard_step_buckets(slices: BucketSlices, loss_scale: float, master_in: torch.Tensor,
+                            exp_avg_in: torch.Tensor, exp_avg_sq_in: torch.Tensor,
+                            master_out: torch.Tensor, exp_avg_out: torch.Tensor,
+                            exp_avg_sq_out: torch.Tensor, param_fp16_out: torch.Tensor,
+                            hp: AdamWParams, d_overflow: Optional[torch.Tensor] = None,
+                            d_sqnorm: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Fused update over every bucket slice of ``slices`` (see zero_step.h)."""
+    n = master_in.numel()
+    for name, t in (("exp_avg_in", exp_avg_in), ("exp_avg_sq_in", exp_avg_sq_in),
+                    ("master_out", master_out), ("exp_avg_out", exp_avg_out),
+                    ("exp_avg_sq_out", exp_avg_sq_out), ("param_fp16_out", param_fp16_out)):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    if not isinstance(hp, AdamWParams):
+        hp = adamw_params(hp)
+    _check(lib.zero_shard_step_buckets(
+        slices.table, slices.count, slices.n_chunks, float(loss_scale), n,
         _dev(master_in, torch.float32, "master_in"), _dev(exp_avg_in, torch.float32, "exp_avg_in"),
         _dev(exp_avg_sq_in, torch.float32, "exp_avg_sq_in"),
         _dev(master_out, torch.float32, "master_out"),

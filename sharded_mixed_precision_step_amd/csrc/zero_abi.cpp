@@ -6,6 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "zero_internal.h"
 #include "zero_step.h"
 
@@ -57,6 +60,12 @@ int check_chunks(const void* const* grad_chunks, int32_t n_chunks, int64_t n, fl
         return fail(ZERO_EINVAL, "loss_scale = %g is not finite and > 0",
                     static_cast<double>(loss_scale));
     memset(table, 0, sizeof *table);
+    gs->n_f = static_cast<float>(n_chunks);
+    gs->inv_n = 1.0f / gs->n_f;
+    gs->mean_by_mul = is_pow2(gs->n_f) ? 1 : 0;
+    gs->s = loss_scale;
+    gs->inv_s = 1.0f / loss_scale;
+    gs->unscale_by_mul = (is_pow2(loss_scale) && finite_f(gs->inv_s)) ? 1 : 0;
     if (n == 0) return ZERO_OK;  // nothing is read: empty (NULL) chunks are fine
     for (int32_t c = 0; c < n_chunks; ++c) {
         if (!grad_chunks[c]) return fail(ZERO_EINVAL, "grad_chunks[%d] is NULL", c);
@@ -64,12 +73,6 @@ int check_chunks(const void* const* grad_chunks, int32_t n_chunks, int64_t n, fl
             return fail(ZERO_EALIGN, "grad_chunks[%d] is not 16-byte aligned", c);
         table->p[c] = static_cast<const uint16_t*>(grad_chunks[c]);
     }
-    gs->n_f = static_cast<float>(n_chunks);
-    gs->inv_n = 1.0f / gs->n_f;
-    gs->mean_by_mul = is_pow2(gs->n_f) ? 1 : 0;
-    gs->s = loss_scale;
-    gs->inv_s = 1.0f / loss_scale;
-    gs->unscale_by_mul = (is_pow2(loss_scale) && finite_f(gs->inv_s)) ? 1 : 0;
     return ZERO_OK;
 }
 
@@ -112,22 +115,12 @@ int adam_scalars(const zero_adamw_params* hp, zero::AdamScalars* as) {
     return ZERO_OK;
 }
 
-// Validation and launch shared by the in-place and the out-of-place step.
-// Output k may equal input k exactly (in place); otherwise no output may
-// share a byte with any input, another output or a gradient chunk.
-int shard_step_common(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
-                      float loss_scale, const float* master_in, const float* exp_avg_in,
-                      const float* exp_avg_sq_in, float* master_out, float* exp_avg_out,
-                      float* exp_avg_sq_out, void* param_fp16_out, const zero_adamw_params* hp,
-                      int32_t* d_overflow, double* d_sqnorm, void* stream, const char* who) {
-    zero::ChunkTable table;
-    zero::GradScalars gs;
-    zero::AdamScalars as;
-    int rc = check_chunks(grad_chunks, n_chunks, n, loss_scale, &table, &gs);
-    if (rc) return rc;
-    if ((rc = adam_scalars(hp, &as))) return rc;
-    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
-    if (n == 0) return ok();  // nothing is read or written
+// The state arrays of a step over n elements: inputs and outputs present and
+// 16-byte aligned; output k may be exactly input k (in place), otherwise no
+// output shares a byte with any input or another output.
+int check_state(int64_t n, const float* master_in, const float* exp_avg_in,
+                const float* exp_avg_sq_in, float* master_out, float* exp_avg_out,
+                float* exp_avg_sq_out, void* param_fp16_out, const char* who) {
     const void* in[3] = {master_in, exp_avg_in, exp_avg_sq_in};
     const void* out[4] = {master_out, exp_avg_out, exp_avg_sq_out, param_fp16_out};
     static const char* in_names[3] = {"master_in", "exp_avg_in", "exp_avg_sq_in"};
@@ -151,10 +144,47 @@ int shard_step_common(const void* const* grad_chunks, int32_t n_chunks, int64_t 
         for (int b = 0; b < 3; ++b)
             if (!(a == b && out[a] == in[b]) && overlap(out[a], out_bytes[a], in[b], 4 * n))
                 return fail(ZERO_EINVAL, "%s: %s overlaps %s", who, out_names[a], in_names[b]);
-        for (int32_t c = 0; c < n_chunks; ++c)
-            if (overlap(out[a], out_bytes[a], grad_chunks[c], 2 * n))
-                return fail(ZERO_EINVAL, "%s: %s overlaps grad_chunks[%d]", who, out_names[a], c);
     }
+    return ZERO_OK;
+}
+
+// No output array (n elements) shares a byte with [p, p + bytes), chunk c.
+int check_outputs_clear_of(int64_t n, const float* master_out, const float* exp_avg_out,
+                           const float* exp_avg_sq_out, const void* param_fp16_out,
+                           const void* p, int64_t bytes, const char* who, int32_t c) {
+    const void* out[4] = {master_out, exp_avg_out, exp_avg_sq_out, param_fp16_out};
+    static const char* out_names[4] = {"master_out", "exp_avg_out", "exp_avg_sq_out",
+                                       "param_fp16_out"};
+    const int64_t out_bytes[4] = {4 * n, 4 * n, 4 * n, 2 * n};
+    for (int a = 0; a < 4; ++a)
+        if (overlap(out[a], out_bytes[a], p, bytes))
+            return fail(ZERO_EINVAL, "%s: %s overlaps grad_chunks[%d]", who, out_names[a], c);
+    return ZERO_OK;
+}
+
+// Validation and launch shared by the in-place and the out-of-place step.
+// Output k may equal input k exactly (in place); otherwise no output may
+// share a byte with any input, another output or a gradient chunk.
+int shard_step_common(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                      float loss_scale, const float* master_in, const float* exp_avg_in,
+                      const float* exp_avg_sq_in, float* master_out, float* exp_avg_out,
+                      float* exp_avg_sq_out, void* param_fp16_out, const zero_adamw_params* hp,
+                      int32_t* d_overflow, double* d_sqnorm, void* stream, const char* who) {
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    zero::AdamScalars as;
+    int rc = check_chunks(grad_chunks, n_chunks, n, loss_scale, &table, &gs);
+    if (rc) return rc;
+    if ((rc = adam_scalars(hp, &as))) return rc;
+    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
+    if (n == 0) return ok();  // nothing is read or written
+    if ((rc = check_state(n, master_in, exp_avg_in, exp_avg_sq_in, master_out, exp_avg_out,
+                          exp_avg_sq_out, param_fp16_out, who)))
+        return rc;
+    for (int32_t c = 0; c < n_chunks; ++c)
+        if ((rc = check_outputs_clear_of(n, master_out, exp_avg_out, exp_avg_sq_out,
+                                         param_fp16_out, grad_chunks[c], 2 * n, who, c)))
+            return rc;
     const zero::ShardState st = {master_in,  exp_avg_in,     exp_avg_sq_in,
                                  master_out, exp_avg_out,    exp_avg_sq_out,
                                  static_cast<uint16_t*>(param_fp16_out)};
@@ -201,6 +231,111 @@ int zero_shard_step_out(const void* const* grad_chunks, int32_t n_chunks, int64_
                              exp_avg_sq_in, master_out, exp_avg_out, exp_avg_sq_out,
                              param_fp16_out, hp, d_overflow, d_sqnorm, stream,
                              "zero_shard_step_out");
+}
+
+int zero_shard_step_buckets(const zero_bucket_slice* slices, int32_t n_slices, int32_t n_chunks,
+                            float loss_scale, int64_t n_state, const float* master_in,
+                            const float* exp_avg_in, const float* exp_avg_sq_in,
+                            float* master_out, float* exp_avg_out, float* exp_avg_sq_out,
+                            void* param_fp16_out, const zero_adamw_params* hp,
+                            int32_t* d_overflow, double* d_sqnorm, void* stream) {
+    static const char* who = "zero_shard_step_buckets";
+    if (n_slices < 0) return fail(ZERO_EINVAL, "%s: n_slices < 0", who);
+    if (n_slices > 0 && !slices) return fail(ZERO_EINVAL, "%s: slices is NULL", who);
+    if (n_chunks < 1 || n_chunks > ZERO_MAX_CHUNKS)
+        return fail(ZERO_EINVAL, "%s: n_chunks = %d outside [1, %d]", who, n_chunks,
+                    ZERO_MAX_CHUNKS);
+    if (n_state < 0) return fail(ZERO_EINVAL, "%s: n_state < 0", who);
+    zero::ChunkTable unused;
+    zero::GradScalars gs;
+    zero::AdamScalars as;
+    const void* no_chunks[1] = {nullptr};
+    int rc = check_chunks(no_chunks, n_chunks, 0, loss_scale, &unused, &gs);  // scalars only
+    if (rc) return rc;
+    if ((rc = adam_scalars(hp, &as))) return rc;
+    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
+    // every slice inside the state arrays, 8-element aligned, chunks present
+    int64_t live = 0;
+    for (int32_t k = 0; k < n_slices; ++k) {
+        const zero_bucket_slice& b = slices[k];
+        if (b.n < 0 || b.offset < 0)
+            return fail(ZERO_EINVAL, "%s: slice %d has n or offset < 0", who, k);
+        if (b.offset % zero::kPack != 0)
+            return fail(ZERO_EALIGN, "%s: slice %d offset %lld is not a multiple of 8", who, k,
+                        static_cast<long long>(b.offset));
+        if (b.n > n_state - b.offset)
+            return fail(ZERO_EINVAL, "%s: slice %d ends past n_state", who, k);
+        if (b.n == 0) continue;
+        ++live;
+        if (!b.grad_chunks) return fail(ZERO_EINVAL, "%s: slice %d grad_chunks is NULL", who, k);
+        for (int32_t c = 0; c < n_chunks; ++c) {
+            if (!b.grad_chunks[c])
+                return fail(ZERO_EINVAL, "%s: slice %d grad_chunks[%d] is NULL", who, k, c);
+            if (!aligned(b.grad_chunks[c], 16))
+                return fail(ZERO_EALIGN, "%s: slice %d grad_chunks[%d] is not 16-byte aligned",
+                            who, k, c);
+        }
+    }
+    if (live == 0) return ok();
+    // slices may not share a state element: sort by offset, compare neighbours
+    std::vector<int32_t> order;
+    order.reserve(static_cast<size_t>(live));
+    for (int32_t k = 0; k < n_slices; ++k)
+        if (slices[k].n > 0) order.push_back(k);
+    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        return slices[a].offset < slices[b].offset;
+    });
+    for (size_t i = 1; i < order.size(); ++i) {
+        const zero_bucket_slice& a = slices[order[i - 1]];
+        if (a.offset + a.n > slices[order[i]].offset)
+            return fail(ZERO_EINVAL, "%s: slices %d and %d overlap", who, order[i - 1], order[i]);
+    }
+    if ((rc = check_state(n_state, master_in, exp_avg_in, exp_avg_sq_in, master_out, exp_avg_out,
+                          exp_avg_sq_out, param_fp16_out, who)))
+        return rc;
+    for (int32_t k = 0; k < n_slices; ++k) {
+        if (slices[k].n == 0) continue;
+        for (int32_t c = 0; c < n_chunks; ++c)
+            if ((rc = check_outputs_clear_of(n_state, master_out, exp_avg_out, exp_avg_sq_out,
+                                             param_fp16_out, slices[k].grad_chunks[c],
+                                             2 * slices[k].n, who, c)))
+                return rc;
+    }
+    // launches of up to kMaxBucketsPerLaunch slices and kBucketTablePtrs chunk pointers
+    const zero::ShardState st = {master_in,  exp_avg_in,  exp_avg_sq_in, master_out,
+                                 exp_avg_out, exp_avg_sq_out,
+                                 static_cast<uint16_t*>(param_fp16_out)};
+    int per_launch = zero::kBucketTablePtrs / n_chunks;
+    if (per_launch > zero::kMaxBucketsPerLaunch) per_launch = zero::kMaxBucketsPerLaunch;
+    const int64_t kMaxGrid = 0x7fffffff;
+    zero::BucketTable t;
+    memset(&t, 0, sizeof t);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    for (int32_t k = 0; k < n_slices; ++k) {
+        const zero_bucket_slice& b = slices[k];
+        if (b.n == 0) continue;
+        const int64_t tiles = zero::step_tiles(b.n);
+        if (t.count > 0 && (t.count == per_launch || t.tile_start[t.count] + tiles > kMaxGrid)) {
+            const hipError_t e = zero::launch_bucket_step(t, n_chunks, gs, as, st, d_overflow,
+                                                          d_sqnorm, hs);
+            if (e != hipSuccess) return hip_fail(e, who);
+            memset(&t, 0, sizeof t);
+        }
+        if (tiles > kMaxGrid) return fail(ZERO_EINVAL, "%s: slice %d is too long", who, k);
+        const int i = t.count;
+        t.n[i] = b.n;
+        t.offset[i] = b.offset;
+        for (int32_t c = 0; c < n_chunks; ++c)
+            t.chunk[i * n_chunks + c] = static_cast<const uint16_t*>(b.grad_chunks[c]);
+        t.tile_start[i + 1] = t.tile_start[i] + tiles;
+        t.count = i + 1;
+    }
+    if (t.count > 0) {
+        const hipError_t e = zero::launch_bucket_step(t, n_chunks, gs, as, st, d_overflow,
+                                                      d_sqnorm, hs);
+        if (e != hipSuccess) return hip_fail(e, who);
+    }
+    return ok();
 }
 
 int zero_bucket_flatten(const void* const* tensors, const int64_t* numels, int32_t n_tensors,

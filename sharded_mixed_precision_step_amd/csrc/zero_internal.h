@@ -15,6 +15,8 @@ constexpr int kWaveSpan = 2;       // packs per lane in a step tile
 constexpr int kTilePacks = kBlock * kWaveSpan;  // packs per step tile (one block)
 constexpr int kCheckBlocksPerCU = 6;            // resident blocks of the check kernel
 constexpr int kFlattenBatch = 32;  // tensors per flatten launch (kernel-argument table)
+constexpr int kMaxBucketsPerLaunch = 32;  // bucket slices per multi-bucket step launch
+constexpr int kBucketTablePtrs = 256;     // chunk pointers per multi-bucket step launch
 
 // Replica gradient chunks, passed by value in the kernel arguments.
 struct ChunkTable {
@@ -59,6 +61,19 @@ struct ShardState {
     uint16_t* param_fp16_out;
 };
 
+// Bucket slices of one multi-bucket step launch, passed by value in the kernel
+// arguments (under 3 KiB).  Slice k: n[k] params whose state starts at element
+// offset[k], chunk pointers chunk[k * N .. k * N + N), blocks
+// [tile_start[k], tile_start[k + 1]).
+struct BucketTable {
+    int64_t tile_start[kMaxBucketsPerLaunch + 1];
+    int64_t n[kMaxBucketsPerLaunch];
+    int64_t offset[kMaxBucketsPerLaunch];
+    const uint16_t* chunk[kBucketTablePtrs];
+    int32_t count;
+    int32_t pad_;
+};
+
 struct FlattenDesc {
     const uint16_t* src;  // fp16 bits, 2-byte aligned
     int64_t numel;        // elements of the tensor
@@ -80,6 +95,12 @@ hipError_t launch_shard_step(const ChunkTable& chunks, int n_chunks, int64_t n,
                              const GradScalars& gs, const AdamScalars& as,
                              const ShardState& st, int32_t* d_overflow,
                              double* d_sqnorm, hipStream_t stream);
+
+hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScalars& gs,
+                              const AdamScalars& as, const ShardState& st, int32_t* d_overflow,
+                              double* d_sqnorm, hipStream_t stream);
+
+int64_t step_tiles(int64_t n);  // blocks of the fused step over n params
 
 hipError_t launch_bucket_flatten(const FlattenTable& table, int count,
                                  int64_t max_slot_len, uint16_t* bucket,

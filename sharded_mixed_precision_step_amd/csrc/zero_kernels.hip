@@ -104,24 +104,24 @@ __device__ __forceinline__ void publish(bool bad, double sq, int32_t* d_overflow
 }
 
 template <int NC>
-__device__ __forceinline__ float replica_sum1(const ChunkTable& chunks, int n_chunks,
+__device__ __forceinline__ float replica_sum1(const uint16_t* const* chunks, int n_chunks,
                                               int64_t j) {
-    float s = load_widen1(chunks.p[0], j);
+    float s = load_widen1(chunks[0], j);
     const int nc = NC > 0 ? NC : n_chunks;
-    for (int c = 1; c < nc; ++c) s += load_widen1(chunks.p[c], j);
+    for (int c = 1; c < nc; ++c) s += load_widen1(chunks[c], j);
     return s;
 }
 
 // Sum of the N replicas' pack `pack`, widened, in replica order 0..N-1.
 template <int NC>
-__device__ __forceinline__ f8 replica_sum8(const ChunkTable& chunks, int n_chunks,
+__device__ __forceinline__ f8 replica_sum8(const uint16_t* const* chunks, int n_chunks,
                                            int64_t pack) {
-    f8 s = load_widen8(chunks.p[0], pack);
+    f8 s = load_widen8(chunks[0], pack);
     if constexpr (NC > 0) {
 #pragma unroll
-        for (int c = 1; c < NC; ++c) s += load_widen8(chunks.p[c], pack);
+        for (int c = 1; c < NC; ++c) s += load_widen8(chunks[c], pack);
     } else {
-        for (int c = 1; c < n_chunks; ++c) s += load_widen8(chunks.p[c], pack);
+        for (int c = 1; c < n_chunks; ++c) s += load_widen8(chunks[c], pack);
     }
     return s;
 }
@@ -135,7 +135,7 @@ __device__ __forceinline__ f8 replica_sum8(const ChunkTable& chunks, int n_chunk
 // the *_out arrays), so in-place (in == out) and out-of-place both hold.
 // FULL: every pack of the tile exists (all tiles but possibly the last).
 template <int NC, bool REDUCE, bool FULL>
-__device__ __forceinline__ void step_tile(const ChunkTable& chunks, int n_chunks, int64_t packs,
+__device__ __forceinline__ void step_tile(const uint16_t* const* chunks, int n_chunks, int64_t packs,
                                           int64_t first, const GradScalars& gs,
                                           const AdamScalars& as, const ShardState& st, bool& bad,
                                           double& sq) {
@@ -191,27 +191,25 @@ __device__ __forceinline__ void step_tile(const ChunkTable& chunks, int n_chunks
     }
 }
 
-// The fused step.  One block per tile (a one-shot grid, not a grid-stride
-// loop): on MI355X a stream over this many arrays (N chunks, three state
-// arrays read and written, the fp16 params) sustains more HBM bandwidth when
-// blocks retire after one tile than when resident blocks loop.
+// One block's share of the fused step: tile `tile` of a shard (or bucket
+// slice) of n params whose chunks and state start at the given pointers.
+// `last`: this is the shard's last tile, so it also updates the n % 8 params
+// after the last full pack, one per thread.
 template <int NC, bool REDUCE>
-__global__ __launch_bounds__(kBlock) void shard_step_kernel(
-    ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs, AdamScalars as, ShardState st,
-    int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
+__device__ __forceinline__ void step_block(const uint16_t* const* chunks, int n_chunks, int64_t n,
+                                           int64_t tile, bool last, const GradScalars& gs,
+                                           const AdamScalars& as, const ShardState& st,
+                                           bool& bad, double& sq) {
     const int64_t packs = n / kPack;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kTilePacks;
+    const int64_t tile0 = tile * kTilePacks;
     const int64_t first = tile0 + wave * (kWaveSpan * 64) + lane;
-    bool bad = false;
-    double sq = 0.0;
     if (tile0 + kTilePacks <= packs)
         step_tile<NC, REDUCE, true>(chunks, n_chunks, packs, first, gs, as, st, bad, sq);
     else
         step_tile<NC, REDUCE, false>(chunks, n_chunks, packs, first, gs, as, st, bad, sq);
-    // The last n % 8 params: one per thread of the last block.
-    if (blockIdx.x == gridDim.x - 1) {
+    if (last) {
         const int64_t j = packs * kPack + threadIdx.x;
         if (j < n) {
             const float g = unscaled_mean(replica_sum1<NC>(chunks, n_chunks, j), gs);
@@ -227,6 +225,42 @@ __global__ __launch_bounds__(kBlock) void shard_step_kernel(
             st.param_fp16_out[j] = to_fp16_bits(p);
         }
     }
+}
+
+// The fused step over one shard.  One block per tile (a one-shot grid, not a
+// grid-stride loop): on MI355X a stream over this many arrays (N chunks,
+// three state arrays read and written, the fp16 params) sustains more HBM
+// bandwidth when blocks retire after one tile than when resident blocks loop.
+template <int NC, bool REDUCE>
+__global__ __launch_bounds__(kBlock) void shard_step_kernel(
+    ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs, AdamScalars as, ShardState st,
+    int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
+    bool bad = false;
+    double sq = 0.0;
+    step_block<NC, REDUCE>(chunks.p, n_chunks, n, blockIdx.x, blockIdx.x == gridDim.x - 1, gs,
+                           as, st, bad, sq);
+    if constexpr (REDUCE) publish(bad, sq, d_overflow, d_sqnorm);
+}
+
+// The fused step over several bucket slices in one launch.  Bucket k owns
+// blocks [tile_start[k], tile_start[k + 1]) and the state elements
+// [offset[k], offset[k] + n[k]); a block finds its bucket by a scan of the
+// (at most kMaxBucketsPerLaunch) tile starts, which are block-uniform.
+template <int NC, bool REDUCE>
+__global__ __launch_bounds__(kBlock) void bucket_step_kernel(
+    BucketTable t, int n_chunks, GradScalars gs, AdamScalars as, ShardState st,
+    int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
+    const int64_t b = blockIdx.x;
+    int k = 0;
+    while (k + 1 < t.count && b >= t.tile_start[k + 1]) ++k;
+    const int64_t off = t.offset[k];
+    const ShardState sk = {st.master_in + off,  st.exp_avg_in + off,  st.exp_avg_sq_in + off,
+                           st.master_out + off, st.exp_avg_out + off, st.exp_avg_sq_out + off,
+                           st.param_fp16_out + off};
+    bool bad = false;
+    double sq = 0.0;
+    step_block<NC, REDUCE>(&t.chunk[k * n_chunks], n_chunks, t.n[k], b - t.tile_start[k],
+                           b + 1 == t.tile_start[k + 1], gs, as, sk, bad, sq);
     if constexpr (REDUCE) publish(bad, sq, d_overflow, d_sqnorm);
 }
 
@@ -261,7 +295,7 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     if (blockIdx.x == gridDim.x - 1) {
         const int64_t j = packs * kPack + threadIdx.x;
         if (j < n) {
-            const float g = unscaled_mean(replica_sum1<NC>(chunks, n_chunks, j), gs);
+            const float g = unscaled_mean(replica_sum1<NC>(chunks.p, n_chunks, j), gs);
             bad |= nonfinite(g);
             sq += static_cast<double>(g) * static_cast<double>(g);
         }
@@ -322,10 +356,7 @@ int current_cus() {
 }
 
 // Step: one block per tile; a grid of one block still runs the tail.
-int64_t step_grid(int64_t n) {
-    const int64_t tiles = (n / kPack + kTilePacks - 1) / kTilePacks;
-    return tiles < 1 ? 1 : tiles;
-}
+int64_t step_grid(int64_t n) { return step_tiles(n); }
 
 // Check: a resident grid (grid-stride loop), no larger than the packs need.
 int64_t check_grid(int64_t n) {
@@ -343,6 +374,16 @@ hipError_t step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const Gr
     hipLaunchKernelGGL((shard_step_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
                        dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, as, st, d_overflow,
                        d_sqnorm);
+    return hipGetLastError();
+}
+
+template <int NC, bool REDUCE>
+hipError_t bucket_impl(const BucketTable& t, int n_chunks, const GradScalars& gs,
+                       const AdamScalars& as, const ShardState& st, int32_t* d_overflow,
+                       double* d_sqnorm, hipStream_t stream) {
+    const int64_t grid = t.tile_start[t.count];
+    hipLaunchKernelGGL((bucket_step_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kBlock), 0, stream, t, n_chunks, gs, as, st, d_overflow, d_sqnorm);
     return hipGetLastError();
 }
 
@@ -379,6 +420,35 @@ hipError_t launch_shard_step(const ChunkTable& chunks, int n_chunks, int64_t n,
                                                d_sqnorm, stream)
                           : step_impl<0, false>(chunks, n_chunks, n, gs, as, st, d_overflow,
                                                 d_sqnorm, stream);
+    }
+#undef ZERO_CASE
+}
+
+// Blocks of the fused step over n > 0 params: one per tile, at least one
+// (a shard shorter than one pack is all tail).
+int64_t step_tiles(int64_t n) {
+    const int64_t tiles = (n / kPack + kTilePacks - 1) / kTilePacks;
+    return tiles < 1 ? 1 : tiles;
+}
+
+hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScalars& gs,
+                              const AdamScalars& as, const ShardState& st, int32_t* d_overflow,
+                              double* d_sqnorm, hipStream_t stream) {
+    if (t.count <= 0 || t.tile_start[t.count] <= 0) return hipSuccess;
+    const bool reduce = d_overflow != nullptr || d_sqnorm != nullptr;
+#define ZERO_CASE(K)                                                                          \
+    case K:                                                                                   \
+        return reduce ? bucket_impl<K, true>(t, n_chunks, gs, as, st, d_overflow, d_sqnorm,   \
+                                             stream)                                          \
+                      : bucket_impl<K, false>(t, n_chunks, gs, as, st, d_overflow, d_sqnorm,  \
+                                              stream);
+    switch (n_chunks) {
+        ZERO_FOR_EACH_N(ZERO_CASE)
+        default:
+            return reduce ? bucket_impl<0, true>(t, n_chunks, gs, as, st, d_overflow, d_sqnorm,
+                                                 stream)
+                          : bucket_impl<0, false>(t, n_chunks, gs, as, st, d_overflow, d_sqnorm,
+                                                  stream);
     }
 #undef ZERO_CASE
 }

@@ -156,6 +156,61 @@ def test_shard_step_out_rejects_bad_state():
     assert _step_out(_ptrs(0), 1, 0, (None, None, None), (None,) * 4, _hp()) == zs.ZERO_OK
 
 
+def _buckets(specs, n_chunks, n_state, ins, outs, hp, flag=None):
+    """specs: (chunk pointers, n, offset) per slice."""
+    keep = []
+    table = (zs.BucketSliceC * max(len(specs), 1))()
+    for k, (ptrs, n, off) in enumerate(specs):
+        arr = _ptrs(*ptrs) if ptrs is not None else None
+        keep.append(arr)
+        table[k].grad_chunks = (ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+                                if arr is not None else None)
+        table[k].n = n
+        table[k].offset = off
+    return zs.lib.zero_shard_step_buckets(table, len(specs), n_chunks, 1024.0, n_state, *ins,
+                                          *outs, ctypes.byref(hp) if hp is not None else None,
+                                          flag, None, None)
+
+
+def test_shard_step_buckets_rejects_bad_slices():
+    n_state = 4096
+    B = A + (1 << 24)
+    ins = (B, B + 4 * n_state, B + 8 * n_state)
+    C = B + (1 << 20)
+    outs = (C, C + 4 * n_state, C + 8 * n_state, C + 12 * n_state)
+    ch = [A, A + 65536]
+    ok = [(ch, 1000, 0), (ch, 1000, 1024)]
+    # a well-formed table fails only at launch, which never happens here: use
+    # one bad field at a time
+    assert _buckets([(ch, 1000, 4)], 2, n_state, ins, outs, _hp()) == zs.ZERO_EALIGN
+    assert _buckets([(ch, 1000, 3200)], 2, n_state, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert "past n_state" in _last()
+    assert _buckets([(ch, -1, 0)], 2, n_state, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert _buckets([(ch, 8, -8)], 2, n_state, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert _buckets([(None, 8, 0)], 2, n_state, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert _buckets([([A, 0], 8, 0)], 2, n_state, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert _buckets([([A, A + 2], 8, 0)], 2, n_state, ins, outs, _hp()) == zs.ZERO_EALIGN
+    # two slices sharing state elements, in either order
+    assert _buckets([(ch, 1000, 0), (ch, 1000, 992)], 2, n_state, ins, outs, _hp()) \
+        == zs.ZERO_EINVAL
+    assert "overlap" in _last()
+    assert _buckets([(ch, 1000, 992), (ch, 1000, 0)], 2, n_state, ins, outs, _hp()) \
+        == zs.ZERO_EINVAL
+    # an output over a chunk, an output over another input
+    assert _buckets([([C + 64, A], 8, 0)], 2, n_state, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert _buckets(ok, 2, n_state, ins, (ins[1],) + outs[1:], _hp()) == zs.ZERO_EINVAL
+    # scalars
+    assert _buckets(ok, 0, n_state, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert _buckets(ok, 65, n_state, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert _buckets(ok, 2, n_state, ins, outs, _hp(step=0)) == zs.ZERO_EINVAL
+    assert _buckets(ok, 2, n_state, ins, outs, None) == zs.ZERO_EINVAL
+    assert _buckets(ok, 2, -1, ins, outs, _hp()) == zs.ZERO_EINVAL
+    assert _buckets(ok, 2, n_state, ins, outs, _hp(), A + 2) == zs.ZERO_EALIGN
+    # only empty slices, or none: a no-op whatever the state pointers
+    assert _buckets([(None, 0, 0)], 2, n_state, (None,) * 3, (None,) * 4, _hp()) == zs.ZERO_OK
+    assert _buckets([], 2, 0, (None,) * 3, (None,) * 4, _hp()) == zs.ZERO_OK
+
+
 def _flatten(ptrs, numels, align, pad, bucket, cap):
     nt = len(numels)
     offs = (ctypes.c_int64 * (nt + 1))()

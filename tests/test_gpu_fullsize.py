@@ -9,9 +9,10 @@ elsewhere.
   skipped, the scale halves, the state stays bit-identical; then a clean
   step at the halved scale matches the oracle everywhere.
 * ZeRO-2 bucketed (160 buckets, 973,111,296 params on one rank): every
-  bucket flattened for 8 replicas and stepped; buckets 0, 3, 4 and 159
-  (both bucket shapes, first and last) checked in full against the oracle's
-  flatten and step, the rest by the fp16 writeback property.
+  bucket flattened for 8 replicas, then all 160 slices stepped by one
+  multi-bucket call; buckets 0, 3, 4 and 159 (both bucket shapes, first and
+  last) checked in full against the oracle's flatten and step, the rest by
+  the fp16 writeback property and against 160 single-slice calls.
 * 70B-class shard (4,412,500,000 params, N = 16) streamed in 23 buckets
   through two chunk buffers: buckets 0, 11 and 22 checked in full, the rest
   by the fp16 writeback property.
@@ -130,6 +131,12 @@ ZERO2_SAMPLED = (0, 3, 4, 159)
 
 
 def test_zero2_bucketed_full():
+    """Every bucket is flattened for the 8 replicas and this rank's slice of
+    each replica's bucket is kept (what the per-bucket reduce-scatter would
+    deliver); then one zero_shard_step_buckets call updates all 160 slices,
+    as a ZeRO-2 rank steps after backward.  Sampled buckets are checked in
+    full against the oracle's flatten and step; 160 per-bucket
+    zero_shard_step_out calls must give the same bits."""
     dev = device()
     w = wl.ZERO2
     N, r, S = w.n_replicas, wl.ZERO2_RANK, w.loss_scale
@@ -139,13 +146,10 @@ def test_zero2_bucketed_full():
     layouts = [ofl.bucket_layout([sizes[k] for k in idx], align, pad) for idx in plan]
     assert len(plan) == 160 and sum(lay[-1] for lay in layouts) // N == w.n
     print(f"case: full {w.name} buckets={len(plan)} rank={r} n={w.n}", flush=True)
-    st = wl.device_state(w, dev)
-    cur = (st["master"], st["m"], st["v"], st["p16"])
-    out = tuple(torch.empty_like(t) for t in cur)
     lmax = max(lay[-1] for lay in layouts)
     buckets = [torch.empty(lmax, dtype=torch.float16, device=dev) for _ in range(N)]
-    hp = zs.adamw_params(w.hyper)
-    fl, sq = flags(dev)
+    owned = [torch.empty(w.n, dtype=torch.float16, device=dev) for _ in range(N)]
+    host_reps, offsets = {}, []
     off = 0
     for b, idx in enumerate(plan):
         L = layouts[b][-1]
@@ -154,32 +158,54 @@ def test_zero2_bucketed_full():
         for i in range(N):
             offs = zs.zero_bucket_flatten(reps[i], buckets[i], align=align, pad_multiple=pad)
             assert offs == layouts[b], (b, offs, layouts[b])
-        chunks = [bk[r * sl:(r + 1) * sl] for bk in buckets]
-        s_in = tuple(t[off:off + sl] for t in cur)
-        s_out = tuple(t[off:off + sl] for t in out)
-        zs.zero_shard_step_out(chunks, S, *s_in[:3], *s_out, hp, fl, sq)
+            owned[i][off:off + sl].copy_(buckets[i][r * sl:(r + 1) * sl])
         if b in ZERO2_SAMPLED:
-            fb, sb = flags(dev)
-            zs.zero_overflow_check(chunks, S, fb, sb)
             torch.cuda.synchronize()
-            print(f"case: zero2 bucket {b} (L={L}) flatten and step vs oracle", flush=True)
-            want_b = [ofl.flatten([t.cpu().numpy() for t in reps[i]], align, pad)[0]
-                      for i in range(N)]
+            host_reps[b] = [[t.cpu().numpy() for t in reps[i]] for i in range(N)]
             for i in range(N):
                 got = buckets[i][:L].cpu().numpy()
-                assert np.array_equal(got.view(np.uint16), want_b[i].view(np.uint16)), (b, i)
-            want = ozs.shard_step([wb[r * sl:(r + 1) * sl] for wb in want_b],
-                                  *[t.cpu().numpy() for t in s_in], w.hyper, S)
-            assert not want.overflow and int(fb.item()) == 0
-            assert rel_close(float(sb.item()), want.sqnorm)
-            for name, t, ref in zip(("master", "m", "v"), s_out[:3], (want.master, want.m, want.v)):
-                assert np.array_equal(t.cpu().numpy().view(np.uint32), ref.view(np.uint32)), (b, name)
-            assert np.array_equal(s_out[3].cpu().numpy().view(np.uint16), want.p16.view(np.uint16))
+                want_b = ofl.flatten(host_reps[b][i], align, pad)[0]
+                assert np.array_equal(got.view(np.uint16), want_b.view(np.uint16)), (b, i)
         del reps
+        offsets.append((off, sl))
         off += sl
+    assert off == w.n
+    del buckets
+    st = wl.device_state(w, dev)
+    cur = (st["master"], st["m"], st["v"], st["p16"])
+    out = tuple(torch.empty_like(t) for t in cur)
+    table = zs.BucketSlices([([o[a:a + n] for o in owned], a) for a, n in offsets])
+    hp = zs.adamw_params(w.hyper)
+    fl, sq = flags(dev)
+    zs.zero_shard_step_buckets(table, S, *cur[:3], *out, hp, fl, sq)
     torch.cuda.synchronize()
-    assert off == w.n and int(fl.item()) == 0
+    assert int(fl.item()) == 0
+    for b in ZERO2_SAMPLED:
+        a, n = offsets[b]
+        L = layouts[b][-1]
+        print(f"case: zero2 bucket {b} (L={L}) step vs oracle", flush=True)
+        want_b = [ofl.flatten(host_reps[b][i], align, pad)[0] for i in range(N)]
+        want = ozs.shard_step([wb[r * n:(r + 1) * n] for wb in want_b],
+                              *[t[a:a + n].cpu().numpy() for t in cur], w.hyper, S)
+        assert not want.overflow
+        fb, sb = flags(dev)
+        zs.zero_overflow_check([o[a:a + n] for o in owned], S, fb, sb)
+        torch.cuda.synchronize()
+        assert int(fb.item()) == 0 and rel_close(float(sb.item()), want.sqnorm)
+        for name, t, ref in zip(("master", "m", "v"), out[:3], (want.master, want.m, want.v)):
+            assert np.array_equal(t[a:a + n].cpu().numpy().view(np.uint32),
+                                  ref.view(np.uint32)), (b, name)
+        assert np.array_equal(out[3][a:a + n].cpu().numpy().view(np.uint16),
+                              want.p16.view(np.uint16))
     _assert_writeback_property(out[0], out[3], "zero2")
+    # the same update as 160 separate calls
+    ref = tuple(torch.empty_like(t) for t in cur)
+    for a, n in offsets:
+        zs.zero_shard_step_out([o[a:a + n] for o in owned], S, *(t[a:a + n] for t in cur[:3]),
+                               *(t[a:a + n] for t in ref), hp)
+    torch.cuda.synchronize()
+    for x, y in zip(out, ref):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
 LLAMA70B_SAMPLED = (0, 11, 22)
