@@ -130,6 +130,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.workload == "zero2_bucketed":
+        return bench_zero2(args, dev)
     w = wl.WORKLOADS[args.workload]
     n, N = w.n, w.n_replicas
     log(f"bench: workload={w.name} n={n} N={N} steps={args.steps} warmup={args.warmup}")
@@ -239,6 +241,116 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def _timed(fn, steps: int, warmup: int = 2):
+    """Average wall time (ms) of fn() over `steps` calls, each ending in a
+    device synchronisation, after `warmup` untimed calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def bench_zero2(args, dev):
+    """ZeRO-2 bucketed workload: 160 buckets of 32 decoder layers, N = 8; this
+    rank owns slice 3 of every bucket (973,111,296 params).  Times, per step:
+    the rank flattening its own 160 gradient buckets, and the update of its
+    160 slices as one zero_shard_step_buckets call, as 160
+    zero_shard_step_out calls, and as one call over the contiguous shard
+    (same bytes, the launch-free ideal).  Prints one JSON line."""
+    import torch
+
+    import sharded_mixed_precision_step_amd as zs
+    import workloads as wl
+
+    w = wl.ZERO2
+    N, r, S = w.n_replicas, wl.ZERO2_RANK, w.loss_scale
+    align, pad = wl.ZERO2_ALIGN, wl.ZERO2_ALIGN * N
+    stream = torch.cuda.current_stream()
+    plan = wl.zero2_bucket_plan()
+    log(f"bench: workload={w.name} buckets={len(plan)} n={w.n} N={N}")
+    # this rank's own gradients, flattened bucket by bucket (the layout gives
+    # each bucket's length and so each slice)
+    grads = [[wl.zero2_device_tensor(r, k, dev) for k in idx] for idx in plan]
+    lmax = 0
+    lengths = []
+    scratch = torch.empty(60_000_000, dtype=torch.float16, device=dev)
+    for ts in grads:
+        offs = zs.zero_bucket_flatten(ts, scratch, align, pad, stream=stream)
+        lengths.append(offs[-1])
+        lmax = max(lmax, offs[-1])
+    buckets = [torch.empty(L, dtype=torch.float16, device=dev) for L in lengths]
+
+    def flatten_all():
+        for ts, bk in zip(grads, buckets):
+            zs.zero_bucket_flatten(ts, bk, align, pad, stream=stream)
+
+    flat_ms = _timed(flatten_all, args.steps)
+    flat_bytes = sum(2 * sum(t.numel() for t in ts) + 2 * L for ts, L in zip(grads, lengths))
+    del grads, buckets, scratch
+    torch.cuda.empty_cache()
+    # the slices this rank owns, as the per-bucket reduce-scatter delivers them
+    offsets, off = [], 0
+    for L in lengths:
+        offsets.append((off, L // N))
+        off += L // N
+    assert off == w.n
+    owned = wl.device_chunks(w, dev)
+    st = wl.device_state(w, dev)
+    cur = (st["master"], st["m"], st["v"], st["p16"])
+    out = tuple(torch.empty_like(t) for t in cur)
+    table = zs.BucketSlices([([o[a:a + n] for o in owned], a) for a, n in offsets])
+    views = [([o[a:a + n] for o in owned], tuple(t[a:a + n] for t in cur[:3]),
+              tuple(t[a:a + n] for t in out)) for a, n in offsets]
+    hp = zs.adamw_params(w.hyper)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    sq = torch.zeros(1, dtype=torch.float64, device=dev)
+
+    def multi():
+        zs.zero_shard_step_buckets(table, S, *cur[:3], *out, hp, flag, sq, stream=stream)
+
+    def per_bucket():
+        for ch, si, so in views:
+            zs.zero_shard_step_out(ch, S, *si, *so, hp, flag, sq, stream=stream)
+
+    def whole():
+        zs.zero_shard_step_out(owned, S, *cur[:3], *out, hp, flag, sq, stream=stream)
+
+    ms = {name: _timed(fn, args.steps) for name, fn in
+          (("multi_bucket", multi), ("per_bucket", per_bucket), ("whole_shard", whole))}
+    step_bytes = w.bytes_per_param_step() * w.n
+    log("bench: " + ", ".join(f"{k} {v:.3f} ms" for k, v in ms.items()) +
+        f", flatten {flat_ms:.3f} ms")
+    out_line = {
+        "metric": METRIC,
+        "value": w.n / (ms["multi_bucket"] * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": 2,
+        "ms_per_step": ms["multi_bucket"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded device draws; fp16 grads, fp32 state)",
+        "config": {"workload": w.name, "buckets": len(plan), "shard_params": w.n,
+                   "replicas": N, "rank": r, "bytes_per_param_fused_step":
+                   w.bytes_per_param_step()},
+        "extra": {
+            **{f"{k}_ms": v for k, v in ms.items()},
+            **{f"{k}_gbps": step_bytes / (v * 1e-3) / 1e9 for k, v in ms.items()},
+            "flatten_own_buckets_ms": flat_ms,
+            "flatten_own_buckets_gbps": flat_bytes / (flat_ms * 1e-3) / 1e9,
+        },
+    }
+    print(json.dumps(out_line), flush=True)
 
 
 def two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):

@@ -15,6 +15,8 @@ constexpr int kWaveSpan = 2;       // packs per lane in a step tile
 constexpr int kTilePacks = kBlock * kWaveSpan;  // packs per step tile (one block)
 constexpr int kCheckBlocksPerCU = 6;            // resident blocks of the check kernel
 constexpr int kFlattenBatch = 32;  // tensors per flatten launch (kernel-argument table)
+constexpr int kFlattenSpan = 4;    // packs per lane in a flatten tile
+constexpr int64_t kFlattenTile = static_cast<int64_t>(kBlock) * kFlattenSpan * kPack;  // elements
 constexpr int kMaxBucketsPerLaunch = 32;  // bucket slices per multi-bucket step launch
 constexpr int kBucketTablePtrs = 256;     // chunk pointers per multi-bucket step launch
 

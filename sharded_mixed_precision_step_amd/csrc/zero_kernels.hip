@@ -304,29 +304,44 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
 }
 
 // One slot per blockIdx.y: the tensor's elements, then zeros up to the next
-// slot.  Slots are disjoint, so blocks never write the same element.
+// slot.  Slots are disjoint, so blocks never write the same element.  Block x
+// copies the slot's tile x (kFlattenTile elements; a one-shot grid, as for
+// the step): wave w the kFlattenSpan * 64 packs from w * kFlattenSpan * 64,
+// lane l the packs l, l + 64, ..., all loads before the stores.
 __global__ __launch_bounds__(kBlock) void bucket_flatten_kernel(FlattenTable table,
                                                                 uint16_t* __restrict__ bucket) {
     const FlattenDesc d = table.d[blockIdx.y];
+    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kFlattenTile;
+    if (tile0 >= d.slot_len) return;  // a shorter slot than the launch's longest
     uint16_t* dst = bucket + d.dst_off;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    const int64_t first = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
     if (d.vec) {
         const bool src_vec = (reinterpret_cast<uintptr_t>(d.src) & 15) == 0;
         const int64_t packs = d.slot_len / kPack;
-        for (int64_t i = first; i < packs; i += stride) {
+        const int lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+        const int64_t first = tile0 / kPack + wave * (kFlattenSpan * 64) + lane;
+        u16x8 val[kFlattenSpan];
+#pragma unroll
+        for (int u = 0; u < kFlattenSpan; ++u) {
+            const int64_t i = first + u * 64;
+            if (i >= packs) continue;
             const int64_t e = i * kPack;
-            u16x8 val;
             if (src_vec && e + kPack <= d.numel) {
-                val = *reinterpret_cast<const u16x8*>(d.src + e);
+                val[u] = *reinterpret_cast<const u16x8*>(d.src + e);
             } else {
 #pragma unroll
-                for (int k = 0; k < kPack; ++k) val[k] = (e + k < d.numel) ? d.src[e + k] : 0;
+                for (int k = 0; k < kPack; ++k) val[u][k] = (e + k < d.numel) ? d.src[e + k] : 0;
             }
-            *reinterpret_cast<u16x8*>(dst + e) = val;
+        }
+#pragma unroll
+        for (int u = 0; u < kFlattenSpan; ++u) {
+            const int64_t i = first + u * 64;
+            if (i < packs) *reinterpret_cast<u16x8*>(dst + i * kPack) = val[u];
         }
     } else {
-        for (int64_t e = first; e < d.slot_len; e += stride) dst[e] = e < d.numel ? d.src[e] : 0;
+        const int64_t end = tile0 + kFlattenTile < d.slot_len ? tile0 + kFlattenTile : d.slot_len;
+        for (int64_t e = tile0 + threadIdx.x; e < end; e += kBlock)
+            dst[e] = e < d.numel ? d.src[e] : 0;
     }
 }
 
@@ -470,10 +485,7 @@ hipError_t launch_overflow_check(const ChunkTable& chunks, int n_chunks, int64_t
 hipError_t launch_bucket_flatten(const FlattenTable& table, int count, int64_t max_slot_len,
                                  uint16_t* bucket, hipStream_t stream) {
     if (count <= 0 || max_slot_len <= 0) return hipSuccess;
-    const int64_t cap = static_cast<int64_t>(current_cus()) * 8;
-    int64_t gx = (max_slot_len / kPack + kBlock) / kBlock;
-    if (gx > cap) gx = cap;
-    if (gx < 1) gx = 1;
+    const int64_t gx = (max_slot_len + kFlattenTile - 1) / kFlattenTile;
     hipLaunchKernelGGL(bucket_flatten_kernel, dim3(static_cast<unsigned>(gx), count), dim3(kBlock),
                        0, stream, table, bucket);
     return hipGetLastError();
