@@ -38,6 +38,10 @@ reason in the design notes):
 * the squared gradient norm is the sum of the exact fp64 squares of g,
   accumulated in fp64 in ascending index order.
 
+The page-literal split (the owner stores its gradient mean as fp16, then
+updates from it) is ``replica_mean_fp16`` / ``accumulate_chunks`` followed by
+``shard_step_from_fp16_mean``.
+
 Pins (tests that tie this module to facts outside itself):
 replica sum -> brute-force ring simulation and the worked 3-GPU example;
 mean and unscale -> identical-replica invariant (exact closed form);
@@ -45,7 +49,10 @@ non-finite flag -> planted inf/NaN and an fp32-overflowing unscale;
 squared norm -> constant-gradient closed form and an exactly rounded sum;
 moments and master -> first-step closed form, zero-gradient and lr = 0
 invariants, and the N = 1, S = 1 special case against torch.optim.AdamW;
-fp16 writeback -> IEEE binary16 bit patterns and torch's own rounding.
+fp16 writeback -> IEEE binary16 bit patterns and torch's own rounding;
+fp16 mean -> exact rational means rounded by hand-coded binary16 rounding on
+exactly summable inputs, and identical replicas (the fp16 mean is then the
+replica itself, and the split equals the fused step bit for bit).
 """
 from __future__ import annotations
 
@@ -169,22 +176,62 @@ class StepResult:
     p16: np.ndarray
 
 
-def shard_step(chunks, master, m, v, p16, hyper, loss_scale,
-               sqnorm_start: float = 0.0) -> StepResult:
-    """The whole per-rank step on one shard (or one slice of it).
-
-    If any unscaled gradient value is non-finite the step is skipped and the
-    returned state equals the input state; otherwise the AdamW update runs.
-    The overflow decision here is local to the given slice: a caller that
-    splits a shard combines the slices' flags before acting on them.
-    """
-    g = unscaled_grad(chunks, loss_scale)
+def step_from_grad(g, master, m, v, p16, hyper, sqnorm_start: float = 0.0) -> StepResult:
+    """Flag, squared norm and (unless the flag is set) the AdamW update from
+    the unscaled fp32 gradient g.  If any element of g is non-finite the step
+    is skipped and the returned state equals the input state."""
     flag = nonfinite(g)
     sq = grad_sqnorm(g, sqnorm_start)
     if flag:
         return StepResult(True, sq, master.copy(), m.copy(), v.copy(), p16.copy())
     master1, m1, v1, p161 = adamw_update(g, master, m, v, hyper)
     return StepResult(False, sq, master1, m1, v1, p161)
+
+
+def shard_step(chunks, master, m, v, p16, hyper, loss_scale,
+               sqnorm_start: float = 0.0) -> StepResult:
+    """The whole per-rank step on one shard (or one slice of it).
+
+    The overflow decision here is local to the given slice: a caller that
+    splits a shard combines the slices' flags before acting on them.
+    """
+    return step_from_grad(unscaled_grad(chunks, loss_scale), master, m, v, p16, hyper,
+                          sqnorm_start)
+
+
+# --------------------------------------------------------------------------
+# The page-literal split: the owner first holds the mean in fp16, then updates.
+# --------------------------------------------------------------------------
+
+def replica_mean_fp16(chunks: Sequence[np.ndarray]) -> np.ndarray:
+    """The owner's gradient mean as the ZeRO notes' ZeRO-1 sync step leaves
+    it: in fp16.  Reading taken for how it is formed: the replica sum in fp32
+    in fixed order, divided by N in fp32, then rounded to nearest-even
+    binary16 once."""
+    with np.errstate(over="ignore", invalid="ignore", under="ignore"):
+        return replica_mean(replica_sum(chunks), len(chunks)).astype(np.float16)
+
+
+def accumulate_chunks(chunks: Sequence[np.ndarray]) -> np.ndarray:
+    """The same fp16 mean, formed as chunks arrive one at a time: an fp32
+    accumulator starts at the first chunk, each later chunk is added to it
+    (one fp32 addition per element), and after the last one the accumulator
+    is divided by N and rounded to binary16."""
+    acc = widen(chunks[0])
+    for x in chunks[1:]:
+        acc = acc + widen(x)
+    with np.errstate(over="ignore", invalid="ignore", under="ignore"):
+        return (acc / F32(len(chunks))).astype(np.float16)
+
+
+def shard_step_from_fp16_mean(mean16, master, m, v, p16, hyper, loss_scale,
+                              sqnorm_start: float = 0.0) -> StepResult:
+    """ZeRO notes, ZeRO-1 update step, from the stored fp16 mean: fp16 to fp32
+    (not stored), scale (divide by S), fp32 moments, fp32 master weights,
+    fp16 params."""
+    with np.errstate(over="ignore", invalid="ignore", under="ignore"):
+        g = unscale(widen(mean16), loss_scale)
+    return step_from_grad(g, master, m, v, p16, hyper, sqnorm_start)
 
 
 def check_only(chunks, loss_scale, sqnorm_start: float = 0.0):

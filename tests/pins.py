@@ -10,6 +10,7 @@ from __future__ import annotations
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 
@@ -135,6 +136,72 @@ def pin_mean_of_distinct_replicas():
         want = np.ldexp(want.astype(np.float64), -log2s).astype(np.float32)
         g = zs.unscaled_grad(chunks, float(2.0 ** log2s))
         assert np.array_equal(_bits32(g), _bits32(want)), (n_rep, log2s)
+
+
+# --------------------------------------------------------------------------
+# The page-literal split: the owner's mean stored as fp16.
+# --------------------------------------------------------------------------
+
+def _round_rne(x: Fraction, mant_bits: int, emin: int, emax: int) -> Fraction:
+    """Round the rational x to the nearest binary floating-point value with
+    `mant_bits` significand bits (hidden bit included), exponents down to
+    emin (subnormals below) and up to emax, ties to even; past the largest
+    finite value it becomes +-inf (returned as None with the sign lost: the
+    callers here never overflow)."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, emin)                      # subnormals share emin's quantum
+    q = Fraction(2) ** (e - mant_bits + 1)  # value of one unit in the last place
+    k, rem = divmod(a, q)
+    k = int(k)
+    if rem * 2 > q or (rem * 2 == q and k % 2 == 1):
+        k += 1
+    r = k * q
+    assert r < Fraction(2) ** (emax + 1), "overflow not expected here"
+    return sign * r
+
+
+def pin_fp16_mean_is_rounded_exact_mean():
+    """On exactly summable replicas the fp32 sum is exact, so the fp16 mean is
+    the exact rational s / N rounded to binary32 (the division), then to
+    binary16, both to nearest even: checked element by element with exact
+    rational arithmetic, for both ways of forming it (all chunks at once,
+    and one chunk arriving at a time)."""
+    for n_rep in (3, 5, 7, 9):
+        chunks = [exactly_summable_fp16(seed_of(97, n_rep, i), 257, bound_log2=4)
+                  for i in range(n_rep)]
+        for form in (zs.replica_mean_fp16, zs.accumulate_chunks):
+            got = form(chunks)
+            for j in range(got.size):
+                s = sum(Fraction(float(c[j])) for c in chunks)
+                want = _round_rne(_round_rne(s / n_rep, 24, -126, 127), 11, -14, 15)
+                assert Fraction(float(got[j])) == want, (form.__name__, n_rep, j)
+
+
+def pin_fp16_split_with_identical_replicas():
+    """Identical replicas x: the mean is x, exactly representable in fp16, so
+    the split (fp16 mean, then the update from it) equals the fused step bit
+    for bit."""
+    x = host_fp16_grad(seed_of(98), 2053, 1e-3, 1024.0)
+    master = host_normal_f32(seed_of(98, 1), 2053, 0.02)
+    m = np.abs(host_normal_f32(seed_of(98, 2), 2053, 1e-4))
+    v = np.abs(host_normal_f32(seed_of(98, 3), 2053, 1e-8))
+    p16 = master.astype(np.float16)
+    hyp = AdamWHyper(step=17)
+    for n_rep in (1, 3, 8):
+        mean16 = zs.replica_mean_fp16([x] * n_rep)
+        assert np.array_equal(mean16.view(np.uint16), x.view(np.uint16))
+        a = zs.shard_step_from_fp16_mean(mean16, master, m, v, p16, hyp, 1024.0)
+        b = zs.shard_step([x] * n_rep, master, m, v, p16, hyp, 1024.0)
+        for u, w in ((a.master, b.master), (a.m, b.m), (a.v, b.v)):
+            assert np.array_equal(_bits32(u), _bits32(w))
+        assert np.array_equal(a.p16.view(np.uint16), b.p16.view(np.uint16))
+        assert a.sqnorm == b.sqnorm and a.overflow == b.overflow is False
 
 
 # --------------------------------------------------------------------------

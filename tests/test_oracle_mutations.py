@@ -144,6 +144,35 @@ for _k in ("eps_inside_sqrt", "m_v_transposed", "wd_sign", "p16_from_old_master"
     MUTATIONS[_k] = (zs, "adamw_update", _adamw_variant(_k))
 
 
+def _mean16_toward_zero(chunks):
+    """The fp16 mean rounded toward zero instead of to nearest even."""
+    x = zs.replica_mean(zs.replica_sum(chunks), len(chunks))
+    h = x.astype(np.float16)
+    away = np.abs(h.astype(np.float32)) > np.abs(x)
+    return np.where(away, np.nextafter(h, np.float16(0)), h).astype(np.float16)
+
+
+def _accumulate_drops_last(chunks):
+    acc = zs.widen(chunks[0])
+    for c in chunks[1:-1]:
+        acc = acc + zs.widen(c)
+    return (acc / F32(len(chunks))).astype(np.float16)
+
+
+def _split_unscale_multiplies(mean16, master, m, v, p16, hyper, loss_scale, sqnorm_start=0.0):
+    g = zs.widen(mean16) * F32(loss_scale)
+    return zs.step_from_grad(g, master, m, v, p16, hyper, sqnorm_start)
+
+
+MUTATIONS.update({
+    "mean16_rounds_toward_zero": (zs, "replica_mean_fp16", _mean16_toward_zero),
+    "mean16_not_divided": (zs, "replica_mean_fp16",
+                           lambda chunks: zs.replica_sum(chunks).astype(np.float16)),
+    "accumulate_drops_last_arrival": (zs, "accumulate_chunks", _accumulate_drops_last),
+    "split_unscale_multiplies": (zs, "shard_step_from_fp16_mean", _split_unscale_multiplies),
+})
+
+
 def test_unmutated_variants_pass(monkeypatch):
     """The variant machinery itself, with no mistake planted, passes every pin."""
     monkeypatch.setattr(zs, "adamw_update", _adamw_variant("none"))
