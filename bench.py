@@ -10,8 +10,9 @@ device flag and norm; run the fused update (replica sum, mean, unscale,
 inf/NaN flag, squared norm, moments, fp32 master, fp16 params) from the
 current copy of the state into the other copy; read the flag back; update
 the dynamic loss scale on the host; and commit the written copy if the step
-is clean.  The two-pass form (overflow check, then the in-place update) is
-timed afterwards on the same state and reported under "extra".
+is clean.  The two-pass form (overflow check, then the in-place update) and
+the page-literal split (the gradient mean stored as fp16, then the update
+from it) are timed afterwards on the same state and reported under "extra".
 
 Prints one JSON line.  `value` is params/s of the whole step.  `roofline`
 rates the fused update kernel, the dominant one, by its algorithmic bytes
@@ -193,6 +194,9 @@ def main():
     two = two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, args.two_pass_steps)
     log(f"bench: two-pass {two['two_pass_ms_per_step']:.3f} ms/step, check "
         f"{two['check_ms']:.3f} ms, in-place step {two['inplace_step_ms']:.3f} ms")
+    lit = page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, args.two_pass_steps)
+    log(f"bench: page-literal split {lit['split_ms_per_step']:.3f} ms/step, fp16 mean "
+        f"{lit['mean_fp16_ms']:.3f} ms, one-chunk step {lit['split_step_ms']:.3f} ms")
 
     k1_bytes = w.bytes_per_param_step() * n
     k1_gbps = k1_bytes / (k1_ms * 1e-3) / 1e9
@@ -206,6 +210,7 @@ def main():
         "skipped_steps": skipped,
     }
     extra.update(two)
+    extra.update(lit)
 
     if not args.no_flatten:
         extra.update(bench_flatten(zs, wl, dev, stream))
@@ -389,6 +394,47 @@ def two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
             "check_ms": check_ms, "check_gbps": 2 * N * n / (check_ms * 1e-3) / 1e9,
             "inplace_step_ms": step_ms,
             "inplace_step_gbps": w.bytes_per_param_step() * n / (step_ms * 1e-3) / 1e9}
+
+
+def page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
+    """The page-literal split on the same state, for comparison: the owner's
+    gradient mean stored as fp16, then the single-pass update from it as a
+    one-chunk step (flag, read-back, loss scale, commit)."""
+    import torch
+    n, N = w.n, w.n_replicas
+    mean16 = torch.empty(n, dtype=torch.float16, device=d["master"].device)
+    ev_mean, ev_step = [], []
+    t0 = None
+    for k in range(steps + 1):           # the first step is an untimed warm-up
+        if k == 1:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        flag.zero_()
+        sq.zero_()
+        scale = scaler.scale
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        zs.zero_reduce_mean_fp16(d["chunks"], mean16, stream=stream)
+        e[1].record(stream)
+        m_in, a_in, v_in, _ = shard.current
+        m_out, a_out, v_out, p_out = shard.other
+        zs.zero_shard_step_out([mean16], scale, m_in, a_in, v_in, m_out, a_out, v_out, p_out,
+                               hp, flag, sq, stream=stream)
+        e[2].record(stream)
+        if not zs.zero_update_loss_scale(scaler, int(flag.item())):
+            shard.cur = 1 - shard.cur
+            hp.step += 1
+        if k >= 1:
+            ev_mean.append((e[0], e[1]))
+            ev_step.append((e[1], e[2]))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    mean_ms = sum(a.elapsed_time(b) for a, b in ev_mean) / max(len(ev_mean), 1)
+    step_ms = sum(a.elapsed_time(b) for a, b in ev_step) / max(len(ev_step), 1)
+    del mean16
+    return {"split_ms_per_step": ms, "split_params_per_s": n / (ms * 1e-3),
+            "mean_fp16_ms": mean_ms, "mean_fp16_gbps": (2 * N + 2) * n / (mean_ms * 1e-3) / 1e9,
+            "split_step_ms": step_ms, "split_step_gbps": 28 * n / (step_ms * 1e-3) / 1e9}
 
 
 def copy_ceiling(dev, stream, reps: int = 5):

@@ -220,6 +220,59 @@ int zero_shard_step_buckets(const zero_bucket_slice* slices, int32_t n_slices, i
                             int32_t* d_overflow, double* d_sqnorm, void* stream);
 
 /*
+ * zero_reduce_mean_fp16 -- the owner's gradient mean, stored as fp16.
+ *
+ * The ZeRO notes (rkmt.cn/news/44736, section "Deepspeed ZeRO-1", step 同步)
+ * leave each owner holding the mean of its part's gradients in fp16; their
+ * update step then takes it to fp32 without storing it, scales it and
+ * updates (step 更新).  This call forms that mean: for each j < n,
+ * mean_fp16[j] = binary16 round-to-nearest-even of s / N, where s is the
+ * replicas' fp32 sum in order 0..N-1 and s / N one fp32 division.  With
+ * d_overflow / d_sqnorm it also accumulates the flag and squared norm of
+ * g = fp32(mean_fp16[j]) / loss_scale, the gradient the update will use.
+ * The update itself is zero_shard_step, zero_shard_step_out or
+ * zero_shard_step_buckets with n_chunks = 1 and mean_fp16 as the only chunk:
+ * with one chunk the sum and the mean are that chunk, exactly.
+ *
+ *   grad_chunks   as for zero_overflow_check
+ *   loss_scale    S, finite and > 0 (used only for the flag and norm)
+ *   mean_fp16     DEVICE fp16[n], 16-byte aligned, written only; must not
+ *                 overlap any chunk
+ *   d_overflow    DEVICE int32 or NULL;  d_sqnorm DEVICE fp64 or NULL
+ * Returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN or ZERO_EHIP.
+ */
+int zero_reduce_mean_fp16(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                          float loss_scale, void* mean_fp16, int32_t* d_overflow,
+                          double* d_sqnorm, void* stream);
+
+/*
+ * zero_accumulate_chunk -- fold one replica's chunk into its owner's
+ * accumulator as it arrives.
+ *
+ * Under ZeRO-2 each bucket's gradients reach their owner as soon as the
+ * bucket is complete (ZeRO notes, section "Deepspeed ZeRO-2", step 同步); the
+ * owner can fold the replicas' chunks in one at a time, in replica order.
+ * For replica `index` of n_chunks (= N), elementwise over j < n:
+ *   N == 1:                 mean_fp16[j] = fp16(x[j])            (acc unused)
+ *   index == 0 < N - 1:     acc[j] = fp32(x[j])                  (mean unused)
+ *   0 < index < N - 1:      acc[j] = acc[j] + fp32(x[j])
+ *   index == N - 1 > 0:     mean_fp16[j] = fp16((acc[j] + fp32(x[j])) / N)
+ * with x the chunk, every operation one fp32 operation and fp16 rounding to
+ * nearest even.  Calling it for index 0, 1, ..., N-1 in that order yields
+ * exactly the mean_fp16 of zero_reduce_mean_fp16 over the same chunks.
+ *
+ *   chunk       DEVICE fp16[n], 16-byte aligned
+ *   acc         DEVICE fp32[n], 16-byte aligned, caller-owned (unused, may be
+ *               NULL, when N == 1)
+ *   mean_fp16   DEVICE fp16[n], 16-byte aligned (read by no call; written by
+ *               the last one; may be NULL for the others)
+ * Written arrays must not overlap the chunk or each other.
+ * Returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN or ZERO_EHIP.
+ */
+int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n_chunks,
+                          float* acc, void* mean_fp16, void* stream);
+
+/*
  * zero_bucket_flatten -- pack whole fp16 gradient tensors into one bucket.
  *
  * Several parameters' gradients are grouped into a bucket and reduced as one

@@ -31,8 +31,8 @@ ZERO_EHIP = -4
 ZERO_MAX_CHUNKS = 64
 
 EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
-            "zero_shard_step_buckets", "zero_bucket_flatten", "zero_update_loss_scale",
-            "zero_last_error_string")
+            "zero_shard_step_buckets", "zero_reduce_mean_fp16", "zero_accumulate_chunk",
+            "zero_bucket_flatten", "zero_update_loss_scale", "zero_last_error_string")
 
 
 class ZeroStepError(RuntimeError):
@@ -89,6 +89,8 @@ def _load() -> ctypes.CDLL:
     lib.zero_shard_step_buckets.argtypes = [ctypes.POINTER(BucketSliceC), i32, i32,
                                              ctypes.c_float, i64, vp, vp, vp, vp, vp, vp, vp,
                                              ctypes.POINTER(AdamWParams), vp, vp, vp]
+    lib.zero_reduce_mean_fp16.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp, vp]
+    lib.zero_accumulate_chunk.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     lib.zero_bucket_flatten.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), i32, i64, i64,
                                         vp, i64, ctypes.POINTER(ctypes.c_int64), vp]
     lib.zero_update_loss_scale.argtypes = [ctypes.POINTER(LossScaler), i32,
@@ -268,6 +270,37 @@ def zero_shard_step_buckets(slices: BucketSlices, loss_scale: float, master_in: 
         _dev(param_fp16_out, torch.float16, "param_fp16_out"), ctypes.byref(hp),
         _opt(d_overflow, torch.int32, "d_overflow"), _opt(d_sqnorm, torch.float64, "d_sqnorm"),
         _stream(stream)))
+
+
+def zero_reduce_mean_fp16(grad_chunks: Sequence[torch.Tensor], mean_fp16: torch.Tensor,
+                          loss_scale: float = 1.0, d_overflow: Optional[torch.Tensor] = None,
+                          d_sqnorm: Optional[torch.Tensor] = None, stream=None) -> None:
+    """mean_fp16 = fp16(sum of the chunks / N); optional flag and squared norm
+    of fp32(mean_fp16) / loss_scale (see zero_step.h)."""
+    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+    n = mean_fp16.numel()
+    for i, c in enumerate(grad_chunks):
+        if c.numel() != n:
+            raise ValueError(f"grad_chunks[{i}] has {c.numel()} elements, expected {n}")
+    _check(lib.zero_reduce_mean_fp16(_ptr_array(ptrs), len(ptrs), n, float(loss_scale),
+                                     _dev(mean_fp16, torch.float16, "mean_fp16"),
+                                     _opt(d_overflow, torch.int32, "d_overflow"),
+                                     _opt(d_sqnorm, torch.float64, "d_sqnorm"), _stream(stream)))
+
+
+def zero_accumulate_chunk(chunk: torch.Tensor, index: int, n_chunks: int,
+                          acc: Optional[torch.Tensor], mean_fp16: Optional[torch.Tensor],
+                          stream=None) -> None:
+    """Fold replica `index`'s chunk into the fp32 accumulator; the last of
+    n_chunks writes the fp16 mean (see zero_step.h)."""
+    n = chunk.numel()
+    for name, t in (("acc", acc), ("mean_fp16", mean_fp16)):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    _check(lib.zero_accumulate_chunk(_dev(chunk, torch.float16, "chunk"), n, int(index),
+                                     int(n_chunks), _opt(acc, torch.float32, "acc"),
+                                     _opt(mean_fp16, torch.float16, "mean_fp16"),
+                                     _stream(stream)))
 
 
 def zero_bucket_flatten(tensors: Sequence[torch.Tensor], bucket: torch.Tensor,

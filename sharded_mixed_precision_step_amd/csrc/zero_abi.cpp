@@ -338,6 +338,66 @@ int zero_shard_step_buckets(const zero_bucket_slice* slices, int32_t n_slices, i
     return ok();
 }
 
+int zero_reduce_mean_fp16(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                          float loss_scale, void* mean_fp16, int32_t* d_overflow,
+                          double* d_sqnorm, void* stream) {
+    static const char* who = "zero_reduce_mean_fp16";
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    int rc = check_chunks(grad_chunks, n_chunks, n, loss_scale, &table, &gs);
+    if (rc) return rc;
+    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
+    if (n == 0) return ok();
+    if (!mean_fp16) return fail(ZERO_EINVAL, "%s: mean_fp16 is NULL", who);
+    if (!aligned(mean_fp16, 16)) return fail(ZERO_EALIGN, "%s: mean_fp16 is not 16-byte aligned", who);
+    for (int32_t c = 0; c < n_chunks; ++c)
+        if (overlap(mean_fp16, 2 * n, grad_chunks[c], 2 * n))
+            return fail(ZERO_EINVAL, "%s: mean_fp16 overlaps grad_chunks[%d]", who, c);
+    const hipError_t e =
+        zero::launch_reduce_mean(table, n_chunks, n, gs, static_cast<uint16_t*>(mean_fp16),
+                                 d_overflow, d_sqnorm, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
+int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n_chunks,
+                          float* acc, void* mean_fp16, void* stream) {
+    static const char* who = "zero_accumulate_chunk";
+    if (n_chunks < 1 || n_chunks > ZERO_MAX_CHUNKS)
+        return fail(ZERO_EINVAL, "%s: n_chunks = %d outside [1, %d]", who, n_chunks,
+                    ZERO_MAX_CHUNKS);
+    if (index < 0 || index >= n_chunks)
+        return fail(ZERO_EINVAL, "%s: index = %d outside [0, %d)", who, index, n_chunks);
+    if (n < 0) return fail(ZERO_EINVAL, "%s: n < 0", who);
+    const int mode = n_chunks == 1 ? 3 : index == 0 ? 0 : index == n_chunks - 1 ? 2 : 1;
+    const bool uses_acc = mode != 3, writes_mean = mode >= 2;
+    if (n == 0) return ok();
+    if (!chunk) return fail(ZERO_EINVAL, "%s: chunk is NULL", who);
+    if (!aligned(chunk, 16)) return fail(ZERO_EALIGN, "%s: chunk is not 16-byte aligned", who);
+    if (uses_acc) {
+        if (!acc) return fail(ZERO_EINVAL, "%s: acc is NULL", who);
+        if (!aligned(acc, 16)) return fail(ZERO_EALIGN, "%s: acc is not 16-byte aligned", who);
+        if (overlap(acc, 4 * n, chunk, 2 * n))
+            return fail(ZERO_EINVAL, "%s: acc overlaps chunk", who);
+    }
+    if (writes_mean) {
+        if (!mean_fp16) return fail(ZERO_EINVAL, "%s: mean_fp16 is NULL", who);
+        if (!aligned(mean_fp16, 16))
+            return fail(ZERO_EALIGN, "%s: mean_fp16 is not 16-byte aligned", who);
+        if (overlap(mean_fp16, 2 * n, chunk, 2 * n) ||
+            (uses_acc && overlap(mean_fp16, 2 * n, acc, 4 * n)))
+            return fail(ZERO_EINVAL, "%s: mean_fp16 overlaps chunk or acc", who);
+    }
+    zero::ChunkTable unused;
+    zero::GradScalars gs;
+    const void* none[1] = {nullptr};
+    int rc = check_chunks(none, n_chunks, 0, 1.0f, &unused, &gs);  // the 1/N scalars
+    if (rc) return rc;
+    const hipError_t e = zero::launch_accumulate(static_cast<const uint16_t*>(chunk), n, mode, gs,
+                                                 acc, static_cast<uint16_t*>(mean_fp16),
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
 int zero_bucket_flatten(const void* const* tensors, const int64_t* numels, int32_t n_tensors,
                         int64_t align, int64_t pad_multiple, void* bucket, int64_t bucket_capacity,
                         int64_t* offsets_out, void* stream) {

@@ -104,6 +104,14 @@ hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScal
 
 int64_t step_tiles(int64_t n);  // blocks of the fused step over n params
 
+hipError_t launch_reduce_mean(const ChunkTable& chunks, int n_chunks, int64_t n,
+                              const GradScalars& gs, uint16_t* mean16, int32_t* d_overflow,
+                              double* d_sqnorm, hipStream_t stream);
+
+// mode 0: acc = x; 1: acc += x; 2: mean16 = fp16((acc + x) / N); 3: mean16 = fp16(x)
+hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const GradScalars& gs,
+                             float* acc, uint16_t* mean16, hipStream_t stream);
+
 hipError_t launch_bucket_flatten(const FlattenTable& table, int count,
                                  int64_t max_slot_len, uint16_t* bucket,
                                  hipStream_t stream);

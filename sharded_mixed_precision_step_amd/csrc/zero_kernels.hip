@@ -44,10 +44,19 @@ __device__ __forceinline__ float load_widen1(const uint16_t* base, int64_t j) {
     return static_cast<float>(__builtin_bit_cast(_Float16, base[j]));
 }
 
+// mean = s / N
+__device__ __forceinline__ float mean_of(float s, const GradScalars& k) {
+    return k.mean_by_mul ? s * k.inv_n : s / k.n_f;
+}
+
+// g = mean / S
+__device__ __forceinline__ float unscaled(float mean, const GradScalars& k) {
+    return k.unscale_by_mul ? mean * k.inv_s : mean / k.s;
+}
+
 // g = (s / N) / S
 __device__ __forceinline__ float unscaled_mean(float s, const GradScalars& k) {
-    const float mean = k.mean_by_mul ? s * k.inv_n : s / k.n_f;
-    return k.unscale_by_mul ? mean * k.inv_s : mean / k.s;
+    return unscaled(mean_of(s, k), k);
 }
 
 __device__ __forceinline__ bool nonfinite(float x) {
@@ -303,6 +312,134 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     publish(bad, sq, d_overflow, d_sqnorm);
 }
 
+// The owner's gradient mean stored as fp16 (the page-literal split): mean16 =
+// fp16(sum / N), rounded to nearest even; with REDUCE, the flag and squared
+// norm of g = fp32(mean16) / S.  Read-heavy (N chunks in, one fp16 array out)
+// and reduced per block, so it runs the check's resident grid-stride loop.
+template <int NC, bool REDUCE>
+__global__ __launch_bounds__(kBlock) void reduce_mean_kernel(
+    ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs, uint16_t* __restrict__ mean16,
+    int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
+    const int64_t packs = n / kPack;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    const int nc = NC > 0 ? NC : n_chunks;
+    bool bad = false;
+    double sq = 0.0;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < packs;
+         i += stride) {
+        f8 s = load_widen8_nt(chunks.p[0], i);
+#pragma unroll
+        for (int c = 1; c < nc; ++c) s += load_widen8_nt(chunks.p[c], i);
+        u16x8 out;
+#pragma unroll
+        for (int e = 0; e < kPack; ++e) {
+            const _Float16 h = static_cast<_Float16>(mean_of(s[e], gs));
+            out[e] = __builtin_bit_cast(uint16_t, h);
+            if constexpr (REDUCE) {
+                const float g = unscaled(static_cast<float>(h), gs);
+                bad |= nonfinite(g);
+                sq += static_cast<double>(g) * static_cast<double>(g);
+            }
+        }
+        *reinterpret_cast<u16x8*>(mean16 + i * kPack) = out;
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        const int64_t j = packs * kPack + threadIdx.x;
+        if (j < n) {
+            const _Float16 h =
+                static_cast<_Float16>(mean_of(replica_sum1<NC>(chunks.p, n_chunks, j), gs));
+            mean16[j] = __builtin_bit_cast(uint16_t, h);
+            if constexpr (REDUCE) {
+                const float g = unscaled(static_cast<float>(h), gs);
+                bad |= nonfinite(g);
+                sq += static_cast<double>(g) * static_cast<double>(g);
+            }
+        }
+    }
+    if constexpr (REDUCE) publish(bad, sq, d_overflow, d_sqnorm);
+}
+
+// One replica's chunk arriving at its owner, folded into an fp32
+// accumulator.  MODE: 0 the first of N > 1 (acc = x), 1 a middle one
+// (acc = acc + x), 2 the last of N > 1 (mean16 = fp16((acc + x) / N)), 3 the
+// only one (mean16 = fp16(x / 1)).  One-shot tiles, as the step.
+template <int MODE>
+__device__ __forceinline__ void accumulate_elems(const f8& x, const f4& a0, const f4& a1,
+                                                 const GradScalars& gs, f4& o0, f4& o1,
+                                                 u16x8& out) {
+    const f4 x0 = {x[0], x[1], x[2], x[3]}, x1 = {x[4], x[5], x[6], x[7]};
+    if constexpr (MODE == 0) {
+        o0 = x0;
+        o1 = x1;
+    } else if constexpr (MODE == 1) {
+        o0 = a0 + x0;
+        o1 = a1 + x1;
+    } else {
+        const f4 s0 = MODE == 2 ? a0 + x0 : x0, s1 = MODE == 2 ? a1 + x1 : x1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            out[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(mean_of(s0[e], gs)));
+            out[e + 4] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(mean_of(s1[e], gs)));
+        }
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(const uint16_t* __restrict__ chunk,
+                                                            int64_t n, GradScalars gs,
+                                                            float* acc,
+                                                            uint16_t* __restrict__ mean16) {
+    constexpr bool kReadAcc = MODE == 1 || MODE == 2;
+    constexpr bool kWriteAcc = MODE == 0 || MODE == 1;
+    const int64_t packs = n / kPack;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kTilePacks +
+                          wave * (kWaveSpan * 64) + lane;
+    f8 x[kWaveSpan];
+    f4 a[kWaveSpan][2];
+#pragma unroll
+    for (int u = 0; u < kWaveSpan; ++u) {
+        const int64_t i = first + u * 64;
+        if (i >= packs) continue;
+        x[u] = load_widen8(chunk, i);
+        if constexpr (kReadAcc) {
+            a[u][0] = reinterpret_cast<const f4*>(acc)[2 * i];
+            a[u][1] = reinterpret_cast<const f4*>(acc)[2 * i + 1];
+        } else {
+            a[u][0] = a[u][1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kWaveSpan; ++u) {
+        const int64_t i = first + u * 64;
+        if (i >= packs) continue;
+        f4 o0, o1;
+        u16x8 out;
+        accumulate_elems<MODE>(x[u], a[u][0], a[u][1], gs, o0, o1, out);
+        if constexpr (kWriteAcc) {
+            reinterpret_cast<f4*>(acc)[2 * i] = o0;
+            reinterpret_cast<f4*>(acc)[2 * i + 1] = o1;
+        } else {
+            *reinterpret_cast<u16x8*>(mean16 + i * kPack) = out;
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        const int64_t j = packs * kPack + threadIdx.x;
+        if (j < n) {
+            const float xj = load_widen1(chunk, j);
+            if constexpr (MODE == 0) {
+                acc[j] = xj;
+            } else if constexpr (MODE == 1) {
+                acc[j] = acc[j] + xj;
+            } else {
+                const float sj = MODE == 2 ? acc[j] + xj : xj;
+                mean16[j] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(mean_of(sj, gs)));
+            }
+        }
+    }
+}
+
 // One slot per blockIdx.y: the tensor's elements, then zeros up to the next
 // slot.  Slots are disjoint, so blocks never write the same element.  Block x
 // copies the slot's tile x (kFlattenTile elements; a one-shot grid, as for
@@ -402,6 +539,17 @@ hipError_t bucket_impl(const BucketTable& t, int n_chunks, const GradScalars& gs
     return hipGetLastError();
 }
 
+template <int NC, bool REDUCE>
+hipError_t mean_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
+                     uint16_t* mean16, int32_t* d_overflow, double* d_sqnorm,
+                     hipStream_t stream) {
+    const int64_t grid = check_grid(n);
+    hipLaunchKernelGGL((reduce_mean_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, mean16, d_overflow,
+                       d_sqnorm);
+    return hipGetLastError();
+}
+
 template <int NC>
 hipError_t check_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
                       int32_t* d_overflow, double* d_sqnorm, hipStream_t stream) {
@@ -466,6 +614,51 @@ hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScal
                                                   stream);
     }
 #undef ZERO_CASE
+}
+
+hipError_t launch_reduce_mean(const ChunkTable& chunks, int n_chunks, int64_t n,
+                              const GradScalars& gs, uint16_t* mean16, int32_t* d_overflow,
+                              double* d_sqnorm, hipStream_t stream) {
+    const bool reduce = d_overflow != nullptr || d_sqnorm != nullptr;
+#define ZERO_CASE(K)                                                                            \
+    case K:                                                                                     \
+        return reduce ? mean_impl<K, true>(chunks, n_chunks, n, gs, mean16, d_overflow,         \
+                                           d_sqnorm, stream)                                    \
+                      : mean_impl<K, false>(chunks, n_chunks, n, gs, mean16, d_overflow,        \
+                                            d_sqnorm, stream);
+    switch (n_chunks) {
+        ZERO_FOR_EACH_N(ZERO_CASE)
+        default:
+            return reduce ? mean_impl<0, true>(chunks, n_chunks, n, gs, mean16, d_overflow,
+                                               d_sqnorm, stream)
+                          : mean_impl<0, false>(chunks, n_chunks, n, gs, mean16, d_overflow,
+                                                d_sqnorm, stream);
+    }
+#undef ZERO_CASE
+}
+
+hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const GradScalars& gs,
+                             float* acc, uint16_t* mean16, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(step_tiles(n))), block(kBlock);
+    switch (mode) {
+        case 0:
+            hipLaunchKernelGGL(accumulate_kernel<0>, grid, block, 0, stream, chunk, n, gs, acc,
+                               mean16);
+            break;
+        case 1:
+            hipLaunchKernelGGL(accumulate_kernel<1>, grid, block, 0, stream, chunk, n, gs, acc,
+                               mean16);
+            break;
+        case 2:
+            hipLaunchKernelGGL(accumulate_kernel<2>, grid, block, 0, stream, chunk, n, gs, acc,
+                               mean16);
+            break;
+        default:
+            hipLaunchKernelGGL(accumulate_kernel<3>, grid, block, 0, stream, chunk, n, gs, acc,
+                               mean16);
+            break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_overflow_check(const ChunkTable& chunks, int n_chunks, int64_t n,

@@ -211,6 +211,33 @@ def test_shard_step_buckets_rejects_bad_slices():
     assert _buckets([], 2, 0, (None,) * 3, (None,) * 4, _hp()) == zs.ZERO_OK
 
 
+def test_reduce_mean_and_accumulate_reject_bad_arguments():
+    B = A + (1 << 20)
+    n = 1000
+    rm = lambda chunks, nc, nn, mean, S=1.0, flag=None: zs.lib.zero_reduce_mean_fp16(
+        chunks, nc, nn, S, mean, flag, None, None)
+    assert rm(_ptrs(A, A + 4096), 2, n, None) == zs.ZERO_EINVAL
+    assert rm(_ptrs(A, A + 4096), 2, n, B + 2) == zs.ZERO_EALIGN
+    assert rm(_ptrs(A, A + 4096), 2, n, A + 1024) == zs.ZERO_EINVAL      # over a chunk
+    assert rm(_ptrs(A, A + 4096), 2, n, B, S=0.0) == zs.ZERO_EINVAL
+    assert rm(_ptrs(A, A + 4096), 2, n, B, flag=A + 2) == zs.ZERO_EALIGN
+    assert rm(_ptrs(A, A + 4), 2, n, B) == zs.ZERO_EALIGN
+    assert rm(_ptrs(0, 0), 2, 0, None) == zs.ZERO_OK                    # n == 0: no-op
+    acc = lambda ch, nn, idx, nc, a, mean: zs.lib.zero_accumulate_chunk(ch, nn, idx, nc, a,
+                                                                        mean, None)
+    assert acc(A, n, 3, 3, B, B + 8192) == zs.ZERO_EINVAL               # index past N - 1
+    assert acc(A, n, -1, 3, B, B + 8192) == zs.ZERO_EINVAL
+    assert acc(A, n, 0, 0, B, B + 8192) == zs.ZERO_EINVAL
+    assert acc(A, n, 0, 3, None, None) == zs.ZERO_EINVAL                # first needs acc
+    assert acc(A, n, 1, 3, B + 4, None) == zs.ZERO_EALIGN
+    assert acc(A, n, 2, 3, B, None) == zs.ZERO_EINVAL                   # last needs the mean
+    assert acc(A, n, 2, 3, B, B + 1024) == zs.ZERO_EINVAL               # mean over acc
+    assert acc(A, n, 0, 3, A + 512, None) == zs.ZERO_EINVAL             # acc over the chunk
+    assert acc(A + 8, n, 0, 1, None, B) == zs.ZERO_EALIGN
+    assert acc(None, n, 0, 1, None, B) == zs.ZERO_EINVAL
+    assert acc(None, 0, 0, 1, None, None) == zs.ZERO_OK                 # n == 0: no-op
+
+
 def _flatten(ptrs, numels, align, pad, bucket, cap):
     nt = len(numels)
     offs = (ctypes.c_int64 * (nt + 1))()
