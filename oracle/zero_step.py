@@ -50,6 +50,8 @@ squared norm -> constant-gradient closed form and an exactly rounded sum;
 moments and master -> first-step closed form, zero-gradient and lr = 0
 invariants, and the N = 1, S = 1 special case against torch.optim.AdamW;
 fp16 writeback -> IEEE binary16 bit patterns and torch's own rounding;
+clip coefficient -> torch.nn.utils.clip_grad_norm_ in fp64, and the
+constant-gradient closed form;
 fp16 mean -> exact rational means rounded by hand-coded binary16 rounding on
 exactly summable inputs, and identical replicas (the fp16 mean is then the
 replica itself, and the split equals the fused step bit for bit).
@@ -57,6 +59,7 @@ replica itself, and the split equals the fused step bit for bit).
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Sequence
 
 import numpy as np
@@ -197,6 +200,37 @@ def shard_step(chunks, master, m, v, p16, hyper, loss_scale,
     """
     return step_from_grad(unscaled_grad(chunks, loss_scale), master, m, v, p16, hyper,
                           sqnorm_start)
+
+
+# --------------------------------------------------------------------------
+# Gradient-norm clipping (not on the pages; the usual global-norm rule).
+# --------------------------------------------------------------------------
+
+CLIP_EPS = 1e-6
+
+
+def clip_coefficient(sqnorm: float, max_norm: float) -> np.float32:
+    """The factor that scales g so that its 2-norm is at most max_norm:
+    min(1, max_norm / (sqrt(sum g^2) + 1e-6)), evaluated in fp64 from the fp64
+    squared norm and rounded once to fp32.  max_norm <= 0 means no clipping
+    (factor 1).  The norm is that of the unscaled mean gradient of the whole
+    shard, taken before clipping."""
+    if not max_norm > 0.0:
+        return F32(1.0)
+    coef = float(max_norm) / (math.sqrt(float(sqnorm)) + CLIP_EPS)
+    return F32(min(1.0, coef))
+
+
+def shard_step_clipped(chunks, master, m, v, p16, hyper, loss_scale, max_norm) -> StepResult:
+    """The two-pass step with clipping: the flag and squared norm of g first,
+    then (unless the step is skipped) the update from fl32(g * coef)."""
+    g = unscaled_grad(chunks, loss_scale)
+    flag = nonfinite(g)
+    sq = grad_sqnorm(g)
+    if flag:
+        return StepResult(True, sq, master.copy(), m.copy(), v.copy(), p16.copy())
+    master1, m1, v1, p161 = adamw_update(g * clip_coefficient(sq, max_norm), master, m, v, hyper)
+    return StepResult(False, sq, master1, m1, v1, p161)
 
 
 # --------------------------------------------------------------------------

@@ -139,6 +139,52 @@ def pin_mean_of_distinct_replicas():
 
 
 # --------------------------------------------------------------------------
+# Gradient-norm clipping.
+# --------------------------------------------------------------------------
+
+def pin_clip_matches_torch():
+    """With fp64 gradients, torch.nn.utils.clip_grad_norm_ scales them by
+    min(1, max_norm / (norm + 1e-6)); the oracle's fp32 clipped gradient
+    agrees to within 2 fp32 roundings, and is left exactly unchanged when the
+    norm is below the limit."""
+    import torch
+    chunks = [host_fp16_grad(seed_of(99, i), 30011, 1e-2, 1024.0) for i in range(4)]
+    g = zs.unscaled_grad(chunks, 1024.0)
+    sq = zs.grad_sqnorm(g)
+    norm = math.sqrt(sq)
+    for max_norm in (0.25 * norm, 0.999 * norm, 2.0 * norm, 0.0, -1.0):
+        t = torch.nn.Parameter(torch.zeros(g.size, dtype=torch.float64))
+        t.grad = torch.from_numpy(g.astype(np.float64))
+        if max_norm > 0:
+            torch.nn.utils.clip_grad_norm_([t], max_norm)
+        want = t.grad.numpy()
+        got = (g * zs.clip_coefficient(sq, max_norm)).astype(np.float64)
+        assert np.all(np.abs(got - want) <= 2 * 2.0 ** -24 * np.abs(want)), max_norm
+        if not (0 < max_norm < norm):
+            assert zs.clip_coefficient(sq, max_norm) == 1.0
+            assert np.array_equal(_bits32(g * zs.clip_coefficient(sq, max_norm)), _bits32(g))
+
+
+def pin_clip_closed_form():
+    """Constant gradient c over n elements: the norm is |c| sqrt(n), so the
+    factor is max_norm / (|c| sqrt(n) + 1e-6)."""
+    n, c = 4096, 0.5                     # sum of squares 1024 exactly, norm 32
+    ch = [np.full(n, c, np.float16)]
+    r = zs.shard_step_clipped(ch, *(_zeros_state(n)), AdamWHyper(step=1, lr=1.0,
+                                                               weight_decay=0.0), 1.0, 8.0)
+    assert r.sqnorm == n * c * c
+    assert zs.clip_coefficient(r.sqnorm, 8.0) == np.float32(8.0 / (32.0 + 1e-6))
+    # first step, m = v = 0: m' = (1 - b1) * g_clipped
+    gc = np.float32(c) * np.float32(8.0 / (32.0 + 1e-6))
+    assert np.all(r.m == np.float32(1 - np.float32(0.9)) * gc)
+
+
+def _zeros_state(n):
+    master = np.zeros(n, np.float32)
+    return master, np.zeros(n, np.float32), np.zeros(n, np.float32), master.astype(np.float16)
+
+
+# --------------------------------------------------------------------------
 # The page-literal split: the owner's mean stored as fp16.
 # --------------------------------------------------------------------------
 

@@ -164,7 +164,24 @@ def _split_unscale_multiplies(mean16, master, m, v, p16, hyper, loss_scale, sqno
     return zs.step_from_grad(g, master, m, v, p16, hyper, sqnorm_start)
 
 
+def _clip_variant(kind):
+    def coef(sqnorm, max_norm):
+        if not max_norm > 0.0:
+            return F32(1.0)
+        if kind == "no_clamp":
+            return F32(max_norm / (np.sqrt(sqnorm) + 1e-6))
+        if kind == "squared_norm":
+            return F32(min(1.0, max_norm / (sqnorm + 1e-6)))
+        if kind == "inverted":
+            return F32(min(1.0, (np.sqrt(sqnorm) + 1e-6) / max_norm))
+        raise ValueError(kind)
+    return coef
+
+
 MUTATIONS.update({
+    "clip_not_clamped_to_one": (zs, "clip_coefficient", _clip_variant("no_clamp")),
+    "clip_by_squared_norm": (zs, "clip_coefficient", _clip_variant("squared_norm")),
+    "clip_inverted": (zs, "clip_coefficient", _clip_variant("inverted")),
     "mean16_rounds_toward_zero": (zs, "replica_mean_fp16", _mean16_toward_zero),
     "mean16_not_divided": (zs, "replica_mean_fp16",
                            lambda chunks: zs.replica_sum(chunks).astype(np.float16)),
