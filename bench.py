@@ -5,12 +5,14 @@ rank owns 1,003,750,000 params), 8 fp16 replica gradient chunks in HBM,
 loss scale 65536, AdamW at t = 1000 with non-zero fp32 m and v.  Inputs are
 seeded synthetic draws made on the device before timing starts.
 
-One timed step is the whole per-rank path in its single-pass form: zero the
-device flag and norm; run the fused update (replica sum, mean, unscale,
-inf/NaN flag, squared norm, moments, fp32 master, fp16 params) from the
-current copy of the state into the other copy; read the flag back; update
-the dynamic loss scale on the host; and commit the written copy if the step
-is clean.  The two-pass form (overflow check, then the in-place update) and
+One timed step is the whole per-rank path in its single-pass form, with the
+decision on the device: start the step in the control block; run the fused
+update (replica sum, mean, unscale, inf/NaN flag, squared norm, moments,
+fp32 master, fp16 params) from the current copy of the state into the other
+copy; then decide on the device (skip, loss-scale move, t, and commit of the
+written copy if the step is clean).  Nothing is read back between steps.
+The host-decided single pass (flag read-back, host loss scale, swap) is
+timed afterwards and reported under "extra".  The two-pass form (overflow check, then the in-place update) and
 the page-literal split (the gradient mean stored as fp16, then the update
 from it) are timed afterwards on the same state and reported under "extra".
 
@@ -147,37 +149,28 @@ def main():
         log(f"bench: cpu oracle {cpu['value']:.3e} params/s on {cpu['cores']} threads "
             f"({cpu['seconds']:.1f} s)")
 
-    flag = torch.zeros(1, dtype=torch.int32, device=dev)
-    sq = torch.zeros(1, dtype=torch.float64, device=dev)
-    scaler = zs.LossScaler.create(scale=w.loss_scale)
-    hp = zs.adamw_params(w.hyper)
     stream = torch.cuda.current_stream()
     shard = zs.DoubleBufferedShard(d["master"], d["m"], d["v"], d["p16"])
+    ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
     fused_events = []
-    skipped = 0
 
     def step(record: bool):
-        """The single-pass step: fused out-of-place update with the flag and
-        squared norm, flag read-back, loss-scale update, commit if clean."""
-        nonlocal skipped
-        flag.zero_()
-        sq.zero_()
-        scale = scaler.scale
-        m_in, a_in, v_in, _ = shard.current
-        m_out, a_out, v_out, p_out = shard.other
+        """One step under the device control block: begin, the fused
+        out-of-place update (flag and squared norm into the block), then the
+        decision, loss-scale move and commit on the device.  Nothing is read
+        back, so the host enqueues the next step at once."""
+        stepper._rebase()
+        zs.zero_control_begin(ctl, stream=stream)
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
-        zs.zero_shard_step_out(d["chunks"], scale, m_in, a_in, v_in, m_out, a_out, v_out, p_out,
-                               hp, flag, sq, stream=stream)
+        zs.zero_shard_step_out_ctl(d["chunks"], shard.copies, stepper.hp, ctl, stream=stream)
         if record:
             e[1].record(stream)
             fused_events.append(e)
-        if zs.zero_update_loss_scale(scaler, int(flag.item())):
-            skipped += 1
-            return
-        shard.cur = 1 - shard.cur
-        hp.step += 1
+        zs.zero_control_decide(ctl, 0.0, True, stream=stream)
+        stepper.since_base += 1
 
     for _ in range(args.warmup):
         step(False)
@@ -189,8 +182,20 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     k1_ms = sum(a.elapsed_time(b) for a, b in fused_events) / max(len(fused_events), 1)
-    log(f"bench: single-pass {ms_per_step:.3f} ms/step, fused step {k1_ms:.3f} ms, "
-        f"skipped {skipped}")
+    c = zs.control_read(ctl)
+    if c.error:
+        raise RuntimeError(f"step control reported error {c.error}")
+    skipped = c.skipped_steps
+    log(f"bench: device single pass {ms_per_step:.3f} ms/step, fused step {k1_ms:.3f} ms, "
+        f"skipped {skipped}, t = {c.step}")
+    # the other forms continue from the current copy at the block's t and scale
+    shard.cur = c.cur & 1
+    scaler = zs.LossScaler.create(scale=c.scale)
+    hp = zs.adamw_params(w.hyper.replace(step=int(c.step)))
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    sq = torch.zeros(1, dtype=torch.float64, device=dev)
+    host = host_single_pass(zs, d, shard, scaler, hp, flag, sq, stream, args.two_pass_steps, n)
+    log(f"bench: host-synced single pass {host['host_single_pass_ms_per_step']:.3f} ms/step")
     two = two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, args.two_pass_steps)
     log(f"bench: two-pass {two['two_pass_ms_per_step']:.3f} ms/step, check "
         f"{two['check_ms']:.3f} ms, in-place step {two['inplace_step_ms']:.3f} ms")
@@ -202,19 +207,22 @@ def main():
     k1_gbps = k1_bytes / (k1_ms * 1e-3) / 1e9
     traffic = read_traffic(_build.kernel_digest(), n)
     extra = {
-        "path": "single pass: zero_shard_step_out with flag and squared norm, "
-                "flag read-back, zero_update_loss_scale, commit by buffer swap",
+        "path": "single pass under the device control block: zero_control_begin, "
+                "zero_shard_step_out_ctl (flag and squared norm), zero_control_decide "
+                "(skip, loss scale, t, commit); no read-back inside the loop",
         "fused_step_ms": k1_ms, "fused_step_params_per_s": n / (k1_ms * 1e-3),
         "fused_step_gbps": k1_gbps, "fused_step_pct_peak": 100 * k1_gbps / HBM_PEAK_GBPS,
         "step_gbps": k1_bytes / (ms_per_step * 1e-3) / 1e9,
         "skipped_steps": skipped,
     }
+    extra.update(host)
     extra.update(two)
     extra.update(lit)
 
     if not args.no_flatten:
         extra.update(bench_flatten(zs, wl, dev, stream))
     extra.update(copy_ceiling(dev, stream))
+    extra.update(tiny_graph(dev))
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -356,6 +364,68 @@ def bench_zero2(args, dev):
         },
     }
     print(json.dumps(out_line), flush=True)
+
+
+def host_single_pass(zs, d, shard, scaler, hp, flag, sq, stream, steps: int, n: int):
+    """The single pass with the decision on the host: fused out-of-place
+    update, flag read-back, zero_update_loss_scale, commit by swapping."""
+    import torch
+    t0 = None
+    for k in range(steps + 1):           # the first step is an untimed warm-up
+        if k == 1:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        zs.committed_step(d["chunks"], shard, hp, scaler, flag, sq, stream=stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"host_single_pass_ms_per_step": ms,
+            "host_single_pass_params_per_s": n / (ms * 1e-3)}
+
+
+def tiny_graph(dev, steps: int = 200):
+    """The tiny workload (1,000,003 params, N = 3), launch-bound: one
+    device-controlled single-pass step as eager launches versus the same step
+    captured once in a HIP graph and replayed."""
+    import torch
+
+    import sharded_mixed_precision_step_amd as zs
+    import workloads as wl
+
+    w = wl.TINY
+    d = wl.device_shard(w, dev)
+    copies = ((d["master"], d["m"], d["v"], d["p16"]),
+              tuple(torch.empty_like(t) for t in (d["master"], d["m"], d["v"], d["p16"])))
+
+    def fresh():
+        ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+        return ctl, zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+
+    ctl, st = fresh()
+    for _ in range(3):
+        st.single_pass(d["chunks"], copies)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.single_pass(d["chunks"], copies)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) * 1e6 / steps
+    ctl, st = fresh()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.single_pass(d["chunks"], copies)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = min(steps, zs.ZERO_CTL_STEPS - 4)   # t stays inside the captured table
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) * 1e6 / reps
+    assert zs.control_read(ctl).error == 0
+    return {"tiny_eager_us_per_step": eager_us, "tiny_graph_us_per_step": graph_us,
+            "tiny_graph_params_per_s": w.n / (graph_us * 1e-6)}
 
 
 def two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):

@@ -75,6 +75,40 @@ typedef struct zero_loss_scaler {
     int64_t skipped_steps;   /* total skipped steps                             */
 } zero_loss_scaler;
 
+/* Step control block, kept in DEVICE memory: the dynamic loss scale, the
+ * update counter t and the decision of the step in flight.  With it a whole
+ * step -- check, decision, update (two-pass, optionally with gradient-norm
+ * clipping), or fused update, decision, commit (single pass) -- is enqueued
+ * without the host reading anything back; the host copies the block back
+ * whenever it wants to look.  The caller allocates sizeof(zero_step_control)
+ * bytes, 8-byte aligned, fills a host copy with zero_control_init and copies
+ * it to the device.  Calls that take it run on `stream` in order; calls on
+ * one block must not overlap in time. */
+typedef struct zero_step_control {
+    /* dynamic loss scale: the same state and rules as zero_loss_scaler */
+    float scale;             /* S of the next step                              */
+    float growth_factor;
+    float backoff_factor;
+    float min_scale;
+    float max_scale;
+    int32_t growth_interval;
+    int32_t good_steps;
+    int32_t cur;             /* single pass: the current copy of the state (0/1) */
+    int64_t skipped_steps;
+    int64_t step;            /* t of the next applied update, >= 1               */
+    /* the step in flight (zero_control_begin sets these) */
+    int64_t step_used;       /* t this step's update uses                        */
+    double sqnorm;           /* sum of g^2 of this step                          */
+    float scale_used;        /* S this step's gradients are unscaled by          */
+    float clip_coef;         /* factor on g of this step's update (1: none)      */
+    int32_t overflow;        /* non-finite flag of this step                     */
+    int32_t skip;            /* the decision: 1 = the update was skipped         */
+    int32_t error;           /* bit 0: step_used was outside the update's table
+                                of bias corrections and nothing was updated;
+                                sticky until the host clears it                 */
+    int32_t reserved;
+} zero_step_control;
+
 /*
  * zero_overflow_check -- overflow flag and squared norm of the unscaled mean
  * gradient, without touching any optimizer state.
@@ -319,6 +353,64 @@ int zero_bucket_flatten(const void* const* tensors, const int64_t* numels,
  * Returns ZERO_OK or ZERO_EINVAL (state left unchanged).
  */
 int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_out);
+
+/*
+ * Device-resident step control.
+ *
+ * zero_control_init (HOST, synchronous): fill *ctl from a validated loss
+ * scaler and the first update's t (>= 1); the in-flight fields are cleared,
+ * cur = 0.  Returns ZERO_OK or ZERO_EINVAL.
+ *
+ * zero_control_begin: start a step: overflow = 0, sqnorm = 0, skip = 0,
+ * clip_coef = 1, scale_used = scale, step_used = step.
+ *
+ * zero_overflow_check_ctl: zero_overflow_check with S = d_ctl->scale_used,
+ * accumulating into d_ctl->overflow and d_ctl->sqnorm.
+ *
+ * zero_control_decide: the decision, on the device, after the step's check
+ * (two-pass) or fused update (single pass): skip = (overflow != 0); the
+ * scale moves as zero_update_loss_scale moves it; on a clean step t advances
+ * (step += 1), clip_coef = min(1, max_grad_norm / (sqrt(sqnorm) + 1e-6))
+ * evaluated in fp64 and rounded to fp32 when max_grad_norm > 0 (else 1), and
+ * if flip_copy is non-zero cur switches to the other copy.
+ *
+ * zero_shard_step_ctl: the two-pass update, in place: if d_ctl->skip is set
+ * nothing is touched; otherwise zero_shard_step with S = scale_used,
+ * g multiplied by clip_coef (one fp32 multiply) before the moments, and the
+ * bias corrections of t = step_used.
+ *
+ * zero_shard_step_out_ctl: the single-pass update: zero_shard_step_out from
+ * copy cur into copy 1 - cur (masters[2], exp_avgs[2], exp_avg_sqs[2],
+ * params_fp16[2]: HOST arrays of two DEVICE pointers each), with
+ * S = scale_used and the bias corrections of t = step_used, accumulating the
+ * flag and squared norm into d_ctl.  Follow it with zero_control_decide(...,
+ * flip_copy = 1): a clean step then makes the written copy current.
+ *
+ * Bias corrections: hp->step is the base t0 of a table the call computes
+ * for t = t0 .. t0 + ZERO_CTL_STEPS - 1 (1 - beta^t in fp64, rounded to fp32,
+ * as for the host calls); a step whose step_used falls outside it sets bit 0
+ * of d_ctl->error and updates nothing.  The caller keeps t0 within reach:
+ * t can only have grown by the number of steps enqueued since it last read
+ * the block.  Other arguments are as for the calls without _ctl; d_ctl is
+ * DEVICE, 8-byte aligned.  Each returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN or
+ * ZERO_EHIP.
+ */
+#define ZERO_CTL_STEPS 64
+
+int zero_control_init(zero_step_control* ctl, const zero_loss_scaler* scaler, int64_t step);
+int zero_control_begin(zero_step_control* d_ctl, void* stream);
+int zero_overflow_check_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                            zero_step_control* d_ctl, void* stream);
+int zero_control_decide(zero_step_control* d_ctl, float max_grad_norm, int32_t flip_copy,
+                        void* stream);
+int zero_shard_step_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                        float* master, float* exp_avg, float* exp_avg_sq, void* param_fp16,
+                        const zero_adamw_params* hp, zero_step_control* d_ctl, void* stream);
+int zero_shard_step_out_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                            float* const* masters, float* const* exp_avgs,
+                            float* const* exp_avg_sqs, void* const* params_fp16,
+                            const zero_adamw_params* hp, zero_step_control* d_ctl,
+                            void* stream);
 
 /* Text of the last error reported by a call on this thread ("" if none). */
 const char* zero_last_error_string(void);

@@ -32,7 +32,10 @@ ZERO_MAX_CHUNKS = 64
 
 EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
             "zero_shard_step_buckets", "zero_reduce_mean_fp16", "zero_accumulate_chunk",
-            "zero_bucket_flatten", "zero_update_loss_scale", "zero_last_error_string")
+            "zero_bucket_flatten", "zero_update_loss_scale", "zero_control_init",
+            "zero_control_begin", "zero_overflow_check_ctl", "zero_control_decide",
+            "zero_shard_step_ctl", "zero_shard_step_out_ctl", "zero_last_error_string")
+ZERO_CTL_STEPS = 64
 
 
 class ZeroStepError(RuntimeError):
@@ -59,6 +62,19 @@ class LossScaler(ctypes.Structure):
                min_scale=1.0, max_scale=float(2 ** 24), growth_interval=1000):
         return cls(scale, growth_factor, backoff_factor, min_scale, max_scale,
                    growth_interval, 0, 0)
+
+
+class StepControl(ctypes.Structure):
+    """zero_step_control: the device-resident loss scale, t and step decision."""
+    _fields_ = [("scale", ctypes.c_float), ("growth_factor", ctypes.c_float),
+                ("backoff_factor", ctypes.c_float), ("min_scale", ctypes.c_float),
+                ("max_scale", ctypes.c_float), ("growth_interval", ctypes.c_int32),
+                ("good_steps", ctypes.c_int32), ("cur", ctypes.c_int32),
+                ("skipped_steps", ctypes.c_int64), ("step", ctypes.c_int64),
+                ("step_used", ctypes.c_int64), ("sqnorm", ctypes.c_double),
+                ("scale_used", ctypes.c_float), ("clip_coef", ctypes.c_float),
+                ("overflow", ctypes.c_int32), ("skip", ctypes.c_int32),
+                ("error", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class BucketSliceC(ctypes.Structure):
@@ -95,6 +111,15 @@ def _load() -> ctypes.CDLL:
                                         vp, i64, ctypes.POINTER(ctypes.c_int64), vp]
     lib.zero_update_loss_scale.argtypes = [ctypes.POINTER(LossScaler), i32,
                                            ctypes.POINTER(ctypes.c_int32)]
+    lib.zero_control_init.argtypes = [ctypes.POINTER(StepControl), ctypes.POINTER(LossScaler),
+                                      i64]
+    lib.zero_control_begin.argtypes = [vp, vp]
+    lib.zero_overflow_check_ctl.argtypes = [pp, i32, i64, vp, vp]
+    lib.zero_control_decide.argtypes = [vp, ctypes.c_float, i32, vp]
+    lib.zero_shard_step_ctl.argtypes = [pp, i32, i64, vp, vp, vp, vp, ctypes.POINTER(AdamWParams),
+                                        vp, vp]
+    lib.zero_shard_step_out_ctl.argtypes = [pp, i32, i64, pp, pp, pp, pp,
+                                            ctypes.POINTER(AdamWParams), vp, vp]
     lib.zero_last_error_string.argtypes = []
     lib.zero_last_error_string.restype = ctypes.c_char_p
     for name in EXPORTED[:-1]:
@@ -394,3 +419,125 @@ def committed_step(grad_chunks, shard: DoubleBufferedShard, hp: AdamWParams,
         shard.cur = 1 - shard.cur
         hp.step += 1
     return ShardStepResult(bool(flag), skip, float(d_sqnorm.item()))
+
+
+# ---------------------------------------------------------------------------
+# Device-resident step control: the whole step enqueued with no read-back.
+# ---------------------------------------------------------------------------
+
+def control_new(scaler: LossScaler, step: int, device) -> torch.Tensor:
+    """A zero_step_control block in device memory (a uint8 tensor), filled
+    from the scaler and the first update's t."""
+    host = StepControl()
+    _check(lib.zero_control_init(ctypes.byref(host), ctypes.byref(scaler), int(step)))
+    raw = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8)
+    return raw.to(device)
+
+
+def control_read(ctl: torch.Tensor) -> StepControl:
+    """A host copy of the block (synchronises with the device)."""
+    return StepControl.from_buffer_copy(ctl.cpu().numpy().tobytes())
+
+
+def _ctl(ctl: torch.Tensor) -> int:
+    if ctl.dtype != torch.uint8 or ctl.numel() != ctypes.sizeof(StepControl):
+        raise TypeError("ctl must be the uint8 tensor control_new returns")
+    return _dev(ctl, torch.uint8, "ctl")
+
+
+def zero_control_begin(ctl: torch.Tensor, stream=None) -> None:
+    _check(lib.zero_control_begin(_ctl(ctl), _stream(stream)))
+
+
+def zero_overflow_check_ctl(grad_chunks: Sequence[torch.Tensor], ctl: torch.Tensor,
+                            stream=None) -> None:
+    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+    n = grad_chunks[0].numel() if grad_chunks else 0
+    for i, c in enumerate(grad_chunks):
+        if c.numel() != n:
+            raise ValueError(f"grad_chunks[{i}] has {c.numel()} elements, expected {n}")
+    _check(lib.zero_overflow_check_ctl(_ptr_array(ptrs), len(ptrs), n, _ctl(ctl),
+                                       _stream(stream)))
+
+
+def zero_control_decide(ctl: torch.Tensor, max_grad_norm: float = 0.0, flip_copy: bool = False,
+                        stream=None) -> None:
+    _check(lib.zero_control_decide(_ctl(ctl), float(max_grad_norm), int(bool(flip_copy)),
+                                   _stream(stream)))
+
+
+def zero_shard_step_ctl(grad_chunks: Sequence[torch.Tensor], master: torch.Tensor,
+                        exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                        param_fp16: torch.Tensor, hp: AdamWParams, ctl: torch.Tensor,
+                        stream=None) -> None:
+    """The two-pass update under the control block (hp.step: the base t of
+    the bias-correction table)."""
+    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+    n = master.numel()
+    for name, t in (("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq), ("param_fp16", param_fp16),
+                    *[(f"grad_chunks[{i}]", c) for i, c in enumerate(grad_chunks)]):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    _check(lib.zero_shard_step_ctl(
+        _ptr_array(ptrs), len(ptrs), n, _dev(master, torch.float32, "master"),
+        _dev(exp_avg, torch.float32, "exp_avg"), _dev(exp_avg_sq, torch.float32, "exp_avg_sq"),
+        _dev(param_fp16, torch.float16, "param_fp16"), ctypes.byref(hp), _ctl(ctl),
+        _stream(stream)))
+
+
+def zero_shard_step_out_ctl(grad_chunks: Sequence[torch.Tensor], copies, hp: AdamWParams,
+                            ctl: torch.Tensor, stream=None) -> None:
+    """The single-pass update under the control block: from copy ctl.cur into
+    the other.  copies: two (master, exp_avg, exp_avg_sq, param_fp16) tuples."""
+    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+    n = copies[0][0].numel()
+    for k, cp in enumerate(copies):
+        for j, t in enumerate(cp):
+            if t.numel() != n:
+                raise ValueError(f"copy {k} array {j} has {t.numel()} elements, expected {n}")
+    for i, c in enumerate(grad_chunks):
+        if c.numel() != n:
+            raise ValueError(f"grad_chunks[{i}] has {c.numel()} elements, expected {n}")
+    dts = (torch.float32, torch.float32, torch.float32, torch.float16)
+    tables = [_ptr_array([_dev(copies[k][j], dts[j], f"copy {k} array {j}") for k in range(2)])
+              for j in range(4)]
+    _check(lib.zero_shard_step_out_ctl(_ptr_array(ptrs), len(ptrs), n, *tables, ctypes.byref(hp),
+                                       _ctl(ctl), _stream(stream)))
+
+
+class DeviceStepper:
+    """Enqueues whole steps under a control block with no read-back.  The
+    update's bias corrections come from a table based at t0 and covering
+    ZERO_CTL_STEPS values of t; since t grows by at most one per step, the
+    stepper reads the block back (once per ZERO_CTL_STEPS steps) only to move
+    the base to the current t."""
+
+    def __init__(self, ctl: torch.Tensor, hp: AdamWParams):
+        self.ctl = ctl
+        self.hp = AdamWParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step,
+                              hp.decoupled_wd, hp.bias_correction)
+        self.since_base = 0
+
+    def _rebase(self):
+        if self.since_base >= ZERO_CTL_STEPS:
+            self.hp.step = control_read(self.ctl).step
+            self.since_base = 0
+
+    def two_pass(self, grad_chunks, master, exp_avg, exp_avg_sq, param_fp16,
+                 max_grad_norm: float = 0.0, stream=None) -> None:
+        """Check, decide (skip, loss scale, clip factor, t), update in place."""
+        self._rebase()
+        zero_control_begin(self.ctl, stream=stream)
+        zero_overflow_check_ctl(grad_chunks, self.ctl, stream=stream)
+        zero_control_decide(self.ctl, max_grad_norm, False, stream=stream)
+        zero_shard_step_ctl(grad_chunks, master, exp_avg, exp_avg_sq, param_fp16, self.hp,
+                            self.ctl, stream=stream)
+        self.since_base += 1
+
+    def single_pass(self, grad_chunks, copies, stream=None) -> None:
+        """Fused update from copy cur into the other, then decide and commit."""
+        self._rebase()
+        zero_control_begin(self.ctl, stream=stream)
+        zero_shard_step_out_ctl(grad_chunks, copies, self.hp, self.ctl, stream=stream)
+        zero_control_decide(self.ctl, 0.0, True, stream=stream)
+        self.since_base += 1

@@ -14,6 +14,8 @@
 
 namespace {
 
+float bias_correction(float beta, int64_t t);
+
 thread_local char g_error[512] = "";
 
 int fail(int code, const char* fmt, ...) {
@@ -99,10 +101,9 @@ int adam_scalars(const zero_adamw_params* hp, zero::AdamScalars* as) {
     as->c1 = 1.0f - hp->beta1;
     as->c2 = 1.0f - hp->beta2;
     if (hp->bias_correction) {
-        const double t = static_cast<double>(hp->step);
-        as->bc1 = static_cast<float>(1.0 - pow(static_cast<double>(hp->beta1), t));
         // beta <= 1 - 2^-24 keeps 1 - beta^t >= 2^-24 > 0 for every t >= 1
-        as->bc2 = static_cast<float>(1.0 - pow(static_cast<double>(hp->beta2), t));
+        as->bc1 = bias_correction(hp->beta1, hp->step);
+        as->bc2 = bias_correction(hp->beta2, hp->step);
     } else {
         as->bc1 = 1.0f;
         as->bc2 = 1.0f;
@@ -160,6 +161,41 @@ int check_outputs_clear_of(int64_t n, const float* master_out, const float* exp_
         if (overlap(out[a], out_bytes[a], p, bytes))
             return fail(ZERO_EINVAL, "%s: %s overlaps grad_chunks[%d]", who, out_names[a], c);
     return ZERO_OK;
+}
+
+// A loss scaler whose fields the state machine accepts.
+int check_scaler(const zero_loss_scaler* s) {
+    if (!finite_f(s->scale) || !(s->scale > 0.0f)) return fail(ZERO_EINVAL, "scale not finite and > 0");
+    if (!finite_f(s->growth_factor) || !(s->growth_factor >= 1.0f))
+        return fail(ZERO_EINVAL, "growth_factor < 1");
+    if (!(s->backoff_factor > 0.0f && s->backoff_factor <= 1.0f))
+        return fail(ZERO_EINVAL, "backoff_factor outside (0, 1]");
+    if (!finite_f(s->min_scale) || !(s->min_scale > 0.0f)) return fail(ZERO_EINVAL, "min_scale <= 0");
+    if (!finite_f(s->max_scale) || !(s->max_scale >= s->min_scale))
+        return fail(ZERO_EINVAL, "max_scale < min_scale");
+    if (s->growth_interval < 1) return fail(ZERO_EINVAL, "growth_interval < 1");
+    if (s->good_steps < 0) return fail(ZERO_EINVAL, "good_steps < 0");
+    return ZERO_OK;
+}
+
+// 1 - beta^t, evaluated in fp64 from the fp32 beta and rounded to fp32.
+float bias_correction(float beta, int64_t t) {
+    return static_cast<float>(1.0 - pow(static_cast<double>(beta), static_cast<double>(t)));
+}
+
+int check_ctl_ptr(const zero_step_control* d_ctl, const char* who) {
+    if (!d_ctl) return fail(ZERO_EINVAL, "%s: d_ctl is NULL", who);
+    if (!aligned(d_ctl, 8)) return fail(ZERO_EALIGN, "%s: d_ctl is not 8-byte aligned", who);
+    return ZERO_OK;
+}
+
+// The table of bias corrections for t = hp->step .. + ZERO_CTL_STEPS - 1.
+void bias_table(const zero_adamw_params* hp, zero::BiasTable* tab) {
+    tab->t0 = hp->step;
+    for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
+        tab->bc1[k] = hp->bias_correction ? bias_correction(hp->beta1, hp->step + k) : 1.0f;
+        tab->bc2[k] = hp->bias_correction ? bias_correction(hp->beta2, hp->step + k) : 1.0f;
+    }
 }
 
 // Validation and launch shared by the in-place and the out-of-place step.
@@ -398,6 +434,140 @@ int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n
     return e == hipSuccess ? ok() : hip_fail(e, who);
 }
 
+int zero_control_init(zero_step_control* ctl, const zero_loss_scaler* scaler, int64_t step) {
+    if (!ctl || !scaler) return fail(ZERO_EINVAL, "zero_control_init: ctl or scaler is NULL");
+    int rc = check_scaler(scaler);
+    if (rc) return rc;
+    if (step < 1) return fail(ZERO_EINVAL, "zero_control_init: step < 1");
+    memset(ctl, 0, sizeof *ctl);
+    ctl->scale = scaler->scale;
+    ctl->growth_factor = scaler->growth_factor;
+    ctl->backoff_factor = scaler->backoff_factor;
+    ctl->min_scale = scaler->min_scale;
+    ctl->max_scale = scaler->max_scale;
+    ctl->growth_interval = scaler->growth_interval;
+    ctl->good_steps = scaler->good_steps;
+    ctl->skipped_steps = scaler->skipped_steps;
+    ctl->step = step;
+    ctl->step_used = step;
+    ctl->scale_used = scaler->scale;
+    ctl->clip_coef = 1.0f;
+    return ok();
+}
+
+int zero_control_begin(zero_step_control* d_ctl, void* stream) {
+    int rc = check_ctl_ptr(d_ctl, "zero_control_begin");
+    if (rc) return rc;
+    const hipError_t e = zero::launch_control_begin(d_ctl, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "zero_control_begin");
+}
+
+int zero_control_decide(zero_step_control* d_ctl, float max_grad_norm, int32_t flip_copy,
+                        void* stream) {
+    int rc = check_ctl_ptr(d_ctl, "zero_control_decide");
+    if (rc) return rc;
+    if (!finite_f(max_grad_norm))
+        return fail(ZERO_EINVAL, "zero_control_decide: max_grad_norm is not finite");
+    const hipError_t e = zero::launch_control_decide(d_ctl, max_grad_norm, flip_copy ? 1 : 0,
+                                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "zero_control_decide");
+}
+
+int zero_overflow_check_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                            zero_step_control* d_ctl, void* stream) {
+    static const char* who = "zero_overflow_check_ctl";
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    int rc = check_chunks(grad_chunks, n_chunks, n, 1.0f, &table, &gs);  // S is on the device
+    if (rc) return rc;
+    if ((rc = check_ctl_ptr(d_ctl, who))) return rc;
+    if (n == 0) return ok();
+    const hipError_t e = zero::launch_overflow_check_ctl(table, n_chunks, n, gs, d_ctl,
+                                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
+int zero_shard_step_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                        float* master, float* exp_avg, float* exp_avg_sq, void* param_fp16,
+                        const zero_adamw_params* hp, zero_step_control* d_ctl, void* stream) {
+    static const char* who = "zero_shard_step_ctl";
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    zero::AdamScalars as;
+    int rc = check_chunks(grad_chunks, n_chunks, n, 1.0f, &table, &gs);
+    if (rc) return rc;
+    if ((rc = adam_scalars(hp, &as))) return rc;
+    if ((rc = check_ctl_ptr(d_ctl, who))) return rc;
+    if (n == 0) return ok();
+    if ((rc = check_state(n, master, exp_avg, exp_avg_sq, master, exp_avg, exp_avg_sq, param_fp16,
+                          who)))
+        return rc;
+    for (int32_t c = 0; c < n_chunks; ++c)
+        if ((rc = check_outputs_clear_of(n, master, exp_avg, exp_avg_sq, param_fp16,
+                                         grad_chunks[c], 2 * n, who, c)))
+            return rc;
+    zero::BiasTable tab;
+    bias_table(hp, &tab);
+    zero::ShardCopies sc;
+    for (int k = 0; k < 2; ++k) {
+        sc.master[k] = master;
+        sc.exp_avg[k] = exp_avg;
+        sc.exp_avg_sq[k] = exp_avg_sq;
+        sc.param_fp16[k] = static_cast<uint16_t*>(param_fp16);
+    }
+    const hipError_t e = zero::launch_ctl_step(table, n_chunks, n, gs, as, tab, sc, false, d_ctl,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
+int zero_shard_step_out_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                            float* const* masters, float* const* exp_avgs,
+                            float* const* exp_avg_sqs, void* const* params_fp16,
+                            const zero_adamw_params* hp, zero_step_control* d_ctl,
+                            void* stream) {
+    static const char* who = "zero_shard_step_out_ctl";
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    zero::AdamScalars as;
+    int rc = check_chunks(grad_chunks, n_chunks, n, 1.0f, &table, &gs);
+    if (rc) return rc;
+    if ((rc = adam_scalars(hp, &as))) return rc;
+    if ((rc = check_ctl_ptr(d_ctl, who))) return rc;
+    if (!masters || !exp_avgs || !exp_avg_sqs || !params_fp16)
+        return fail(ZERO_EINVAL, "%s: a copy table is NULL", who);
+    if (n == 0) return ok();
+    // either copy may be read and the other written: the eight arrays are all
+    // distinct, disjoint and clear of the chunks
+    const void* arr[8] = {masters[0], exp_avgs[0], exp_avg_sqs[0], params_fp16[0],
+                          masters[1], exp_avgs[1], exp_avg_sqs[1], params_fp16[1]};
+    const int64_t bytes[8] = {4 * n, 4 * n, 4 * n, 2 * n, 4 * n, 4 * n, 4 * n, 2 * n};
+    for (int a = 0; a < 8; ++a) {
+        if (!arr[a]) return fail(ZERO_EINVAL, "%s: state array %d of 8 is NULL", who, a);
+        if (!aligned(arr[a], 16))
+            return fail(ZERO_EALIGN, "%s: state array %d of 8 is not 16-byte aligned", who, a);
+    }
+    for (int a = 0; a < 8; ++a) {
+        for (int b = a + 1; b < 8; ++b)
+            if (overlap(arr[a], bytes[a], arr[b], bytes[b]))
+                return fail(ZERO_EINVAL, "%s: state arrays %d and %d overlap", who, a, b);
+        for (int32_t c = 0; c < n_chunks; ++c)
+            if (overlap(arr[a], bytes[a], grad_chunks[c], 2 * n))
+                return fail(ZERO_EINVAL, "%s: state array %d overlaps grad_chunks[%d]", who, a, c);
+    }
+    zero::BiasTable tab;
+    bias_table(hp, &tab);
+    zero::ShardCopies sc;
+    for (int k = 0; k < 2; ++k) {
+        sc.master[k] = masters[k];
+        sc.exp_avg[k] = exp_avgs[k];
+        sc.exp_avg_sq[k] = exp_avg_sqs[k];
+        sc.param_fp16[k] = static_cast<uint16_t*>(params_fp16[k]);
+    }
+    const hipError_t e = zero::launch_ctl_step(table, n_chunks, n, gs, as, tab, sc, true, d_ctl,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
 int zero_bucket_flatten(const void* const* tensors, const int64_t* numels, int32_t n_tensors,
                         int64_t align, int64_t pad_multiple, void* bucket, int64_t bucket_capacity,
                         int64_t* offsets_out, void* stream) {
@@ -463,16 +633,8 @@ int zero_bucket_flatten(const void* const* tensors, const int64_t* numels, int32
 
 int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_out) {
     if (!s || !skip_out) return fail(ZERO_EINVAL, "scaler or skip_out is NULL");
-    if (!finite_f(s->scale) || !(s->scale > 0.0f)) return fail(ZERO_EINVAL, "scale not finite and > 0");
-    if (!finite_f(s->growth_factor) || !(s->growth_factor >= 1.0f))
-        return fail(ZERO_EINVAL, "growth_factor < 1");
-    if (!(s->backoff_factor > 0.0f && s->backoff_factor <= 1.0f))
-        return fail(ZERO_EINVAL, "backoff_factor outside (0, 1]");
-    if (!finite_f(s->min_scale) || !(s->min_scale > 0.0f)) return fail(ZERO_EINVAL, "min_scale <= 0");
-    if (!finite_f(s->max_scale) || !(s->max_scale >= s->min_scale))
-        return fail(ZERO_EINVAL, "max_scale < min_scale");
-    if (s->growth_interval < 1) return fail(ZERO_EINVAL, "growth_interval < 1");
-    if (s->good_steps < 0) return fail(ZERO_EINVAL, "good_steps < 0");
+    int rc = check_scaler(s);
+    if (rc) return rc;
     if (overflow) {
         const float backed = s->scale * s->backoff_factor;
         s->scale = backed > s->min_scale ? backed : s->min_scale;

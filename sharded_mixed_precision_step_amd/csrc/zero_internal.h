@@ -76,6 +76,23 @@ struct BucketTable {
     int32_t pad_;
 };
 
+// Bias corrections 1 - beta^t for t = t0 .. t0 + ZERO_CTL_STEPS - 1 (fp64,
+// rounded to fp32, as the host computes them), for updates whose t lives in
+// a device control block.
+struct BiasTable {
+    int64_t t0;
+    float bc1[ZERO_CTL_STEPS];
+    float bc2[ZERO_CTL_STEPS];
+};
+
+// Two copies of a shard's state; a control block's `cur` picks the one read.
+struct ShardCopies {
+    float* master[2];
+    float* exp_avg[2];
+    float* exp_avg_sq[2];
+    uint16_t* param_fp16[2];
+};
+
 struct FlattenDesc {
     const uint16_t* src;  // fp16 bits, 2-byte aligned
     int64_t numel;        // elements of the tensor
@@ -103,6 +120,17 @@ hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScal
                               double* d_sqnorm, hipStream_t stream);
 
 int64_t step_tiles(int64_t n);  // blocks of the fused step over n params
+
+hipError_t launch_ctl_step(const ChunkTable& chunks, int n_chunks, int64_t n,
+                           const GradScalars& gs, const AdamScalars& as, const BiasTable& tab,
+                           const ShardCopies& sc, bool single_pass, zero_step_control* ctl,
+                           hipStream_t stream);
+hipError_t launch_overflow_check_ctl(const ChunkTable& chunks, int n_chunks, int64_t n,
+                                     const GradScalars& gs, zero_step_control* ctl,
+                                     hipStream_t stream);
+hipError_t launch_control_begin(zero_step_control* ctl, hipStream_t stream);
+hipError_t launch_control_decide(zero_step_control* ctl, float max_norm, int flip,
+                                 hipStream_t stream);
 
 hipError_t launch_reduce_mean(const ChunkTable& chunks, int n_chunks, int64_t n,
                               const GradScalars& gs, uint16_t* mean16, int32_t* d_overflow,

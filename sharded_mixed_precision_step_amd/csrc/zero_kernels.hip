@@ -143,11 +143,13 @@ __device__ __forceinline__ f8 replica_sum8(const uint16_t* const* chunks, int n_
 // and each element is read (from the *_in arrays) before it is written (to
 // the *_out arrays), so in-place (in == out) and out-of-place both hold.
 // FULL: every pack of the tile exists (all tiles but possibly the last).
-template <int NC, bool REDUCE, bool FULL>
+// CLIP: g is multiplied by `clip` (one fp32 multiply) after the flag and the
+// squared norm have seen it and before the moments.
+template <int NC, bool REDUCE, bool FULL, bool CLIP = false>
 __device__ __forceinline__ void step_tile(const uint16_t* const* chunks, int n_chunks, int64_t packs,
                                           int64_t first, const GradScalars& gs,
                                           const AdamScalars& as, const ShardState& st, bool& bad,
-                                          double& sq) {
+                                          double& sq, float clip = 1.0f) {
     f8 s[kWaveSpan];
     f4 p[kWaveSpan][2], m[kWaveSpan][2], v[kWaveSpan][2];
 #pragma unroll
@@ -179,11 +181,12 @@ __device__ __forceinline__ void step_tile(const uint16_t* const* chunks, int n_c
         u16x8 out;
 #pragma unroll
         for (int e = 0; e < kPack; ++e) {
-            const float g = unscaled_mean(s[u][e], gs);
+            float g = unscaled_mean(s[u][e], gs);
             if constexpr (REDUCE) {
                 bad |= nonfinite(g);
                 sq += static_cast<double>(g) * static_cast<double>(g);
             }
+            if constexpr (CLIP) g = g * clip;
             adam_update(g, pe[e], me[e], ve[e], as);
             out[e] = to_fp16_bits(pe[e]);
         }
@@ -204,28 +207,31 @@ __device__ __forceinline__ void step_tile(const uint16_t* const* chunks, int n_c
 // slice) of n params whose chunks and state start at the given pointers.
 // `last`: this is the shard's last tile, so it also updates the n % 8 params
 // after the last full pack, one per thread.
-template <int NC, bool REDUCE>
+template <int NC, bool REDUCE, bool CLIP = false>
 __device__ __forceinline__ void step_block(const uint16_t* const* chunks, int n_chunks, int64_t n,
                                            int64_t tile, bool last, const GradScalars& gs,
                                            const AdamScalars& as, const ShardState& st,
-                                           bool& bad, double& sq) {
+                                           bool& bad, double& sq, float clip = 1.0f) {
     const int64_t packs = n / kPack;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t tile0 = tile * kTilePacks;
     const int64_t first = tile0 + wave * (kWaveSpan * 64) + lane;
     if (tile0 + kTilePacks <= packs)
-        step_tile<NC, REDUCE, true>(chunks, n_chunks, packs, first, gs, as, st, bad, sq);
+        step_tile<NC, REDUCE, true, CLIP>(chunks, n_chunks, packs, first, gs, as, st, bad, sq,
+                                          clip);
     else
-        step_tile<NC, REDUCE, false>(chunks, n_chunks, packs, first, gs, as, st, bad, sq);
+        step_tile<NC, REDUCE, false, CLIP>(chunks, n_chunks, packs, first, gs, as, st, bad, sq,
+                                           clip);
     if (last) {
         const int64_t j = packs * kPack + threadIdx.x;
         if (j < n) {
-            const float g = unscaled_mean(replica_sum1<NC>(chunks, n_chunks, j), gs);
+            float g = unscaled_mean(replica_sum1<NC>(chunks, n_chunks, j), gs);
             if constexpr (REDUCE) {
                 bad |= nonfinite(g);
                 sq += static_cast<double>(g) * static_cast<double>(g);
             }
+            if constexpr (CLIP) g = g * clip;
             float p = st.master_in[j], m = st.exp_avg_in[j], v = st.exp_avg_sq_in[j];
             adam_update(g, p, m, v, as);
             st.master_out[j] = p;
@@ -280,10 +286,30 @@ __device__ __forceinline__ f8 load_widen8_nt(const uint16_t* base, int64_t pack)
 
 // The check reads only the chunks, once: a grid-stride loop over a grid of
 // kCheckBlocksPerCU blocks per CU, with non-temporal (streaming) loads.
-template <int NC>
+// The loss-scale scalars of S read from a control block: multiply by 1/S
+// exactly when the host would (S a power of two whose inverse is finite).
+__device__ __forceinline__ GradScalars with_scale(GradScalars gs, float S) {
+    gs.s = S;
+    gs.inv_s = 1.0f / S;
+    const uint32_t b = __float_as_uint(S);
+    const uint32_t mant = b & 0x007fffffu, ex = (b >> 23) & 0xffu;
+    const bool pow2 = S > 0.0f && ((ex != 0 && ex != 0xffu && mant == 0) ||
+                                   (ex == 0 && __popc(mant) == 1));
+    gs.unscale_by_mul = (pow2 && !nonfinite(gs.inv_s)) ? 1 : 0;
+    return gs;
+}
+
+// CTL: S is the control block's scale_used, and the flag and squared norm go
+// to its overflow and sqnorm fields.
+template <int NC, bool CTL = false>
 __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs,
-    int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
+    int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm, zero_step_control* ctl) {
+    if constexpr (CTL) {
+        gs = with_scale(gs, ctl->scale_used);
+        d_overflow = &ctl->overflow;
+        d_sqnorm = &ctl->sqnorm;
+    }
     const int64_t packs = n / kPack;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
     const int nc = NC > 0 ? NC : n_chunks;
@@ -310,6 +336,81 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
         }
     }
     publish(bad, sq, d_overflow, d_sqnorm);
+}
+
+// The update under a device control block.  SINGLE = false: the two-pass
+// update, in place on copy 0, skipped whole when ctl->skip is set, with g
+// clipped by ctl->clip_coef.  SINGLE = true: the single-pass update from copy
+// cur into copy 1 - cur, with the flag and squared norm into the block.  In
+// both, S = scale_used and the bias corrections are those of t = step_used,
+// looked up in the table the host computed.  Every block reads the same few
+// words of the block (no block writes them here).
+template <int NC, bool SINGLE>
+__global__ __launch_bounds__(kBlock) void ctl_step_kernel(ChunkTable chunks, int n_chunks,
+                                                          int64_t n, GradScalars gs,
+                                                          AdamScalars as, BiasTable tab,
+                                                          ShardCopies sc,
+                                                          zero_step_control* ctl) {
+    if constexpr (!SINGLE) {
+        if (ctl->skip) return;
+    }
+    const int64_t k = ctl->step_used - tab.t0;
+    if (k < 0 || k >= ZERO_CTL_STEPS) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&ctl->error, 1);
+        return;
+    }
+    as.bc1 = tab.bc1[k];
+    as.bc2 = tab.bc2[k];
+    gs = with_scale(gs, ctl->scale_used);
+    const int in = SINGLE ? (ctl->cur & 1) : 0;
+    const int out = SINGLE ? 1 - in : 0;
+    const ShardState st = {sc.master[in],  sc.exp_avg[in],  sc.exp_avg_sq[in],
+                           sc.master[out], sc.exp_avg[out], sc.exp_avg_sq[out],
+                           sc.param_fp16[out]};
+    bool bad = false;
+    double sq = 0.0;
+    step_block<NC, SINGLE, !SINGLE>(chunks.p, n_chunks, n, blockIdx.x, blockIdx.x == gridDim.x - 1,
+                                    gs, as, st, bad, sq, SINGLE ? 1.0f : ctl->clip_coef);
+    if constexpr (SINGLE) publish(bad, sq, &ctl->overflow, &ctl->sqnorm);
+}
+
+// One thread: start a step.
+__global__ void control_begin_kernel(zero_step_control* c) {
+    c->overflow = 0;
+    c->sqnorm = 0.0;
+    c->skip = 0;
+    c->clip_coef = 1.0f;
+    c->scale_used = c->scale;
+    c->step_used = c->step;
+}
+
+// One thread: the decision, the loss-scale move (the rules of the host's
+// zero_update_loss_scale, in fp32), the clip factor, t and the copy.
+__global__ void control_decide_kernel(zero_step_control* c, float max_norm, int flip) {
+    const bool skip = c->overflow != 0;
+    c->skip = skip ? 1 : 0;
+    if (skip) {
+        const float backed = c->scale * c->backoff_factor;
+        c->scale = backed > c->min_scale ? backed : c->min_scale;
+        c->good_steps = 0;
+        c->skipped_steps += 1;
+        c->clip_coef = 1.0f;
+        return;
+    }
+    c->good_steps += 1;
+    if (c->good_steps >= c->growth_interval) {
+        const float grown = c->scale * c->growth_factor;
+        c->scale = grown < c->max_scale ? grown : c->max_scale;
+        c->good_steps = 0;
+    }
+    if (max_norm > 0.0f) {
+        const double coef = static_cast<double>(max_norm) / (__builtin_sqrt(c->sqnorm) + 1e-6);
+        c->clip_coef = static_cast<float>(coef < 1.0 ? coef : 1.0);
+    } else {
+        c->clip_coef = 1.0f;
+    }
+    c->step += 1;
+    if (flip) c->cur = 1 - (c->cur & 1);
 }
 
 // The owner's gradient mean stored as fp16 (the page-literal split): mean16 =
@@ -550,12 +651,32 @@ hipError_t mean_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const Gr
     return hipGetLastError();
 }
 
+template <int NC, bool SINGLE>
+hipError_t ctl_step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
+                         const AdamScalars& as, const BiasTable& tab, const ShardCopies& sc,
+                         zero_step_control* ctl, hipStream_t stream) {
+    const int64_t grid = step_grid(n);
+    hipLaunchKernelGGL((ctl_step_kernel<NC, SINGLE>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, as, tab, sc, ctl);
+    return hipGetLastError();
+}
+
+template <int NC>
+hipError_t check_ctl_impl(const ChunkTable& chunks, int n_chunks, int64_t n,
+                          const GradScalars& gs, zero_step_control* ctl, hipStream_t stream) {
+    const int64_t grid = check_grid(n);
+    hipLaunchKernelGGL((overflow_check_kernel<NC, true>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, nullptr, nullptr, ctl);
+    return hipGetLastError();
+}
+
 template <int NC>
 hipError_t check_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
                       int32_t* d_overflow, double* d_sqnorm, hipStream_t stream) {
     const int64_t grid = check_grid(n);
-    hipLaunchKernelGGL(overflow_check_kernel<NC>, dim3(static_cast<unsigned>(grid)), dim3(kBlock),
-                       0, stream, chunks, n_chunks, n, gs, d_overflow, d_sqnorm);
+    hipLaunchKernelGGL((overflow_check_kernel<NC, false>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, d_overflow, d_sqnorm,
+                       nullptr);
     return hipGetLastError();
 }
 
@@ -658,6 +779,51 @@ hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const G
                                mean16);
             break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_ctl_step(const ChunkTable& chunks, int n_chunks, int64_t n,
+                           const GradScalars& gs, const AdamScalars& as, const BiasTable& tab,
+                           const ShardCopies& sc, bool single_pass, zero_step_control* ctl,
+                           hipStream_t stream) {
+#define ZERO_CASE(K)                                                                           \
+    case K:                                                                                    \
+        return single_pass                                                                     \
+                   ? ctl_step_impl<K, true>(chunks, n_chunks, n, gs, as, tab, sc, ctl, stream) \
+                   : ctl_step_impl<K, false>(chunks, n_chunks, n, gs, as, tab, sc, ctl, stream);
+    switch (n_chunks) {
+        ZERO_FOR_EACH_N(ZERO_CASE)
+        default:
+            return single_pass
+                       ? ctl_step_impl<0, true>(chunks, n_chunks, n, gs, as, tab, sc, ctl, stream)
+                       : ctl_step_impl<0, false>(chunks, n_chunks, n, gs, as, tab, sc, ctl,
+                                                 stream);
+    }
+#undef ZERO_CASE
+}
+
+hipError_t launch_overflow_check_ctl(const ChunkTable& chunks, int n_chunks, int64_t n,
+                                     const GradScalars& gs, zero_step_control* ctl,
+                                     hipStream_t stream) {
+#define ZERO_CASE(K) \
+    case K:          \
+        return check_ctl_impl<K>(chunks, n_chunks, n, gs, ctl, stream);
+    switch (n_chunks) {
+        ZERO_FOR_EACH_N(ZERO_CASE)
+        default:
+            return check_ctl_impl<0>(chunks, n_chunks, n, gs, ctl, stream);
+    }
+#undef ZERO_CASE
+}
+
+hipError_t launch_control_begin(zero_step_control* ctl, hipStream_t stream) {
+    hipLaunchKernelGGL(control_begin_kernel, dim3(1), dim3(1), 0, stream, ctl);
+    return hipGetLastError();
+}
+
+hipError_t launch_control_decide(zero_step_control* ctl, float max_norm, int flip,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(control_decide_kernel, dim3(1), dim3(1), 0, stream, ctl, max_norm, flip);
     return hipGetLastError();
 }
 

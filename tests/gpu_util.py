@@ -60,9 +60,9 @@ def ulp16(a, b) -> np.ndarray:
     return np.abs(ordered16(a) - ordered16(b))
 
 
-def assert_fp32_close(name: str, got: np.ndarray, want: np.ndarray) -> int:
-    """1e-6 relative or 1e-9 absolute per element, and at most MAX_ULP fp32
-    ulps; returns the largest ulp distance."""
+def assert_fp32_close(name: str, got: np.ndarray, want: np.ndarray, max_ulp=MAX_ULP) -> int:
+    """1e-6 relative or 1e-9 absolute per element, and (unless max_ulp is
+    None) at most max_ulp fp32 ulps; returns the largest ulp distance."""
     got = np.asarray(got, np.float32)
     want = np.asarray(want, np.float32)
     assert got.shape == want.shape, name
@@ -74,7 +74,8 @@ def assert_fp32_close(name: str, got: np.ndarray, want: np.ndarray) -> int:
     assert not bad.any(), (f"{name}: {int(bad.sum())} of {bad.size} outside 1e-6 rel / 1e-9 abs; "
                            f"first at {np.flatnonzero(bad)[:5]}")
     u = int(ulp32(got[fin], want[fin]).max()) if fin.any() else 0
-    assert u <= MAX_ULP, f"{name}: {u} ulp"
+    if max_ulp is not None:
+        assert u <= max_ulp, f"{name}: {u} ulp"
     return u
 
 
@@ -84,10 +85,10 @@ def assert_fp16_close(name: str, got: np.ndarray, want: np.ndarray) -> int:
     return u
 
 
-def assert_matches_oracle(d: dict, want, label: str = "") -> dict:
+def assert_matches_oracle(d: dict, want, label: str = "", max_ulp=MAX_ULP) -> dict:
     """Compare the device state after a step with an oracle StepResult."""
     ulps = {}
     for k, ref in (("master", want.master), ("m", want.m), ("v", want.v)):
-        ulps[k] = assert_fp32_close(f"{label}{k}", d[k].cpu().numpy(), ref)
+        ulps[k] = assert_fp32_close(f"{label}{k}", d[k].cpu().numpy(), ref, max_ulp)
     ulps["p16"] = assert_fp16_close(f"{label}p16", d["p16"].cpu().numpy(), want.p16)
     return ulps

@@ -238,6 +238,43 @@ def test_reduce_mean_and_accumulate_reject_bad_arguments():
     assert acc(None, 0, 0, 1, None, None) == zs.ZERO_OK                 # n == 0: no-op
 
 
+def test_control_init_and_ctl_calls_reject_bad_arguments():
+    ctl = zs.StepControl()
+    good = zs.LossScaler.create(scale=65536.0, growth_interval=3)
+    assert zs.lib.zero_control_init(ctypes.byref(ctl), ctypes.byref(good), 7) == zs.ZERO_OK
+    assert (ctl.scale, ctl.step, ctl.step_used, ctl.growth_interval, ctl.cur) == \
+        (65536.0, 7, 7, 3, 0)
+    assert ctl.clip_coef == 1.0 and ctl.overflow == 0 and ctl.error == 0
+    assert zs.lib.zero_control_init(ctypes.byref(ctl), ctypes.byref(good), 0) == zs.ZERO_EINVAL
+    bad = zs.LossScaler.create(scale=float("inf"))
+    assert zs.lib.zero_control_init(ctypes.byref(ctl), ctypes.byref(bad), 1) == zs.ZERO_EINVAL
+    assert zs.lib.zero_control_init(None, ctypes.byref(good), 1) == zs.ZERO_EINVAL
+    # device-side calls: bad pointers are refused before any launch
+    assert zs.lib.zero_control_begin(None, None) == zs.ZERO_EINVAL
+    assert zs.lib.zero_control_begin(A + 4, None) == zs.ZERO_EALIGN
+    assert zs.lib.zero_control_decide(A, float("nan"), 0, None) == zs.ZERO_EINVAL
+    assert zs.lib.zero_control_decide(None, 1.0, 0, None) == zs.ZERO_EINVAL
+    assert zs.lib.zero_overflow_check_ctl(_ptrs(A), 1, 10, None, None) == zs.ZERO_EINVAL
+    assert zs.lib.zero_overflow_check_ctl(_ptrs(A + 2), 1, 10, A, None) == zs.ZERO_EALIGN
+    B = A + (1 << 20)
+    n = 1000
+    st = (B, B + 4 * n, B + 8 * n, B + 12 * n)
+    step_ctl = lambda ch, s4, hp, c: zs.lib.zero_shard_step_ctl(
+        ch, 1, n, *s4, ctypes.byref(hp) if hp is not None else None, c, None)
+    assert step_ctl(_ptrs(A), st, _hp(), None) == zs.ZERO_EINVAL
+    assert step_ctl(_ptrs(A), st, _hp(step=0), A) == zs.ZERO_EINVAL
+    assert step_ctl(_ptrs(A), (st[0], st[0] + 16) + st[2:], _hp(), A) == zs.ZERO_EINVAL
+    assert step_ctl(_ptrs(B + 64), st, _hp(), A) == zs.ZERO_EINVAL          # chunk on the state
+    C = B + (1 << 20)
+    other = (C, C + 4 * n, C + 8 * n, C + 12 * n)
+    out_ctl = lambda c0, c1: zs.lib.zero_shard_step_out_ctl(
+        _ptrs(A), 1, n, *[_ptrs(c0[j], c1[j]) for j in range(4)], ctypes.byref(_hp()), A, None)
+    assert out_ctl(st, st) == zs.ZERO_EINVAL                                # the same copy twice
+    assert out_ctl(st, (st[1],) + other[1:]) == zs.ZERO_EINVAL               # copies overlap
+    assert out_ctl(st, (other[0] + 4,) + other[1:]) == zs.ZERO_EALIGN
+    assert out_ctl(st, other[:3] + (A,)) == zs.ZERO_EINVAL                   # over the chunk
+
+
 def _flatten(ptrs, numels, align, pad, bucket, cap):
     nt = len(numels)
     offs = (ctypes.c_int64 * (nt + 1))()

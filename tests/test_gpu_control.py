@@ -1,0 +1,225 @@
+"""The device-resident step control against the CPU oracle: whole steps
+enqueued with no read-back (two-pass with and without gradient-norm
+clipping, and single pass with the commit on the device) walk the same
+states as the oracle's step, loss scaler and t over clean and overflowing
+steps; a stale bias-correction table is refused on the device; and a HIP
+graph of one step replays like the eager calls."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.loss_scale as ols
+import oracle.zero_step as ozs
+import sharded_mixed_precision_step_amd as zs
+import workloads as wl
+from gpu_util import assert_matches_oracle, device
+
+pytestmark = pytest.mark.gpu
+
+N, n = 8, 40_009
+PLAN = [False, True, False, False, True, False, False]      # overflow injected or not
+
+
+def _workload():
+    base = wl.LLAMA3_8B_SHARD
+    return wl.ShardWorkload(name="ctl", wid=base.wid, n=n, n_replicas=N, grad_sigma=1e-4,
+                            loss_scale=65536.0, hyper=base.hyper.replace(step=3),
+                            m_sigma=1e-4, v_sigma=1e-8)
+
+
+def _grads(w, k, S, plant):
+    g = [wl.host_fp16_grad(wl.seed_of(w.wid, 900 + k, wl.ARRAY_GRAD, i), n, w.grad_sigma, S)
+         for i in range(N)]
+    if plant:
+        g[k % N][(97 * k) % n] = np.float16(np.inf if k % 2 else np.nan)
+    return g
+
+
+def _scaler():
+    return (zs.LossScaler.create(scale=65536.0, growth_interval=2),
+            ols.ScalerState(scale=65536.0, growth_interval=2))
+
+
+def _check_control(c, os_, t, skip, want):
+    assert c.scale == np.float32(os_.scale) and c.good_steps == os_.good_steps
+    assert c.skipped_steps == os_.skipped_steps and c.step == t
+    assert c.skip == int(skip) and c.overflow == int(want.overflow) and c.error == 0
+    if not want.overflow:
+        assert abs(c.sqnorm - want.sqnorm) <= 1e-6 * want.sqnorm
+
+
+@pytest.mark.parametrize("clip", [0.0, 2e-3, 1e9])
+def test_two_pass_sequence_matches_oracle(clip):
+    """Check, decide, update in place, all on the device.  clip 0: none;
+    2e-3: the update's gradient is clipped (its norm is about 7e-3, the mean
+    of 8 replicas of N(0, 1e-4) over 40,009 params); 1e9: factor 1."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=901)
+    d = {k: torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16")}
+    scaler, os_ = _scaler()
+    ctl = zs.control_new(scaler, w.hyper.step, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+    state, t = (h["master"], h["m"], h["v"], h["p16"]), w.hyper.step
+    chunks = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(N)]
+    for k, plant in enumerate(PLAN):
+        S = os_.scale
+        g = _grads(w, k, S, plant)
+        for c, src in zip(chunks, g):
+            c.copy_(torch.from_numpy(src))
+        stepper.two_pass(chunks, d["master"], d["m"], d["v"], d["p16"], max_grad_norm=clip)
+        want = ozs.shard_step_clipped(g, *state, w.hyper.replace(step=t), S, clip)
+        skip = ols.update_loss_scale(os_, want.overflow)
+        t += 0 if skip else 1
+        c = zs.control_read(ctl)
+        print(f"case: ctl two-pass clip={clip} step {k} plant={plant} S={S}", flush=True)
+        _check_control(c, os_, t, skip, want)
+        if not skip:
+            coef = ozs.clip_coefficient(want.sqnorm, clip)
+            assert abs(c.clip_coef - coef) <= 1e-6 * coef
+        if clip == 2e-3 and not skip:
+            assert c.clip_coef < 0.5
+        if clip == 2e-3:
+            # The clip factor comes from the squared norm, summed in fp64 in
+            # atomic order on the device and in index order by the oracle; the
+            # factor can then differ by an fp32 ulp, and where the moment
+            # update cancels to near zero a tiny absolute difference is many
+            # ulps.  The bar here is the stated one: 1e-6 relative or 1e-9
+            # absolute, fp16 params within 1 ulp.
+            assert_matches_oracle(d, want, label=f"step {k} ", max_ulp=None)
+        else:
+            for name, ref in (("master", want.master), ("m", want.m), ("v", want.v)):
+                assert np.array_equal(d[name].cpu().numpy().view(np.uint32),
+                                      ref.view(np.uint32)), (k, name)
+            assert np.array_equal(d["p16"].cpu().numpy().view(np.uint16),
+                                  want.p16.view(np.uint16))
+        state = (want.master, want.m, want.v, want.p16)
+
+
+def test_single_pass_sequence_matches_oracle():
+    """Fused update into the other copy, then decide and commit on the device."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=902)
+    a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+    b = tuple(torch.full_like(x, float("nan")) for x in a)
+    copies = (a, b)
+    scaler, os_ = _scaler()
+    ctl = zs.control_new(scaler, w.hyper.step, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+    state, t, cur = (h["master"], h["m"], h["v"], h["p16"]), w.hyper.step, 0
+    chunks = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(N)]
+    for k, plant in enumerate(PLAN):
+        S = os_.scale
+        g = _grads(w, k, S, plant)
+        for c, src in zip(chunks, g):
+            c.copy_(torch.from_numpy(src))
+        before = [x.clone() for x in copies[cur]]
+        stepper.single_pass(chunks, copies)
+        want = ozs.shard_step(g, *state, w.hyper.replace(step=t), S)
+        skip = ols.update_loss_scale(os_, want.overflow)
+        t += 0 if skip else 1
+        c = zs.control_read(ctl)
+        print(f"case: ctl single-pass step {k} plant={plant} S={S}", flush=True)
+        _check_control(c, os_, t, skip, want)
+        if skip:
+            assert c.cur == cur
+            for x, y in zip(before, copies[cur]):
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+            continue
+        cur = 1 - cur
+        assert c.cur == cur
+        got = dict(zip(("master", "m", "v", "p16"), copies[cur]))
+        for name, ref in (("master", want.master), ("m", want.m), ("v", want.v)):
+            assert np.array_equal(got[name].cpu().numpy().view(np.uint32),
+                                  ref.view(np.uint32)), (k, name)
+        assert np.array_equal(got["p16"].cpu().numpy().view(np.uint16), want.p16.view(np.uint16))
+        state = (want.master, want.m, want.v, want.p16)
+
+
+def test_two_pass_without_clip_equals_host_driven_step():
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=903)
+    a = {k: torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16")}
+    b = {k: x.clone() for k, x in a.items()}
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    scaler, _ = _scaler()
+    ctl = zs.control_new(scaler, w.hyper.step, dev)
+    zs.DeviceStepper(ctl, zs.adamw_params(w.hyper)).two_pass(chunks, a["master"], a["m"],
+                                                             a["v"], a["p16"])
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    sq = torch.zeros(1, dtype=torch.float64, device=dev)
+    r = zs.checked_step(chunks, b["master"], b["m"], b["v"], b["p16"], zs.adamw_params(w.hyper),
+                        zs.LossScaler.create(scale=65536.0, growth_interval=2), fl, sq)
+    torch.cuda.synchronize()
+    assert not r.skipped
+    for k in a:
+        assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), k
+
+
+def test_stale_bias_table_is_refused_on_the_device():
+    """t = 100 against a table based at t0 = 1 (covering t = 1..64): bit 0 of
+    the error word is set and the state is left alone."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=904)
+    d = {k: torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16")}
+    snap = {k: x.clone() for k, x in d.items()}
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    scaler, _ = _scaler()
+    ctl = zs.control_new(scaler, 100, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper.replace(step=1)))
+    stepper.two_pass(chunks, d["master"], d["m"], d["v"], d["p16"])
+    c = zs.control_read(ctl)
+    assert c.error & 1 and c.skip == 0
+    for k in d:
+        assert torch.equal(d[k].view(torch.uint8), snap[k].view(torch.uint8)), k
+
+
+def test_graph_of_one_step_replays_like_eager_calls():
+    """One single-pass step (begin, fused update, decide and commit) captured
+    in a HIP graph and replayed five times, with eager work and device
+    synchronisations between replays: after every replay the state copies
+    and the control block equal those of the same steps run eagerly."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=905)
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+
+    def fresh():
+        a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+        b = tuple(torch.zeros_like(x) for x in a)
+        scaler, _ = _scaler()
+        ctl = zs.control_new(scaler, w.hyper.step, dev)
+        return (a, b), ctl, zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+
+    g_copies, g_ctl, g_stepper = fresh()
+    e_copies, e_ctl, e_stepper = fresh()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_stepper.single_pass(chunks, g_copies)
+    torch.cuda.synchronize()
+    # capture does not run the step: the block is untouched
+    assert zs.control_read(g_ctl).step == w.hyper.step
+    for r in range(5):
+        graph.replay()
+        torch.cuda.synchronize()
+        e_stepper.single_pass(chunks, e_copies)
+        junk = torch.randn(1 << 20, device=dev).sum()      # unrelated eager work
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        gc, ec = zs.control_read(g_ctl), zs.control_read(e_ctl)
+        print(f"case: graph replay {r}: t={gc.step} cur={gc.cur}", flush=True)
+        # every field equal, except the squared norm: its fp64 sum takes one
+        # atomic add per block, in whatever order the blocks finish
+        for name, _ in zs.StepControl._fields_:
+            if name == "sqnorm":
+                assert abs(gc.sqnorm - ec.sqnorm) <= 1e-12 * ec.sqnorm
+            else:
+                assert getattr(gc, name) == getattr(ec, name), name
+        assert gc.step == w.hyper.step + r + 1
+        for cp_g, cp_e in zip(g_copies, e_copies):
+            for x, y in zip(cp_g, cp_e):
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
