@@ -541,3 +541,27 @@ class DeviceStepper:
         zero_shard_step_out_ctl(grad_chunks, copies, self.hp, self.ctl, stream=stream)
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
+
+
+# ---------------------------------------------------------------------------
+# Checkpoint and resume: the shard's state is its four arrays plus the step
+# control block (loss scale, t, current copy); nothing else carries over.
+# ---------------------------------------------------------------------------
+
+def save_shard_state(path: str, master: torch.Tensor, exp_avg: torch.Tensor,
+                     exp_avg_sq: torch.Tensor, param_fp16: torch.Tensor,
+                     ctl: Optional[torch.Tensor] = None) -> None:
+    """Write the shard's state (and control block, if any) as raw tensors to
+    a safetensors file."""
+    from safetensors.torch import save_file
+    tensors = {"master": master, "exp_avg": exp_avg, "exp_avg_sq": exp_avg_sq,
+               "param_fp16": param_fp16}
+    if ctl is not None:
+        tensors["control"] = ctl
+    save_file({k: v.detach().contiguous().cpu() for k, v in tensors.items()}, path)
+
+
+def load_shard_state(path: str, device) -> dict:
+    """The tensors save_shard_state wrote, on `device`, bit for bit."""
+    from safetensors.torch import load_file
+    return {k: v.to(device) for k, v in load_file(path).items()}
