@@ -1,0 +1,331 @@
+// Host-only harness of the C-ABI layer, built with g++ and AddressSanitizer
+// plus UndefinedBehaviorSanitizer (tests/test_host_sanitizers.py).  The
+// device side is replaced by stubs that record what each launch would
+// receive, so the validation paths and the launch tables (bucket batching,
+// flatten batching, bias tables, accumulate modes) run under the sanitizers
+// with no GPU.  Device pointers are fake addresses: any dereference by the
+// host layer would fault here.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <utility>
+#include <vector>
+
+#include "zero_internal.h"
+#include "zero_step.h"
+
+namespace {
+
+struct BucketLaunch {
+    int n_chunks;
+    std::vector<int64_t> tile_start, n, offset;
+    std::vector<const void*> chunk;
+};
+struct FlattenLaunch {
+    int count;
+    int64_t max_slot;
+    std::vector<zero::FlattenDesc> d;
+};
+
+std::vector<BucketLaunch> g_bucket;
+std::vector<FlattenLaunch> g_flatten;
+std::vector<zero::BiasTable> g_bias;
+std::vector<int> g_accumulate_mode;
+int g_other_launches = 0;
+
+void reset() {
+    g_bucket.clear();
+    g_flatten.clear();
+    g_bias.clear();
+    g_accumulate_mode.clear();
+    g_other_launches = 0;
+}
+
+#define EXPECT(c)                                                                \
+    do {                                                                         \
+        if (!(c)) {                                                              \
+            fprintf(stderr, "FAIL %s:%d: %s (%s)\n", __FILE__, __LINE__, #c,     \
+                    zero_last_error_string());                                   \
+            exit(1);                                                             \
+        }                                                                        \
+    } while (0)
+
+void* fake(uint64_t a) { return reinterpret_cast<void*>(a); }
+
+const uint64_t kBase = 0x7f0000000000ull;
+
+}  // namespace
+
+// ---- stubs of the device side ----------------------------------------------
+namespace zero {
+
+int64_t step_tiles(int64_t n) {
+    const int64_t t = (n / kPack + kTilePacks - 1) / kTilePacks;
+    return t < 1 ? 1 : t;
+}
+
+hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScalars&,
+                              const AdamScalars&, const ShardState&, int32_t*, double*,
+                              hipStream_t) {
+    BucketLaunch b;
+    b.n_chunks = n_chunks;
+    for (int k = 0; k <= t.count; ++k) b.tile_start.push_back(t.tile_start[k]);
+    for (int k = 0; k < t.count; ++k) {
+        b.n.push_back(t.n[k]);
+        b.offset.push_back(t.offset[k]);
+        for (int c = 0; c < n_chunks; ++c) b.chunk.push_back(t.chunk[k * n_chunks + c]);
+    }
+    g_bucket.push_back(b);
+    return hipSuccess;
+}
+
+hipError_t launch_bucket_flatten(const FlattenTable& table, int count, int64_t max_slot_len,
+                                 uint16_t*, hipStream_t) {
+    FlattenLaunch f;
+    f.count = count;
+    f.max_slot = max_slot_len;
+    for (int k = 0; k < count; ++k) f.d.push_back(table.d[k]);
+    g_flatten.push_back(f);
+    return hipSuccess;
+}
+
+hipError_t launch_ctl_step(const ChunkTable&, int, int64_t, const GradScalars&,
+                           const AdamScalars&, const BiasTable& tab, const ShardCopies&, bool,
+                           zero_step_control*, hipStream_t) {
+    g_bias.push_back(tab);
+    return hipSuccess;
+}
+
+hipError_t launch_accumulate(const uint16_t*, int64_t, int mode, const GradScalars&, float*,
+                             uint16_t*, hipStream_t) {
+    g_accumulate_mode.push_back(mode);
+    return hipSuccess;
+}
+
+#define ZERO_STUB          \
+    {                      \
+        ++g_other_launches; \
+        return hipSuccess;  \
+    }
+hipError_t launch_shard_step(const ChunkTable&, int, int64_t, const GradScalars&,
+                             const AdamScalars&, const ShardState&, int32_t*, double*,
+                             hipStream_t) ZERO_STUB
+hipError_t launch_overflow_check(const ChunkTable&, int, int64_t, const GradScalars&, int32_t*,
+                                 double*, hipStream_t) ZERO_STUB
+hipError_t launch_overflow_check_ctl(const ChunkTable&, int, int64_t, const GradScalars&,
+                                     zero_step_control*, hipStream_t) ZERO_STUB
+hipError_t launch_reduce_mean(const ChunkTable&, int, int64_t, const GradScalars&, uint16_t*,
+                              int32_t*, double*, hipStream_t) ZERO_STUB
+hipError_t launch_control_begin(zero_step_control*, hipStream_t) ZERO_STUB
+hipError_t launch_control_decide(zero_step_control*, float, int, hipStream_t) ZERO_STUB
+
+}  // namespace zero
+
+extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }
+
+// ---- checks ------------------------------------------------------------------
+
+static zero_adamw_params hp(int64_t step = 1) {
+    zero_adamw_params p = {1e-3f, 0.9f, 0.999f, 1e-8f, 0.01f, step, 1, 1};
+    return p;
+}
+
+// 100 bucket slices of ragged sizes at N = 8, 3 and 64: batching into
+// launches, the tile prefix, the offsets and the chunk pointers.
+static void bucket_tables() {
+    for (int N : {8, 3, 64, 1}) {
+        reset();
+        const int S = 100;
+        std::vector<std::vector<const void*>> ptrs(S);
+        std::vector<zero_bucket_slice> sl(S);
+        int64_t off = 0;
+        for (int k = 0; k < S; ++k) {
+            const int64_t n = (k % 7 == 3) ? 0 : 1 + (k * 7919) % 20000;
+            for (int c = 0; c < N; ++c)
+                ptrs[k].push_back(fake(kBase + (uint64_t(k) << 24) + (uint64_t(c) << 18)));
+            sl[k].grad_chunks = ptrs[k].data();
+            sl[k].n = n;
+            sl[k].offset = off;
+            off += (n + 7) / 8 * 8 + 8;
+        }
+        const int64_t n_state = off;
+        float* in[3] = {(float*)fake(0x100000000000ull), (float*)fake(0x110000000000ull),
+                        (float*)fake(0x120000000000ull)};
+        float* out[3] = {(float*)fake(0x130000000000ull), (float*)fake(0x140000000000ull),
+                         (float*)fake(0x150000000000ull)};
+        zero_adamw_params p = hp();
+        EXPECT(zero_shard_step_buckets(sl.data(), S, N, 1024.0f, n_state, in[0], in[1], in[2],
+                                       out[0], out[1], out[2], fake(0x160000000000ull), &p,
+                                       nullptr, nullptr, nullptr) == ZERO_OK);
+        const int per = std::min(zero::kMaxBucketsPerLaunch, zero::kBucketTablePtrs / N);
+        int live = 0;
+        for (int k = 0; k < S; ++k) live += sl[k].n > 0;
+        EXPECT(int(g_bucket.size()) == (live + per - 1) / per);
+        int k = 0;
+        for (const BucketLaunch& b : g_bucket) {
+            EXPECT(b.n_chunks == N && b.tile_start[0] == 0);
+            EXPECT(int(b.n.size()) <= per);
+            for (size_t i = 0; i < b.n.size(); ++i, ++k) {
+                while (sl[k].n == 0) ++k;
+                EXPECT(b.n[i] == sl[k].n && b.offset[i] == sl[k].offset);
+                EXPECT(b.tile_start[i + 1] - b.tile_start[i] == zero::step_tiles(sl[k].n));
+                for (int c = 0; c < N; ++c) EXPECT(b.chunk[i * N + c] == ptrs[k][c]);
+            }
+        }
+        // overlapping slices, in either order, and a misaligned offset
+        zero_bucket_slice two[2] = {sl[0], sl[1]};
+        two[1].offset = two[0].offset + two[0].n - 1;
+        two[1].offset -= two[1].offset % 8;
+        EXPECT(zero_shard_step_buckets(two, 2, N, 1.0f, n_state, in[0], in[1], in[2], out[0],
+                                       out[1], out[2], fake(0x160000000000ull), &p, nullptr,
+                                       nullptr, nullptr) == ZERO_EINVAL);
+        std::swap(two[0], two[1]);
+        EXPECT(zero_shard_step_buckets(two, 2, N, 1.0f, n_state, in[0], in[1], in[2], out[0],
+                                       out[1], out[2], fake(0x160000000000ull), &p, nullptr,
+                                       nullptr, nullptr) == ZERO_EINVAL);
+        two[0].offset = 4;
+        EXPECT(zero_shard_step_buckets(two, 1, N, 1.0f, n_state, in[0], in[1], in[2], out[0],
+                                       out[1], out[2], fake(0x160000000000ull), &p, nullptr,
+                                       nullptr, nullptr) == ZERO_EALIGN);
+    }
+}
+
+// 100 tensors into one bucket: flatten launches of at most 32 slots, the
+// offsets, the slot lengths and the padded total.
+static void flatten_tables() {
+    reset();
+    const int T = 100;
+    std::vector<const void*> src(T);
+    std::vector<int64_t> numel(T);
+    for (int k = 0; k < T; ++k) {
+        numel[k] = (k % 9 == 4) ? 0 : 1 + (k * 104729) % 5000;
+        src[k] = numel[k] ? fake(kBase + (uint64_t(k) << 20) + 2 * (k % 3)) : nullptr;
+    }
+    std::vector<int64_t> offs(T + 1);
+    EXPECT(zero_bucket_flatten(src.data(), numel.data(), T, 256, 2048,
+                               fake(0x200000000000ull), int64_t(1) << 30, offs.data(),
+                               nullptr) == ZERO_OK);
+    int64_t end = 0;
+    for (int k = 0; k < T; ++k) {
+        const int64_t start = (end + 255) / 256 * 256;
+        EXPECT(offs[k] == start);
+        end = start + numel[k];
+    }
+    EXPECT(offs[T] == (end + 2047) / 2048 * 2048);
+    int seen = 0;
+    for (const FlattenLaunch& f : g_flatten) {
+        EXPECT(f.count >= 1 && f.count <= zero::kFlattenBatch);
+        for (const zero::FlattenDesc& d : f.d) {
+            EXPECT(d.slot_len > 0 && d.slot_len <= f.max_slot);
+            EXPECT(d.numel <= d.slot_len);
+            ++seen;
+        }
+    }
+    int nonempty_slots = 0;
+    for (int k = 0; k < T; ++k) nonempty_slots += ((k + 1 < T ? offs[k + 1] : offs[T]) > offs[k]);
+    EXPECT(seen == nonempty_slots);
+    // capacity too small: ZERO_ERANGE with the offsets still filled
+    EXPECT(zero_bucket_flatten(src.data(), numel.data(), T, 256, 2048, fake(0x200000000000ull),
+                               offs[T] - 1, offs.data(), nullptr) == ZERO_ERANGE);
+    // lengths that would overflow
+    int64_t huge[2] = {INT64_MAX / 4, INT64_MAX / 4};
+    const void* hs[2] = {fake(kBase), fake(kBase + 0x1000)};
+    EXPECT(zero_bucket_flatten(hs, huge, 2, 256, 0, fake(0x200000000000ull), INT64_MAX,
+                               offs.data(), nullptr) == ZERO_EINVAL);
+}
+
+// Bias tables of the control-block steps: 64 values of t from hp->step.
+static void bias_tables() {
+    reset();
+    const void* ch[2] = {fake(kBase), fake(kBase + (1 << 20))};
+    float* st[4] = {(float*)fake(0x300000000000ull), (float*)fake(0x310000000000ull),
+                    (float*)fake(0x320000000000ull), (float*)fake(0x330000000000ull)};
+    zero_adamw_params p = hp(1000);
+    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
+                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    p.bias_correction = 0;
+    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
+                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    EXPECT(g_bias.size() == 2);
+    EXPECT(g_bias[0].t0 == 1000 && g_bias[1].t0 == 1000);
+    for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
+        const double t = 1000.0 + k;
+        EXPECT(g_bias[0].bc1[k] == float(1.0 - pow(double(0.9f), t)));
+        EXPECT(g_bias[0].bc2[k] == float(1.0 - pow(double(0.999f), t)));
+        EXPECT(g_bias[1].bc1[k] == 1.0f && g_bias[1].bc2[k] == 1.0f);
+    }
+}
+
+// Which accumulate mode each (index, N) selects, and what it may leave NULL.
+static void accumulate_modes() {
+    reset();
+    const void* x = fake(kBase);
+    float* acc = (float*)fake(0x400000000000ull);
+    void* mean = fake(0x410000000000ull);
+    EXPECT(zero_accumulate_chunk(x, 100, 0, 1, nullptr, mean, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunk(x, 100, 0, 4, acc, nullptr, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunk(x, 100, 1, 4, acc, nullptr, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunk(x, 100, 2, 4, acc, nullptr, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunk(x, 100, 3, 4, acc, mean, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunk(x, 100, 1, 2, acc, mean, nullptr) == ZERO_OK);
+    const int want[6] = {3, 0, 1, 1, 2, 2};
+    EXPECT(g_accumulate_mode.size() == 6);
+    for (int i = 0; i < 6; ++i) EXPECT(g_accumulate_mode[i] == want[i]);
+}
+
+// The host loss scaler and the control block initialiser.
+static void scaler_and_control() {
+    zero_loss_scaler s = {65536.0f, 2.0f, 0.5f, 1.0f, 16777216.0f, 3, 0, 0};
+    int32_t skip = -1;
+    const int flags[8] = {1, 0, 0, 0, 1, 1, 0, 0};
+    const float scales[8] = {32768, 32768, 32768, 65536, 32768, 16384, 16384, 16384};
+    for (int i = 0; i < 8; ++i) {
+        EXPECT(zero_update_loss_scale(&s, flags[i], &skip) == ZERO_OK);
+        EXPECT(skip == flags[i] && s.scale == scales[i]);
+    }
+    EXPECT(s.skipped_steps == 3 && s.good_steps == 2);
+    zero_step_control c;
+    memset(&c, 0x5a, sizeof c);
+    EXPECT(zero_control_init(&c, &s, 42) == ZERO_OK);
+    EXPECT(c.scale == 16384.0f && c.step == 42 && c.step_used == 42 && c.cur == 0);
+    EXPECT(c.good_steps == 2 && c.skipped_steps == 3 && c.error == 0 && c.overflow == 0);
+    s.backoff_factor = 1.5f;
+    EXPECT(zero_control_init(&c, &s, 1) == ZERO_EINVAL);
+    EXPECT(zero_update_loss_scale(&s, 0, &skip) == ZERO_EINVAL);
+}
+
+// Every entry point: n == 0 launches nothing; a failure sets the thread's
+// error text and a success clears it.
+static void empty_and_errors() {
+    reset();
+    zero_adamw_params p = hp();
+    const void* none[1] = {nullptr};
+    EXPECT(zero_overflow_check(none, 1, 0, 1.0f, (int32_t*)fake(0x500000000000ull), nullptr,
+                               nullptr) == ZERO_OK);
+    EXPECT(zero_shard_step(none, 1, 0, 1.0f, nullptr, nullptr, nullptr, nullptr, &p, nullptr,
+                           nullptr, nullptr) == ZERO_OK);
+    EXPECT(zero_reduce_mean_fp16(none, 1, 0, 1.0f, nullptr, nullptr, nullptr, nullptr) ==
+           ZERO_OK);
+    EXPECT(g_other_launches == 0);
+    EXPECT(zero_shard_step(nullptr, 1, 8, 1.0f, nullptr, nullptr, nullptr, nullptr, &p, nullptr,
+                           nullptr, nullptr) == ZERO_EINVAL);
+    EXPECT(strlen(zero_last_error_string()) > 0);
+    EXPECT(zero_overflow_check(none, 1, 0, 1.0f, (int32_t*)fake(0x500000000000ull), nullptr,
+                               nullptr) == ZERO_OK);
+    EXPECT(strlen(zero_last_error_string()) == 0);
+}
+
+int main() {
+    bucket_tables();
+    flatten_tables();
+    bias_tables();
+    accumulate_modes();
+    scaler_and_control();
+    empty_and_errors();
+    printf("abi harness: ok\n");
+    return 0;
+}
