@@ -183,6 +183,14 @@ float bias_correction(float beta, int64_t t) {
     return static_cast<float>(1.0 - pow(static_cast<double>(beta), static_cast<double>(t)));
 }
 
+// A shard of n params fits one step launch (one block per 4096 params).
+int check_step_length(int64_t n, const char* who) {
+    if (zero::step_tiles(n) > zero::kMaxGridBlocks)
+        return fail(ZERO_EINVAL, "%s: n = %lld is longer than one launch covers", who,
+                    static_cast<long long>(n));
+    return ZERO_OK;
+}
+
 int check_ctl_ptr(const zero_step_control* d_ctl, const char* who) {
     if (!d_ctl) return fail(ZERO_EINVAL, "%s: d_ctl is NULL", who);
     if (!aligned(d_ctl, 8)) return fail(ZERO_EALIGN, "%s: d_ctl is not 8-byte aligned", who);
@@ -214,6 +222,7 @@ int shard_step_common(const void* const* grad_chunks, int32_t n_chunks, int64_t 
     if ((rc = adam_scalars(hp, &as))) return rc;
     if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
     if (n == 0) return ok();  // nothing is read or written
+    if ((rc = check_step_length(n, who))) return rc;
     if ((rc = check_state(n, master_in, exp_avg_in, exp_avg_sq_in, master_out, exp_avg_out,
                           exp_avg_sq_out, param_fp16_out, who)))
         return rc;
@@ -302,6 +311,7 @@ int zero_shard_step_buckets(const zero_bucket_slice* slices, int32_t n_slices, i
         if (b.n > n_state - b.offset)
             return fail(ZERO_EINVAL, "%s: slice %d ends past n_state", who, k);
         if (b.n == 0) continue;
+        if ((rc = check_step_length(b.n, who))) return rc;
         ++live;
         if (!b.grad_chunks) return fail(ZERO_EINVAL, "%s: slice %d grad_chunks is NULL", who, k);
         for (int32_t c = 0; c < n_chunks; ++c) {
@@ -343,7 +353,7 @@ int zero_shard_step_buckets(const zero_bucket_slice* slices, int32_t n_slices, i
                                  static_cast<uint16_t*>(param_fp16_out)};
     int per_launch = zero::kBucketTablePtrs / n_chunks;
     if (per_launch > zero::kMaxBucketsPerLaunch) per_launch = zero::kMaxBucketsPerLaunch;
-    const int64_t kMaxGrid = 0x7fffffff;
+    const int64_t kMaxGrid = zero::kMaxGridBlocks;
     zero::BucketTable t;
     memset(&t, 0, sizeof t);
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -357,7 +367,6 @@ int zero_shard_step_buckets(const zero_bucket_slice* slices, int32_t n_slices, i
             if (e != hipSuccess) return hip_fail(e, who);
             memset(&t, 0, sizeof t);
         }
-        if (tiles > kMaxGrid) return fail(ZERO_EINVAL, "%s: slice %d is too long", who, k);
         const int i = t.count;
         t.n[i] = b.n;
         t.offset[i] = b.offset;
@@ -407,6 +416,8 @@ int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n
     const int mode = n_chunks == 1 ? 3 : index == 0 ? 0 : index == n_chunks - 1 ? 2 : 1;
     const bool uses_acc = mode != 3, writes_mean = mode >= 2;
     if (n == 0) return ok();
+    int rc = check_step_length(n, who);
+    if (rc) return rc;
     if (!chunk) return fail(ZERO_EINVAL, "%s: chunk is NULL", who);
     if (!aligned(chunk, 16)) return fail(ZERO_EALIGN, "%s: chunk is not 16-byte aligned", who);
     if (uses_acc) {
@@ -426,8 +437,7 @@ int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n
     zero::ChunkTable unused;
     zero::GradScalars gs;
     const void* none[1] = {nullptr};
-    int rc = check_chunks(none, n_chunks, 0, 1.0f, &unused, &gs);  // the 1/N scalars
-    if (rc) return rc;
+    if ((rc = check_chunks(none, n_chunks, 0, 1.0f, &unused, &gs))) return rc;  // the 1/N scalars
     const hipError_t e = zero::launch_accumulate(static_cast<const uint16_t*>(chunk), n, mode, gs,
                                                  acc, static_cast<uint16_t*>(mean_fp16),
                                                  static_cast<hipStream_t>(stream));
@@ -499,6 +509,7 @@ int zero_shard_step_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_
     if ((rc = adam_scalars(hp, &as))) return rc;
     if ((rc = check_ctl_ptr(d_ctl, who))) return rc;
     if (n == 0) return ok();
+    if ((rc = check_step_length(n, who))) return rc;
     if ((rc = check_state(n, master, exp_avg, exp_avg_sq, master, exp_avg, exp_avg_sq, param_fp16,
                           who)))
         return rc;
@@ -536,6 +547,7 @@ int zero_shard_step_out_ctl(const void* const* grad_chunks, int32_t n_chunks, in
     if (!masters || !exp_avgs || !exp_avg_sqs || !params_fp16)
         return fail(ZERO_EINVAL, "%s: a copy table is NULL", who);
     if (n == 0) return ok();
+    if ((rc = check_step_length(n, who))) return rc;
     // either copy may be read and the other written: the eight arrays are all
     // distinct, disjoint and clear of the chunks
     const void* arr[8] = {masters[0], exp_avgs[0], exp_avg_sqs[0], params_fp16[0],
@@ -602,6 +614,12 @@ int zero_bucket_flatten(const void* const* tensors, const int64_t* numels, int32
         if (overlap(tensors[k], 2 * numels[k], bucket, 2 * total))
             return fail(ZERO_EINVAL, "tensors[%d] overlaps the bucket", k);
     if (total == 0) return ok();
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        const int64_t next = k + 1 < n_tensors ? offsets_out[k + 1] : total;
+        if ((next - offsets_out[k] + zero::kFlattenTile - 1) / zero::kFlattenTile >
+            zero::kMaxGridBlocks)
+            return fail(ZERO_EINVAL, "tensor %d's slot is longer than one launch covers", k);
+    }
     // Slots: tensor k owns [off_k, off_{k+1}); the last slot runs to the padded end.
     // A bucket with no tensors (all numels 0 and total 0) returned above.
     zero::FlattenTable table;

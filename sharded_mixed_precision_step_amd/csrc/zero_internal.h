@@ -17,6 +17,7 @@ constexpr int kCheckBlocksPerCU = 6;            // resident blocks of the check 
 constexpr int kFlattenBatch = 32;  // tensors per flatten launch (kernel-argument table)
 constexpr int kFlattenSpan = 4;    // packs per lane in a flatten tile
 constexpr int64_t kFlattenTile = static_cast<int64_t>(kBlock) * kFlattenSpan * kPack;  // elements
+constexpr int64_t kMaxGridBlocks = 0x7fffffff;  // blocks in one launch's x dimension
 constexpr int kMaxBucketsPerLaunch = 32;  // bucket slices per multi-bucket step launch
 constexpr int kBucketTablePtrs = 256;     // chunk pointers per multi-bucket step launch
 

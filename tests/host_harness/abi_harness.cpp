@@ -319,7 +319,37 @@ static void empty_and_errors() {
     EXPECT(strlen(zero_last_error_string()) == 0);
 }
 
+// Shards and slots longer than one launch's grid covers are refused before
+// anything is launched (the grid would otherwise wrap and skip work).
+static void launch_length_limits() {
+    reset();
+    // one block per 4096 params; a ragged tail rides in the last block
+    const int64_t fits = zero::kMaxGridBlocks * zero::kTilePacks * zero::kPack + 7;
+    const int64_t too_long = (zero::kMaxGridBlocks + 1) * zero::kTilePacks * zero::kPack;
+    const void* ch[1] = {fake(kBase)};
+    zero_adamw_params p = hp();
+    float* st[7];
+    for (int k = 0; k < 7; ++k) st[k] = (float*)fake(0x100000000000ull * (k + 1));
+    EXPECT(zero_shard_step_out(ch, 1, too_long, 1.0f, st[0], st[1], st[2], st[3], st[4], st[5],
+                               st[6], &p, nullptr, nullptr, nullptr) == ZERO_EINVAL);
+    EXPECT(strstr(zero_last_error_string(), "longer than one launch") != nullptr);
+    zero_shard_step_out(ch, 1, fits, 1.0f, st[0], st[1], st[2], st[3], st[4], st[5], st[6], &p,
+                        nullptr, nullptr, nullptr);     // refused later, for overlapping arrays
+    EXPECT(strstr(zero_last_error_string(), "longer than one launch") == nullptr);
+    EXPECT(zero_accumulate_chunk(ch[0], too_long, 0, 2, st[0], nullptr, nullptr) == ZERO_EINVAL);
+    zero_bucket_slice sl = {ch, too_long, 0};
+    EXPECT(zero_shard_step_buckets(&sl, 1, 1, 1.0f, too_long, st[0], st[1], st[2], st[3], st[4],
+                                   st[5], st[6], &p, nullptr, nullptr, nullptr) == ZERO_EINVAL);
+    int64_t numel[1] = {zero::kMaxGridBlocks * zero::kFlattenTile + 1};
+    int64_t offs[2];
+    EXPECT(zero_bucket_flatten(ch, numel, 1, 256, 0, fake(0x200000000000ull), INT64_MAX, offs,
+                               nullptr) == ZERO_EINVAL);
+    EXPECT(g_bucket.empty() && g_flatten.empty() && g_accumulate_mode.empty() &&
+           g_other_launches == 0);
+}
+
 int main() {
+    launch_length_limits();
     bucket_tables();
     flatten_tables();
     bias_tables();
