@@ -411,6 +411,17 @@ int zero_shard_step_out_ctl(const void* const* grad_chunks, int32_t n_chunks, in
                             float* const* exp_avg_sqs, void* const* params_fp16,
                             const zero_adamw_params* hp, zero_step_control* d_ctl,
                             void* stream);
+/* zero_shard_step_buckets_ctl: zero_shard_step_out_ctl over a table of
+ * bucket slices (ZeRO-2), in the launches zero_shard_step_buckets makes.  The
+ * non-empty slices must tile [0, n_state) exactly (an element no slice writes
+ * would hold stale data in the copy a clean step makes current); n_state is
+ * the length of each of the eight state arrays.  Follow it with
+ * zero_control_decide(..., flip_copy = 1). */
+int zero_shard_step_buckets_ctl(const zero_bucket_slice* slices, int32_t n_slices,
+                                int32_t n_chunks, int64_t n_state, float* const* masters,
+                                float* const* exp_avgs, float* const* exp_avg_sqs,
+                                void* const* params_fp16, const zero_adamw_params* hp,
+                                zero_step_control* d_ctl, void* stream);
 
 /* Text of the last error reported by a call on this thread ("" if none). */
 const char* zero_last_error_string(void);

@@ -34,7 +34,8 @@ EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
             "zero_shard_step_buckets", "zero_reduce_mean_fp16", "zero_accumulate_chunk",
             "zero_bucket_flatten", "zero_update_loss_scale", "zero_control_init",
             "zero_control_begin", "zero_overflow_check_ctl", "zero_control_decide",
-            "zero_shard_step_ctl", "zero_shard_step_out_ctl", "zero_last_error_string")
+            "zero_shard_step_ctl", "zero_shard_step_out_ctl", "zero_shard_step_buckets_ctl",
+            "zero_last_error_string")
 ZERO_CTL_STEPS = 64
 
 
@@ -120,6 +121,8 @@ def _load() -> ctypes.CDLL:
                                         vp, vp]
     lib.zero_shard_step_out_ctl.argtypes = [pp, i32, i64, pp, pp, pp, pp,
                                             ctypes.POINTER(AdamWParams), vp, vp]
+    lib.zero_shard_step_buckets_ctl.argtypes = [ctypes.POINTER(BucketSliceC), i32, i32, i64, pp,
+                                                pp, pp, pp, ctypes.POINTER(AdamWParams), vp, vp]
     lib.zero_last_error_string.argtypes = []
     lib.zero_last_error_string.restype = ctypes.c_char_p
     for name in EXPORTED[:-1]:
@@ -505,6 +508,24 @@ def zero_shard_step_out_ctl(grad_chunks: Sequence[torch.Tensor], copies, hp: Ada
                                        _ctl(ctl), _stream(stream)))
 
 
+def zero_shard_step_buckets_ctl(slices: BucketSlices, copies, hp: AdamWParams,
+                                ctl: torch.Tensor, stream=None) -> None:
+    """The single-pass update over a bucket table under the control block:
+    every slice from copy ctl.cur into the other.  The slices must tile the
+    state arrays exactly."""
+    n = copies[0][0].numel()
+    for k, cp in enumerate(copies):
+        for j, t in enumerate(cp):
+            if t.numel() != n:
+                raise ValueError(f"copy {k} array {j} has {t.numel()} elements, expected {n}")
+    dts = (torch.float32, torch.float32, torch.float32, torch.float16)
+    tables = [_ptr_array([_dev(copies[k][j], dts[j], f"copy {k} array {j}") for k in range(2)])
+              for j in range(4)]
+    _check(lib.zero_shard_step_buckets_ctl(slices.table, slices.count, slices.n_chunks, n,
+                                           *tables, ctypes.byref(hp), _ctl(ctl),
+                                           _stream(stream)))
+
+
 class DeviceStepper:
     """Enqueues whole steps under a control block with no read-back.  The
     update's bias corrections come from a table based at t0 and covering
@@ -539,6 +560,14 @@ class DeviceStepper:
         self._rebase()
         zero_control_begin(self.ctl, stream=stream)
         zero_shard_step_out_ctl(grad_chunks, copies, self.hp, self.ctl, stream=stream)
+        zero_control_decide(self.ctl, 0.0, True, stream=stream)
+        self.since_base += 1
+
+    def single_pass_buckets(self, slices: BucketSlices, copies, stream=None) -> None:
+        """single_pass over the bucket slices of a ZeRO-2 shard."""
+        self._rebase()
+        zero_control_begin(self.ctl, stream=stream)
+        zero_shard_step_buckets_ctl(slices, copies, self.hp, self.ctl, stream=stream)
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
 

@@ -206,6 +206,137 @@ void bias_table(const zero_adamw_params* hp, zero::BiasTable* tab) {
     }
 }
 
+// Scalars and slices of a bucket-table call: every slice inside the state,
+// 8-element aligned, of a length one launch covers, with its chunks present
+// and aligned; no two slices on one state element.  *live counts the
+// non-empty slices; *covers (if asked) tells whether they tile [0, n_state).
+int check_bucket_call(const zero_bucket_slice* slices, int32_t n_slices, int32_t n_chunks,
+                      float loss_scale, int64_t n_state, const zero_adamw_params* hp,
+                      const char* who, zero::GradScalars* gs, zero::AdamScalars* as,
+                      int64_t* live, bool* covers) {
+    if (n_slices < 0) return fail(ZERO_EINVAL, "%s: n_slices < 0", who);
+    if (n_slices > 0 && !slices) return fail(ZERO_EINVAL, "%s: slices is NULL", who);
+    if (n_chunks < 1 || n_chunks > ZERO_MAX_CHUNKS)
+        return fail(ZERO_EINVAL, "%s: n_chunks = %d outside [1, %d]", who, n_chunks,
+                    ZERO_MAX_CHUNKS);
+    if (n_state < 0) return fail(ZERO_EINVAL, "%s: n_state < 0", who);
+    zero::ChunkTable unused;
+    const void* no_chunks[1] = {nullptr};
+    int rc = check_chunks(no_chunks, n_chunks, 0, loss_scale, &unused, gs);  // scalars only
+    if (rc) return rc;
+    if ((rc = adam_scalars(hp, as))) return rc;
+    *live = 0;
+    for (int32_t k = 0; k < n_slices; ++k) {
+        const zero_bucket_slice& b = slices[k];
+        if (b.n < 0 || b.offset < 0)
+            return fail(ZERO_EINVAL, "%s: slice %d has n or offset < 0", who, k);
+        if (b.offset % zero::kPack != 0)
+            return fail(ZERO_EALIGN, "%s: slice %d offset %lld is not a multiple of 8", who, k,
+                        static_cast<long long>(b.offset));
+        if (b.n > n_state - b.offset)
+            return fail(ZERO_EINVAL, "%s: slice %d ends past n_state", who, k);
+        if (b.n == 0) continue;
+        if ((rc = check_step_length(b.n, who))) return rc;
+        ++*live;
+        if (!b.grad_chunks) return fail(ZERO_EINVAL, "%s: slice %d grad_chunks is NULL", who, k);
+        for (int32_t c = 0; c < n_chunks; ++c) {
+            if (!b.grad_chunks[c])
+                return fail(ZERO_EINVAL, "%s: slice %d grad_chunks[%d] is NULL", who, k, c);
+            if (!aligned(b.grad_chunks[c], 16))
+                return fail(ZERO_EALIGN, "%s: slice %d grad_chunks[%d] is not 16-byte aligned",
+                            who, k, c);
+        }
+    }
+    // slices may not share a state element: sort by offset, compare neighbours
+    std::vector<int32_t> order;
+    order.reserve(static_cast<size_t>(*live));
+    for (int32_t k = 0; k < n_slices; ++k)
+        if (slices[k].n > 0) order.push_back(k);
+    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        return slices[a].offset < slices[b].offset;
+    });
+    int64_t end = 0;
+    bool tiles = true;
+    for (size_t i = 0; i < order.size(); ++i) {
+        const zero_bucket_slice& b = slices[order[i]];
+        if (i > 0 && slices[order[i - 1]].offset + slices[order[i - 1]].n > b.offset)
+            return fail(ZERO_EINVAL, "%s: slices %d and %d overlap", who, order[i - 1], order[i]);
+        if (b.offset != end) tiles = false;
+        end = b.offset + b.n;
+    }
+    if (covers) *covers = tiles && end == n_state;
+    return ZERO_OK;
+}
+
+// No state array (n_state elements; fp32 but for every fourth, fp16) shares
+// a byte with any slice's chunks.
+int check_slices_clear_of(const zero_bucket_slice* slices, int32_t n_slices, int32_t n_chunks,
+                          int64_t n_state, const void* const* arrays, int n_arrays,
+                          const char* who) {
+    for (int32_t k = 0; k < n_slices; ++k) {
+        if (slices[k].n == 0) continue;
+        for (int32_t c = 0; c < n_chunks; ++c)
+            for (int a = 0; a < n_arrays; ++a) {
+                const int64_t bytes = (a % 4 == 3 ? 2 : 4) * n_state;
+                if (overlap(arrays[a], bytes, slices[k].grad_chunks[c], 2 * slices[k].n))
+                    return fail(ZERO_EINVAL, "%s: state array %d overlaps slice %d chunk %d", who,
+                                a, k, c);
+            }
+    }
+    return ZERO_OK;
+}
+
+// Two copies of a state (master, exp_avg, exp_avg_sq, param_fp16 each): all
+// eight arrays present, 16-byte aligned and pairwise disjoint, since either
+// copy may be read while the other is written.
+int check_copy_pair(const void* const* arr, int64_t n, const char* who) {
+    const int64_t bytes[8] = {4 * n, 4 * n, 4 * n, 2 * n, 4 * n, 4 * n, 4 * n, 2 * n};
+    for (int a = 0; a < 8; ++a) {
+        if (!arr[a]) return fail(ZERO_EINVAL, "%s: state array %d of 8 is NULL", who, a);
+        if (!aligned(arr[a], 16))
+            return fail(ZERO_EALIGN, "%s: state array %d of 8 is not 16-byte aligned", who, a);
+    }
+    for (int a = 0; a < 8; ++a)
+        for (int b = a + 1; b < 8; ++b)
+            if (overlap(arr[a], bytes[a], arr[b], bytes[b]))
+                return fail(ZERO_EINVAL, "%s: state arrays %d and %d overlap", who, a, b);
+    return ZERO_OK;
+}
+
+// Launches of up to kMaxBucketsPerLaunch slices and kBucketTablePtrs chunk
+// pointers each, in slice order, through `launch`.
+template <typename Launch>
+int launch_bucket_batches(const zero_bucket_slice* slices, int32_t n_slices, int32_t n_chunks,
+                          const char* who, Launch launch) {
+    int per_launch = zero::kBucketTablePtrs / n_chunks;
+    if (per_launch > zero::kMaxBucketsPerLaunch) per_launch = zero::kMaxBucketsPerLaunch;
+    zero::BucketTable t;
+    memset(&t, 0, sizeof t);
+    for (int32_t k = 0; k < n_slices; ++k) {
+        const zero_bucket_slice& b = slices[k];
+        if (b.n == 0) continue;
+        const int64_t tiles = zero::step_tiles(b.n);
+        if (t.count > 0 &&
+            (t.count == per_launch || t.tile_start[t.count] + tiles > zero::kMaxGridBlocks)) {
+            const hipError_t e = launch(t);
+            if (e != hipSuccess) return hip_fail(e, who);
+            memset(&t, 0, sizeof t);
+        }
+        const int i = t.count;
+        t.n[i] = b.n;
+        t.offset[i] = b.offset;
+        for (int32_t c = 0; c < n_chunks; ++c)
+            t.chunk[i * n_chunks + c] = static_cast<const uint16_t*>(b.grad_chunks[c]);
+        t.tile_start[i + 1] = t.tile_start[i] + tiles;
+        t.count = i + 1;
+    }
+    if (t.count > 0) {
+        const hipError_t e = launch(t);
+        if (e != hipSuccess) return hip_fail(e, who);
+    }
+    return ok();
+}
+
 // Validation and launch shared by the in-place and the out-of-place step.
 // Output k may equal input k exactly (in place); otherwise no output may
 // share a byte with any input, another output or a gradient chunk.
@@ -285,102 +416,64 @@ int zero_shard_step_buckets(const zero_bucket_slice* slices, int32_t n_slices, i
                             void* param_fp16_out, const zero_adamw_params* hp,
                             int32_t* d_overflow, double* d_sqnorm, void* stream) {
     static const char* who = "zero_shard_step_buckets";
-    if (n_slices < 0) return fail(ZERO_EINVAL, "%s: n_slices < 0", who);
-    if (n_slices > 0 && !slices) return fail(ZERO_EINVAL, "%s: slices is NULL", who);
-    if (n_chunks < 1 || n_chunks > ZERO_MAX_CHUNKS)
-        return fail(ZERO_EINVAL, "%s: n_chunks = %d outside [1, %d]", who, n_chunks,
-                    ZERO_MAX_CHUNKS);
-    if (n_state < 0) return fail(ZERO_EINVAL, "%s: n_state < 0", who);
-    zero::ChunkTable unused;
     zero::GradScalars gs;
     zero::AdamScalars as;
-    const void* no_chunks[1] = {nullptr};
-    int rc = check_chunks(no_chunks, n_chunks, 0, loss_scale, &unused, &gs);  // scalars only
-    if (rc) return rc;
-    if ((rc = adam_scalars(hp, &as))) return rc;
-    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
-    // every slice inside the state arrays, 8-element aligned, chunks present
     int64_t live = 0;
-    for (int32_t k = 0; k < n_slices; ++k) {
-        const zero_bucket_slice& b = slices[k];
-        if (b.n < 0 || b.offset < 0)
-            return fail(ZERO_EINVAL, "%s: slice %d has n or offset < 0", who, k);
-        if (b.offset % zero::kPack != 0)
-            return fail(ZERO_EALIGN, "%s: slice %d offset %lld is not a multiple of 8", who, k,
-                        static_cast<long long>(b.offset));
-        if (b.n > n_state - b.offset)
-            return fail(ZERO_EINVAL, "%s: slice %d ends past n_state", who, k);
-        if (b.n == 0) continue;
-        if ((rc = check_step_length(b.n, who))) return rc;
-        ++live;
-        if (!b.grad_chunks) return fail(ZERO_EINVAL, "%s: slice %d grad_chunks is NULL", who, k);
-        for (int32_t c = 0; c < n_chunks; ++c) {
-            if (!b.grad_chunks[c])
-                return fail(ZERO_EINVAL, "%s: slice %d grad_chunks[%d] is NULL", who, k, c);
-            if (!aligned(b.grad_chunks[c], 16))
-                return fail(ZERO_EALIGN, "%s: slice %d grad_chunks[%d] is not 16-byte aligned",
-                            who, k, c);
-        }
-    }
+    int rc = check_bucket_call(slices, n_slices, n_chunks, loss_scale, n_state, hp, who, &gs, &as,
+                               &live, nullptr);
+    if (rc) return rc;
+    if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
     if (live == 0) return ok();
-    // slices may not share a state element: sort by offset, compare neighbours
-    std::vector<int32_t> order;
-    order.reserve(static_cast<size_t>(live));
-    for (int32_t k = 0; k < n_slices; ++k)
-        if (slices[k].n > 0) order.push_back(k);
-    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-        return slices[a].offset < slices[b].offset;
-    });
-    for (size_t i = 1; i < order.size(); ++i) {
-        const zero_bucket_slice& a = slices[order[i - 1]];
-        if (a.offset + a.n > slices[order[i]].offset)
-            return fail(ZERO_EINVAL, "%s: slices %d and %d overlap", who, order[i - 1], order[i]);
-    }
     if ((rc = check_state(n_state, master_in, exp_avg_in, exp_avg_sq_in, master_out, exp_avg_out,
                           exp_avg_sq_out, param_fp16_out, who)))
         return rc;
-    for (int32_t k = 0; k < n_slices; ++k) {
-        if (slices[k].n == 0) continue;
-        for (int32_t c = 0; c < n_chunks; ++c)
-            if ((rc = check_outputs_clear_of(n_state, master_out, exp_avg_out, exp_avg_sq_out,
-                                             param_fp16_out, slices[k].grad_chunks[c],
-                                             2 * slices[k].n, who, c)))
-                return rc;
-    }
-    // launches of up to kMaxBucketsPerLaunch slices and kBucketTablePtrs chunk pointers
+    const void* outs[4] = {master_out, exp_avg_out, exp_avg_sq_out, param_fp16_out};
+    if ((rc = check_slices_clear_of(slices, n_slices, n_chunks, n_state, outs, 4, who))) return rc;
     const zero::ShardState st = {master_in,  exp_avg_in,  exp_avg_sq_in, master_out,
                                  exp_avg_out, exp_avg_sq_out,
                                  static_cast<uint16_t*>(param_fp16_out)};
-    int per_launch = zero::kBucketTablePtrs / n_chunks;
-    if (per_launch > zero::kMaxBucketsPerLaunch) per_launch = zero::kMaxBucketsPerLaunch;
-    const int64_t kMaxGrid = zero::kMaxGridBlocks;
-    zero::BucketTable t;
-    memset(&t, 0, sizeof t);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    for (int32_t k = 0; k < n_slices; ++k) {
-        const zero_bucket_slice& b = slices[k];
-        if (b.n == 0) continue;
-        const int64_t tiles = zero::step_tiles(b.n);
-        if (t.count > 0 && (t.count == per_launch || t.tile_start[t.count] + tiles > kMaxGrid)) {
-            const hipError_t e = zero::launch_bucket_step(t, n_chunks, gs, as, st, d_overflow,
-                                                          d_sqnorm, hs);
-            if (e != hipSuccess) return hip_fail(e, who);
-            memset(&t, 0, sizeof t);
-        }
-        const int i = t.count;
-        t.n[i] = b.n;
-        t.offset[i] = b.offset;
-        for (int32_t c = 0; c < n_chunks; ++c)
-            t.chunk[i * n_chunks + c] = static_cast<const uint16_t*>(b.grad_chunks[c]);
-        t.tile_start[i + 1] = t.tile_start[i] + tiles;
-        t.count = i + 1;
+    return launch_bucket_batches(slices, n_slices, n_chunks, who, [&](const zero::BucketTable& t) {
+        return zero::launch_bucket_step(t, n_chunks, gs, as, st, d_overflow, d_sqnorm, hs);
+    });
+}
+
+int zero_shard_step_buckets_ctl(const zero_bucket_slice* slices, int32_t n_slices,
+                                int32_t n_chunks, int64_t n_state, float* const* masters,
+                                float* const* exp_avgs, float* const* exp_avg_sqs,
+                                void* const* params_fp16, const zero_adamw_params* hp,
+                                zero_step_control* d_ctl, void* stream) {
+    static const char* who = "zero_shard_step_buckets_ctl";
+    zero::GradScalars gs;
+    zero::AdamScalars as;
+    int64_t live = 0;
+    bool covers = false;
+    int rc = check_bucket_call(slices, n_slices, n_chunks, 1.0f, n_state, hp, who, &gs, &as,
+                               &live, &covers);
+    if (rc) return rc;
+    if ((rc = check_ctl_ptr(d_ctl, who))) return rc;
+    if (!masters || !exp_avgs || !exp_avg_sqs || !params_fp16)
+        return fail(ZERO_EINVAL, "%s: a copy table is NULL", who);
+    if (n_state == 0) return ok();
+    if (!covers)
+        return fail(ZERO_EINVAL, "%s: the slices do not cover [0, n_state) exactly", who);
+    const void* arr[8] = {masters[0], exp_avgs[0], exp_avg_sqs[0], params_fp16[0],
+                          masters[1], exp_avgs[1], exp_avg_sqs[1], params_fp16[1]};
+    if ((rc = check_copy_pair(arr, n_state, who))) return rc;
+    if ((rc = check_slices_clear_of(slices, n_slices, n_chunks, n_state, arr, 8, who))) return rc;
+    zero::BiasTable tab;
+    bias_table(hp, &tab);
+    zero::ShardCopies sc;
+    for (int k = 0; k < 2; ++k) {
+        sc.master[k] = masters[k];
+        sc.exp_avg[k] = exp_avgs[k];
+        sc.exp_avg_sq[k] = exp_avg_sqs[k];
+        sc.param_fp16[k] = static_cast<uint16_t*>(params_fp16[k]);
     }
-    if (t.count > 0) {
-        const hipError_t e = zero::launch_bucket_step(t, n_chunks, gs, as, st, d_overflow,
-                                                      d_sqnorm, hs);
-        if (e != hipSuccess) return hip_fail(e, who);
-    }
-    return ok();
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return launch_bucket_batches(slices, n_slices, n_chunks, who, [&](const zero::BucketTable& t) {
+        return zero::launch_bucket_ctl_step(t, n_chunks, gs, as, tab, sc, d_ctl, hs);
+    });
 }
 
 int zero_reduce_mean_fp16(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
@@ -552,20 +645,12 @@ int zero_shard_step_out_ctl(const void* const* grad_chunks, int32_t n_chunks, in
     // distinct, disjoint and clear of the chunks
     const void* arr[8] = {masters[0], exp_avgs[0], exp_avg_sqs[0], params_fp16[0],
                           masters[1], exp_avgs[1], exp_avg_sqs[1], params_fp16[1]};
+    if ((rc = check_copy_pair(arr, n, who))) return rc;
     const int64_t bytes[8] = {4 * n, 4 * n, 4 * n, 2 * n, 4 * n, 4 * n, 4 * n, 2 * n};
-    for (int a = 0; a < 8; ++a) {
-        if (!arr[a]) return fail(ZERO_EINVAL, "%s: state array %d of 8 is NULL", who, a);
-        if (!aligned(arr[a], 16))
-            return fail(ZERO_EALIGN, "%s: state array %d of 8 is not 16-byte aligned", who, a);
-    }
-    for (int a = 0; a < 8; ++a) {
-        for (int b = a + 1; b < 8; ++b)
-            if (overlap(arr[a], bytes[a], arr[b], bytes[b]))
-                return fail(ZERO_EINVAL, "%s: state arrays %d and %d overlap", who, a, b);
+    for (int a = 0; a < 8; ++a)
         for (int32_t c = 0; c < n_chunks; ++c)
             if (overlap(arr[a], bytes[a], grad_chunks[c], 2 * n))
                 return fail(ZERO_EINVAL, "%s: state array %d overlaps grad_chunks[%d]", who, a, c);
-    }
     zero::BiasTable tab;
     bias_table(hp, &tab);
     zero::ShardCopies sc;

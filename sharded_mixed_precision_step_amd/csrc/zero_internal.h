@@ -126,6 +126,10 @@ hipError_t launch_ctl_step(const ChunkTable& chunks, int n_chunks, int64_t n,
                            const GradScalars& gs, const AdamScalars& as, const BiasTable& tab,
                            const ShardCopies& sc, bool single_pass, zero_step_control* ctl,
                            hipStream_t stream);
+hipError_t launch_bucket_ctl_step(const BucketTable& t, int n_chunks, const GradScalars& gs,
+                                  const AdamScalars& as, const BiasTable& tab,
+                                  const ShardCopies& sc, zero_step_control* ctl,
+                                  hipStream_t stream);
 hipError_t launch_overflow_check_ctl(const ChunkTable& chunks, int n_chunks, int64_t n,
                                      const GradScalars& gs, zero_step_control* ctl,
                                      hipStream_t stream);

@@ -374,6 +374,37 @@ __global__ __launch_bounds__(kBlock) void ctl_step_kernel(ChunkTable chunks, int
     if constexpr (SINGLE) publish(bad, sq, &ctl->overflow, &ctl->sqnorm);
 }
 
+// The single-pass update over a bucket table under a control block: slice k
+// of copy cur is read and slice k of copy 1 - cur written, with S, t and
+// the copy from the block and the flag and squared norm into it.
+template <int NC>
+__global__ __launch_bounds__(kBlock) void bucket_ctl_step_kernel(BucketTable t, int n_chunks,
+                                                                 GradScalars gs, AdamScalars as,
+                                                                 BiasTable tab, ShardCopies sc,
+                                                                 zero_step_control* ctl) {
+    const int64_t kt = ctl->step_used - tab.t0;
+    if (kt < 0 || kt >= ZERO_CTL_STEPS) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&ctl->error, 1);
+        return;
+    }
+    as.bc1 = tab.bc1[kt];
+    as.bc2 = tab.bc2[kt];
+    gs = with_scale(gs, ctl->scale_used);
+    const int in = ctl->cur & 1, out = 1 - in;
+    const int64_t b = blockIdx.x;
+    int k = 0;
+    while (k + 1 < t.count && b >= t.tile_start[k + 1]) ++k;
+    const int64_t off = t.offset[k];
+    const ShardState sk = {sc.master[in] + off,  sc.exp_avg[in] + off,  sc.exp_avg_sq[in] + off,
+                           sc.master[out] + off, sc.exp_avg[out] + off, sc.exp_avg_sq[out] + off,
+                           sc.param_fp16[out] + off};
+    bool bad = false;
+    double sq = 0.0;
+    step_block<NC, true>(&t.chunk[k * n_chunks], n_chunks, t.n[k], b - t.tile_start[k],
+                         b + 1 == t.tile_start[k + 1], gs, as, sk, bad, sq);
+    publish(bad, sq, &ctl->overflow, &ctl->sqnorm);
+}
+
 // One thread: start a step.
 __global__ void control_begin_kernel(zero_step_control* c) {
     c->overflow = 0;
@@ -662,6 +693,16 @@ hipError_t ctl_step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, cons
 }
 
 template <int NC>
+hipError_t bucket_ctl_impl(const BucketTable& t, int n_chunks, const GradScalars& gs,
+                           const AdamScalars& as, const BiasTable& tab, const ShardCopies& sc,
+                           zero_step_control* ctl, hipStream_t stream) {
+    const int64_t grid = t.tile_start[t.count];
+    hipLaunchKernelGGL(bucket_ctl_step_kernel<NC>, dim3(static_cast<unsigned>(grid)),
+                       dim3(kBlock), 0, stream, t, n_chunks, gs, as, tab, sc, ctl);
+    return hipGetLastError();
+}
+
+template <int NC>
 hipError_t check_ctl_impl(const ChunkTable& chunks, int n_chunks, int64_t n,
                           const GradScalars& gs, zero_step_control* ctl, hipStream_t stream) {
     const int64_t grid = check_grid(n);
@@ -798,6 +839,22 @@ hipError_t launch_ctl_step(const ChunkTable& chunks, int n_chunks, int64_t n,
                        ? ctl_step_impl<0, true>(chunks, n_chunks, n, gs, as, tab, sc, ctl, stream)
                        : ctl_step_impl<0, false>(chunks, n_chunks, n, gs, as, tab, sc, ctl,
                                                  stream);
+    }
+#undef ZERO_CASE
+}
+
+hipError_t launch_bucket_ctl_step(const BucketTable& t, int n_chunks, const GradScalars& gs,
+                                  const AdamScalars& as, const BiasTable& tab,
+                                  const ShardCopies& sc, zero_step_control* ctl,
+                                  hipStream_t stream) {
+    if (t.count <= 0 || t.tile_start[t.count] <= 0) return hipSuccess;
+#define ZERO_CASE(K) \
+    case K:          \
+        return bucket_ctl_impl<K>(t, n_chunks, gs, as, tab, sc, ctl, stream);
+    switch (n_chunks) {
+        ZERO_FOR_EACH_N(ZERO_CASE)
+        default:
+            return bucket_ctl_impl<0>(t, n_chunks, gs, as, tab, sc, ctl, stream);
     }
 #undef ZERO_CASE
 }

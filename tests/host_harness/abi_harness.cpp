@@ -83,6 +83,13 @@ hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScal
     return hipSuccess;
 }
 
+hipError_t launch_bucket_ctl_step(const BucketTable& t, int n_chunks, const GradScalars& gs,
+                                  const AdamScalars& as, const BiasTable& tab,
+                                  const ShardCopies&, zero_step_control*, hipStream_t s) {
+    g_bias.push_back(tab);
+    return launch_bucket_step(t, n_chunks, gs, as, ShardState{}, nullptr, nullptr, s);
+}
+
 hipError_t launch_bucket_flatten(const FlattenTable& table, int count, int64_t max_slot_len,
                                  uint16_t*, hipStream_t) {
     FlattenLaunch f;
@@ -348,8 +355,47 @@ static void launch_length_limits() {
            g_other_launches == 0);
 }
 
+// The bucket table under a control block: the same batching, one bias table
+// per launch, and slices that must tile the state exactly.
+static void bucket_tables_ctl() {
+    reset();
+    const int S = 40, N = 8;
+    std::vector<std::vector<const void*>> ptrs(S);
+    std::vector<zero_bucket_slice> sl(S);
+    int64_t off = 0;
+    for (int k = 0; k < S; ++k) {
+        for (int c = 0; c < N; ++c)
+            ptrs[k].push_back(fake(kBase + (uint64_t(k) << 24) + (uint64_t(c) << 18)));
+        sl[k].grad_chunks = ptrs[k].data();
+        sl[k].n = 8 * (1 + (k * 131) % 900);
+        sl[k].offset = off;
+        off += sl[k].n;
+    }
+    float* m[2] = {(float*)fake(0x100000000000ull), (float*)fake(0x180000000000ull)};
+    float* a[2] = {(float*)fake(0x110000000000ull), (float*)fake(0x190000000000ull)};
+    float* v[2] = {(float*)fake(0x120000000000ull), (float*)fake(0x1a0000000000ull)};
+    void* p16[2] = {fake(0x130000000000ull), fake(0x1b0000000000ull)};
+    zero_step_control* ctl = (zero_step_control*)fake(0x1c0000000000ull);
+    zero_adamw_params p = hp(7);
+    EXPECT(zero_shard_step_buckets_ctl(sl.data(), S, N, off, m, a, v, p16, &p, ctl, nullptr) ==
+           ZERO_OK);
+    EXPECT(g_bucket.size() == 2 && g_bias.size() == 2 && g_bias[0].t0 == 7);
+    EXPECT(g_bucket[0].n.size() == 32 && g_bucket[1].n.size() == 8);
+    // a gap, a missing end, the same copy twice
+    EXPECT(zero_shard_step_buckets_ctl(sl.data(), S, N, off + 8, m, a, v, p16, &p, ctl, nullptr) ==
+           ZERO_EINVAL);
+    std::vector<zero_bucket_slice> gap(sl);
+    gap[5].offset += 8;
+    EXPECT(zero_shard_step_buckets_ctl(gap.data(), S, N, off + 8, m, a, v, p16, &p, ctl,
+                                       nullptr) == ZERO_EINVAL);
+    float* same[2] = {m[0], m[0]};
+    EXPECT(zero_shard_step_buckets_ctl(sl.data(), S, N, off, same, a, v, p16, &p, ctl, nullptr) ==
+           ZERO_EINVAL);
+}
+
 int main() {
     launch_length_limits();
+    bucket_tables_ctl();
     bucket_tables();
     flatten_tables();
     bias_tables();

@@ -273,6 +273,19 @@ def test_control_init_and_ctl_calls_reject_bad_arguments():
     assert out_ctl(st, (st[1],) + other[1:]) == zs.ZERO_EINVAL               # copies overlap
     assert out_ctl(st, (other[0] + 4,) + other[1:]) == zs.ZERO_EALIGN
     assert out_ctl(st, other[:3] + (A,)) == zs.ZERO_EINVAL                   # over the chunk
+    # the bucket table under the block must tile the state exactly
+    table = (zs.BucketSliceC * 2)()
+    keep = [_ptrs(A), _ptrs(A + 65536)]
+    for k, (nn, off) in enumerate(((504, 0), (496, 504))):
+        table[k].grad_chunks = ctypes.cast(keep[k], ctypes.POINTER(ctypes.c_void_p))
+        table[k].n, table[k].offset = nn, off
+    bctl = lambda count, n_state: zs.lib.zero_shard_step_buckets_ctl(
+        table, count, 1, n_state, *[_ptrs(st[j], other[j]) for j in range(4)],
+        ctypes.byref(_hp()), A, None)
+    assert bctl(1, n) == zs.ZERO_EINVAL                                     # a gap at the end
+    assert "cover" in _last()
+    table[1].offset = 512
+    assert bctl(2, 1008) == zs.ZERO_EINVAL                                   # a gap between
 
 
 def _flatten(ptrs, numels, align, pad, bucket, cap):

@@ -223,3 +223,52 @@ def test_graph_of_one_step_replays_like_eager_calls():
         for cp_g, cp_e in zip(g_copies, e_copies):
             for x, y in zip(cp_g, cp_e):
                 assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+def test_bucket_table_single_pass_matches_oracle():
+    """ZeRO-2 slices (ragged, tiling the shard) stepped by one call per step
+    under the control block: the skip decision covers every slice, and the
+    committed copy is the oracle's step of the whole shard."""
+    dev = device()
+    w = _workload()
+    sizes = [8 * s for s in (1, 511, 512, 513, 2048, 1, 7, 1000)]
+    sizes.append(n // 8 * 8 - sum(sizes))
+    assert sizes[-1] > 0
+    nn = sum(sizes)
+    h = wl.host_shard(w, n=nn, offset_seed=906)
+    a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+    b = tuple(torch.full_like(x, float("nan")) for x in a)
+    copies = (a, b)
+    scaler, os_ = _scaler()
+    ctl = zs.control_new(scaler, w.hyper.step, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+    full = [torch.empty(nn, dtype=torch.float16, device=dev) for _ in range(N)]
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int)
+    table = zs.BucketSlices([([f[o:o + s] for f in full], int(o)) for o, s in zip(offs, sizes)])
+    state, t, cur = (h["master"], h["m"], h["v"], h["p16"]), w.hyper.step, 0
+    for k, plant in enumerate(PLAN):
+        S = os_.scale
+        g = [wl.host_fp16_grad(wl.seed_of(w.wid, 950 + k, i), nn, w.grad_sigma, S)
+             for i in range(N)]
+        if plant:
+            g[k % N][int(offs[-1]) + 5] = np.float16(np.nan)    # in the last slice only
+        for f, src in zip(full, g):
+            f.copy_(torch.from_numpy(src))
+        stepper.single_pass_buckets(table, copies)
+        want = ozs.shard_step(g, *state, w.hyper.replace(step=t), S)
+        skip = ols.update_loss_scale(os_, want.overflow)
+        t += 0 if skip else 1
+        c = zs.control_read(ctl)
+        print(f"case: ctl bucket table step {k} plant={plant} S={S}", flush=True)
+        _check_control(c, os_, t, skip, want)
+        if skip:
+            assert c.cur == cur
+            continue
+        cur = 1 - cur
+        assert c.cur == cur
+        got = dict(zip(("master", "m", "v", "p16"), copies[cur]))
+        for name, ref in (("master", want.master), ("m", want.m), ("v", want.v)):
+            assert np.array_equal(got[name].cpu().numpy().view(np.uint32),
+                                  ref.view(np.uint32)), (k, name)
+        assert np.array_equal(got["p16"].cpu().numpy().view(np.uint16), want.p16.view(np.uint16))
+        state = (want.master, want.m, want.v, want.p16)
