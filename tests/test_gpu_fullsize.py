@@ -4,7 +4,8 @@ with the CPU oracle element by element wherever the oracle can follow in
 seconds on the host's cores, and by properties that hold at any size
 elsewhere.
 
-* Llama-3-8B shard (1,003,750,000 params, N = 8): every element, both paths.
+* Llama-3-8B shard (1,003,750,000 params, N = 8): every element, for the
+  device-controlled single pass and for the two-pass step.
 * Overflow (125,468,750 params, 100,375 injected inf/NaN): the step is
   skipped, the scale halves, the state stays bit-identical; then a clean
   step at the halved scale matches the oracle everywhere.
@@ -66,23 +67,28 @@ def _assert_writeback_property(master, p16, label, piece=1 << 24):
 
 
 def test_llama3_8b_shard_full():
+    """The step bench.py times (single pass under the device control block)
+    against the oracle at every element; then the two-pass check-then-step
+    on the same inputs against the same expected state."""
     dev = device()
     w = wl.LLAMA3_8B_SHARD
     print(f"case: full {w.name} n={w.n} N={w.n_replicas}", flush=True)
     d = wl.device_shard(w, dev)
     cur = (d["master"], d["m"], d["v"], d["p16"])
     out = tuple(torch.empty_like(t) for t in cur)
-    hp = zs.adamw_params(w.hyper)
-    fl, sq = flags(dev)
-    zs.zero_shard_step_out(d["chunks"], w.loss_scale, *cur[:3], *out, hp, fl, sq)
-    torch.cuda.synchronize()
-    print("case: full llama3_8b_shard, single-pass step vs oracle", flush=True)
+    ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+    zs.DeviceStepper(ctl, zs.adamw_params(w.hyper)).single_pass(d["chunks"], (cur, out))
+    c = zs.control_read(ctl)
+    assert c.error == 0 and c.overflow == 0 and c.skip == 0 and c.cur == 1
+    assert c.step == w.hyper.step + 1 and c.scale == w.loss_scale
+    print("case: full llama3_8b_shard, device-controlled single pass vs oracle", flush=True)
     overflow, want_sq, expected = compare_with_oracle(d["chunks"], cur, out, w.hyper,
                                                       w.loss_scale, label="single-pass ",
                                                       keep_expected=True)
-    assert not overflow and int(fl.item()) == 0
-    assert rel_close(float(sq.item()), want_sq), (float(sq.item()), want_sq)
+    assert not overflow
+    assert rel_close(c.sqnorm, want_sq), (c.sqnorm, want_sq)
     del out
+    hp = zs.adamw_params(w.hyper)
     fl2, sq2 = flags(dev)
     zs.zero_overflow_check(d["chunks"], w.loss_scale, fl2, sq2)
     zs.zero_shard_step(d["chunks"], w.loss_scale, *cur, hp)
@@ -198,13 +204,22 @@ def test_zero2_bucketed_full():
         assert np.array_equal(out[3][a:a + n].cpu().numpy().view(np.uint16),
                               want.p16.view(np.uint16))
     _assert_writeback_property(out[0], out[3], "zero2")
-    # the same update as 160 separate calls
+    # the same update as 160 separate calls, and as the whole step under the
+    # device control block (what bench.py --workload zero2_bucketed times)
     ref = tuple(torch.empty_like(t) for t in cur)
     for a, n in offsets:
         zs.zero_shard_step_out([o[a:a + n] for o in owned], S, *(t[a:a + n] for t in cur[:3]),
                                *(t[a:a + n] for t in ref), hp)
     torch.cuda.synchronize()
     for x, y in zip(out, ref):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    del ref
+    ctl = zs.control_new(zs.LossScaler.create(scale=S), w.hyper.step, dev)
+    dst = tuple(torch.empty_like(t) for t in cur)
+    zs.DeviceStepper(ctl, hp).single_pass_buckets(table, (cur, dst))
+    c = zs.control_read(ctl)
+    assert c.error == 0 and c.skip == 0 and c.cur == 1 and c.step == w.hyper.step + 1
+    for x, y in zip(out, dst):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
