@@ -571,6 +571,30 @@ class DeviceStepper:
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
 
+    def single_pass_streamed(self, arrivals, copies, stream=None) -> None:
+        """single_pass over a shard whose gradients arrive bucket by bucket.
+        `arrivals` yields (grad_chunks, offset) in arrival order; each bucket
+        is updated as it is yielded, from copy cur into the other at state
+        elements [offset, offset + len(chunk)), and the decision and commit
+        follow the last.  The generator may refill a chunk buffer once the
+        update that read it has been enqueued on the same stream.  The
+        buckets must cover the state arrays exactly once."""
+        self._rebase()
+        n = copies[0][0].numel()
+        covered = 0
+        zero_control_begin(self.ctl, stream=stream)
+        for chunks, off in arrivals:
+            nb = chunks[0].numel()
+            if off < 0 or off + nb > n:
+                raise ValueError(f"bucket at {off} of {nb} elements lies outside the {n}-element state")
+            view = tuple(tuple(t[off:off + nb] for t in cp) for cp in copies)
+            zero_shard_step_out_ctl(chunks, view, self.hp, self.ctl, stream=stream)
+            covered += nb
+        if covered != n:
+            raise ValueError(f"the buckets cover {covered} elements of a {n}-element state")
+        zero_control_decide(self.ctl, 0.0, True, stream=stream)
+        self.since_base += 1
+
 
 # ---------------------------------------------------------------------------
 # Checkpoint and resume: the shard's state is its four arrays plus the step

@@ -2,7 +2,8 @@
 enqueued with no read-back (two-pass with and without gradient-norm
 clipping, and single pass with the commit on the device) walk the same
 states as the oracle's step, loss scaler and t over clean and overflowing
-steps; a stale bias-correction table is refused on the device; and a HIP
+steps (whole shard, a bucket table, and buckets streamed as they arrive); a
+stale bias-correction table is refused on the device; and a HIP
 graph of one step replays like the eager calls."""
 import numpy as np
 import pytest
@@ -272,3 +273,81 @@ def test_bucket_table_single_pass_matches_oracle():
                                   ref.view(np.uint32)), (k, name)
         assert np.array_equal(got["p16"].cpu().numpy().view(np.uint16), want.p16.view(np.uint16))
         state = (want.master, want.m, want.v, want.p16)
+
+
+def test_streamed_buckets_single_pass_matches_oracle():
+    """Buckets arriving one at a time through two reused chunk buffers (the
+    last one ragged), each updated as it arrives, one decision per step: the
+    same states as the oracle's step of the whole shard, with an overflow in
+    any one bucket skipping the whole step."""
+    dev = device()
+    w = _workload()
+    sizes = [8 * s for s in (1, 511, 512, 513, 2048, 7)]
+    sizes.append(n - sum(sizes))
+    assert sizes[-1] % 8 != 0
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int)
+    h = wl.host_shard(w, n=n, offset_seed=907)
+    a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+    b = tuple(torch.full_like(x, float("nan")) for x in a)
+    copies = (a, b)
+    scaler, os_ = _scaler()
+    ctl = zs.control_new(scaler, w.hyper.step, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+    bufs = [[torch.empty(max(sizes), dtype=torch.float16, device=dev) for _ in range(N)]
+            for _ in range(2)]
+    state, t, cur = (h["master"], h["m"], h["v"], h["p16"]), w.hyper.step, 0
+    for k, plant in enumerate(PLAN):
+        S = os_.scale
+        g = [wl.host_fp16_grad(wl.seed_of(w.wid, 960 + k, i), n, w.grad_sigma, S)
+             for i in range(N)]
+        if plant:
+            g[k % N][int(offs[3]) + 17] = np.float16(-np.inf)    # in bucket 3 only
+
+        def arrivals():
+            for j, (o, s) in enumerate(zip(offs, sizes)):
+                chunks = [buf[:s] for buf in bufs[j % 2]]
+                for c, src in zip(chunks, g):
+                    c.copy_(torch.from_numpy(src[o:o + s]))
+                yield chunks, int(o)
+
+        stepper.single_pass_streamed(arrivals(), copies)
+        want = ozs.shard_step(g, *state, w.hyper.replace(step=t), S)
+        skip = ols.update_loss_scale(os_, want.overflow)
+        t += 0 if skip else 1
+        c = zs.control_read(ctl)
+        print(f"case: ctl streamed buckets step {k} plant={plant} S={S}", flush=True)
+        _check_control(c, os_, t, skip, want)
+        if skip:
+            assert c.cur == cur
+            continue
+        cur = 1 - cur
+        assert c.cur == cur
+        got = dict(zip(("master", "m", "v", "p16"), copies[cur]))
+        for name, ref in (("master", want.master), ("m", want.m), ("v", want.v)):
+            assert np.array_equal(got[name].cpu().numpy().view(np.uint32),
+                                  ref.view(np.uint32)), (k, name)
+        assert np.array_equal(got["p16"].cpu().numpy().view(np.uint16), want.p16.view(np.uint16))
+        state = (want.master, want.m, want.v, want.p16)
+
+
+def test_streamed_buckets_that_miss_the_state_commit_nothing():
+    """Buckets that do not cover the state raise before the decision: the
+    control block's t and current copy stay where they were."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=908)
+    a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+    b = tuple(torch.empty_like(x) for x in a)
+    ctl = zs.control_new(_scaler()[0], w.hyper.step, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    half = [c[:8 * 2500] for c in chunks]
+    with pytest.raises(ValueError, match="cover"):
+        stepper.single_pass_streamed(iter([(half, 0)]), (a, b))
+    with pytest.raises(ValueError, match="outside"):
+        stepper.single_pass_streamed(iter([(chunks, 8)]), (a, b))
+    c = zs.control_read(ctl)
+    assert c.cur == 0 and c.step == w.hyper.step and c.error == 0
+    for x, k in zip(a, ("master", "m", "v", "p16")):
+        bits = np.uint16 if h[k].dtype == np.float16 else np.uint32
+        assert np.array_equal(x.cpu().numpy().view(bits), h[k].view(bits))

@@ -227,6 +227,9 @@ LLAMA70B_SAMPLED = (0, 11, 22)
 
 
 def test_llama70b_shard_streamed():
+    """The launch sequence bench.py times for this shard: one step under the
+    device control block, each bucket updated as it arrives in one of two
+    chunk buffers (the other refilled meanwhile), one decision at the end."""
     dev = device()
     w = wl.LLAMA70B_SHARD
     N, S = w.n_replicas, w.loss_scale
@@ -238,24 +241,34 @@ def test_llama70b_shard_streamed():
     bmax = max(w.buckets)
     bufs = [[torch.empty(bmax, dtype=torch.float16, device=dev) for _ in range(N)]
             for _ in range(2)]
-    hp = zs.adamw_params(w.hyper)
-    fl, sq = flags(dev)
-    off = 0
-    for b, nb in enumerate(w.buckets):
-        chunks = [c[:nb] for c in bufs[b % 2]]
-        wl.device_chunks(w, dev, n=nb, offset_seed=100 + b, out=chunks)
-        s_in = tuple(t[off:off + nb] for t in cur)
-        s_out = tuple(t[off:off + nb] for t in out)
-        zs.zero_shard_step_out(chunks, S, *s_in[:3], *s_out, hp, fl, sq)
-        if b in LLAMA70B_SAMPLED:
-            fb, sb = flags(dev)
-            zs.zero_overflow_check(chunks, S, fb, sb)
-            torch.cuda.synchronize()
-            print(f"case: llama70b bucket {b} (n={nb}) step vs oracle", flush=True)
-            overflow, want_sq, _ = compare_with_oracle(chunks, s_in, s_out, w.hyper, S,
-                                                       label=f"bucket {b} ")
-            assert not overflow and int(fb.item()) == 0 and rel_close(float(sb.item()), want_sq)
-        off += nb
-    torch.cuda.synchronize()
-    assert int(fl.item()) == 0
+    ctl = zs.control_new(zs.LossScaler.create(scale=S), w.hyper.step, dev)
+    checked = []
+
+    def arrivals():
+        off = 0
+        for b, nb in enumerate(w.buckets):
+            chunks = [c[:nb] for c in bufs[b % 2]]
+            wl.device_chunks(w, dev, n=nb, offset_seed=100 + b, out=chunks)
+            yield chunks, off
+            # bucket b's update is enqueued; check the sampled ones now,
+            # before their buffer is refilled
+            if b in LLAMA70B_SAMPLED:
+                torch.cuda.synchronize()
+                print(f"case: llama70b bucket {b} (n={nb}) step vs oracle", flush=True)
+                s_in = tuple(t[off:off + nb] for t in cur)
+                s_out = tuple(t[off:off + nb] for t in out)
+                overflow, want_sq, _ = compare_with_oracle(chunks, s_in, s_out, w.hyper, S,
+                                                           label=f"bucket {b} ")
+                fb, sb = flags(dev)
+                zs.zero_overflow_check(chunks, S, fb, sb)
+                assert not overflow and int(fb.item()) == 0
+                assert rel_close(float(sb.item()), want_sq)
+                checked.append(b)
+            off += nb
+
+    zs.DeviceStepper(ctl, zs.adamw_params(w.hyper)).single_pass_streamed(arrivals(), (cur, out))
+    c = zs.control_read(ctl)
+    assert checked == list(LLAMA70B_SAMPLED)
+    assert c.error == 0 and c.overflow == 0 and c.skip == 0 and c.cur == 1
+    assert c.step == w.hyper.step + 1 and c.scale == S and c.sqnorm > 0.0
     _assert_writeback_property(out[0], out[3], "llama70b")
