@@ -141,6 +141,8 @@ def main():
         return bench_zero2(args, dev)
     if args.workload == "llama70b_shard":
         return bench_streamed(args, dev)
+    if args.workload == "overflow":
+        return bench_overflow(args, dev)
     w = wl.WORKLOADS[args.workload]
     n, N = w.n, w.n_replicas
     log(f"bench: workload={w.name} n={n} N={N} steps={args.steps} warmup={args.warmup}")
@@ -486,6 +488,146 @@ def bench_streamed(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_overflow(args, dev):
+    """Overflow workload (125,468,750 params, N = 8, S = 65536, 100,375 of
+    the N * n gradient entries set to +inf, -inf, NaN).  Times, per step:
+    the device-controlled single pass over the overflowing gradients (the
+    update is written to the spare copy and not committed: skip, scale
+    backs off); the device-controlled two-pass form over the same gradients
+    (check, decide; the update kernel sees the skip and returns at once);
+    and, after the gradients are drawn again clean at the halved scale
+    32768, the clean single pass.  Asserts that the skipped steps leave t,
+    the current copy and the state bit-identical.  Prints one JSON line."""
+    import torch
+
+    import sharded_mixed_precision_step_amd as zs
+    import workloads as wl
+
+    w = wl.OVERFLOW
+    n, N = w.n, w.n_replicas
+    stream = torch.cuda.current_stream()
+    log(f"bench: workload={w.name} n={n} N={N} injected={w.n_inject} "
+        f"steps={args.steps} warmup={args.warmup}")
+    d = wl.device_shard(w, dev)
+    wl.device_inject(d["chunks"], wl.injection_sites(w))
+    cur = (d["master"], d["m"], d["v"], d["p16"])
+    spare = tuple(torch.empty_like(t) for t in cur)
+    before = [t.clone() for t in cur]
+    hp = zs.adamw_params(w.hyper)
+    torch.cuda.synchronize()
+
+    def timed_single(ctl, steps, events):
+        for k in range(steps):
+            zs.zero_control_begin(ctl, stream=stream)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            zs.zero_shard_step_out_ctl(d["chunks"], (cur, spare), hp, ctl, stream=stream)
+            e[1].record(stream)
+            zs.zero_control_decide(ctl, 0.0, True, stream=stream)
+            if events is not None:
+                events.append(e)
+
+    def run(fn, ctl):
+        ev = []
+        fn(ctl, args.warmup, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn(ctl, args.steps, ev)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        return ms, sum(a.elapsed_time(b) for a, b in ev) / max(len(ev), 1)
+
+    def timed_two_pass(ctl, steps, events):
+        for k in range(steps):
+            zs.zero_control_begin(ctl, stream=stream)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            zs.zero_overflow_check_ctl(d["chunks"], ctl, stream=stream)
+            e[1].record(stream)
+            zs.zero_control_decide(ctl, 0.0, False, stream=stream)
+            zs.zero_shard_step_ctl(d["chunks"], *cur, hp, ctl, stream=stream)
+            if events is not None:
+                events.append(e)
+
+    # every step is skipped; the scale backs off to min_scale (1) and stays
+    scaler = zs.LossScaler.create(scale=w.loss_scale)
+    ctl = zs.control_new(scaler, w.hyper.step, dev)
+    skip_ms, skip_upd_ms = run(timed_single, ctl)
+    c = zs.control_read(ctl)
+    total = args.warmup + args.steps
+    assert c.skipped_steps == total and c.step == w.hyper.step and c.cur == 0 and c.error == 0
+    ctl2 = zs.control_new(scaler, w.hyper.step, dev)
+    two_ms, check_ms = run(timed_two_pass, ctl2)
+    c2 = zs.control_read(ctl2)
+    assert c2.skipped_steps == total and c2.step == w.hyper.step and c2.error == 0
+    for a, b in zip(before, cur):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "a skipped step wrote"
+    del before
+    # the retry: clean gradients at the halved scale, one clean step each
+    S2 = w.loss_scale * 0.5
+    wl.device_chunks(w, dev, loss_scale=S2, out=d["chunks"])
+    ctl3 = zs.control_new(zs.LossScaler.create(scale=S2), w.hyper.step, dev)
+
+    stepper3 = zs.DeviceStepper(ctl3, hp)
+
+    def timed_clean(ctl, steps, events):
+        for k in range(steps):
+            stepper3._rebase()
+            zs.zero_control_begin(ctl, stream=stream)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            zs.zero_shard_step_out_ctl(d["chunks"], (cur, spare), stepper3.hp, ctl,
+                                       stream=stream)
+            e[1].record(stream)
+            zs.zero_control_decide(ctl, 0.0, True, stream=stream)
+            stepper3.since_base += 1
+            if events is not None:
+                events.append(e)
+
+    clean_ms, clean_upd_ms = run(timed_clean, ctl3)
+    c3 = zs.control_read(ctl3)
+    assert c3.skipped_steps == 0 and c3.error == 0 and c3.step == w.hyper.step + total
+    step_bytes = w.bytes_per_param_step() * n
+    check_bytes = 2 * N * n
+    upd_gbps = step_bytes / (skip_upd_ms * 1e-3) / 1e9
+    log(f"bench: overflowing single pass {skip_ms:.3f} ms/step (update {skip_upd_ms:.3f} ms), "
+        f"two-pass {two_ms:.3f} ms/step (check {check_ms:.3f} ms), clean retry "
+        f"{clean_ms:.3f} ms/step")
+    out = {
+        "metric": METRIC,
+        "value": n / (skip_ms * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": skip_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded device draws; fp16 grads with injected inf/NaN, fp32 state)",
+        "config": {"workload": w.name, "shard_params": n, "replicas": N,
+                   "injected": w.n_inject, "loss_scale": w.loss_scale,
+                   "adam_step": w.hyper.step,
+                   "bytes_per_param_fused_step": w.bytes_per_param_step()},
+        "roofline": {"bound": "hbm", "achieved": upd_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": upd_gbps / HBM_PEAK_GBPS, "traffic": None},
+        "cpu_baseline": None,
+        "extra": {
+            "path": "device single pass over overflowing gradients: the update goes to the "
+                    "spare copy, the decision skips it and backs the scale off",
+            "skipped_single_pass_ms": skip_ms, "skipped_update_ms": skip_upd_ms,
+            "skipped_update_gbps": upd_gbps,
+            "skipped_two_pass_ms": two_ms, "check_ms": check_ms,
+            "check_gbps": check_bytes / (check_ms * 1e-3) / 1e9,
+            "clean_retry_single_pass_ms": clean_ms, "clean_retry_update_ms": clean_upd_ms,
+            "clean_retry_update_gbps": step_bytes / (clean_upd_ms * 1e-3) / 1e9,
+            "final_scale_after_skips": c.scale,
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline_buckets(w, items, state, sampled):
     """The CPU oracle as it stands on whole buckets of a streamed shard (host
     copies of their device chunks and state slices), in 2^22-param slices
@@ -544,7 +686,8 @@ def host_single_pass(zs, d, shard, scaler, hp, flag, sq, stream, steps: int, n: 
 def tiny_graph(dev, steps: int = 200):
     """The tiny workload (1,000,003 params, N = 3), launch-bound: one
     device-controlled single-pass step as eager launches versus the same step
-    captured once in a HIP graph and replayed."""
+    captured once in a HIP graph and replayed; and the fused update alone,
+    warm in the MALL and flushed from it (medians of HIP-event timings)."""
     import torch
 
     import sharded_mixed_precision_step_amd as zs
@@ -583,8 +726,38 @@ def tiny_graph(dev, steps: int = 200):
     torch.cuda.synchronize()
     graph_us = (time.perf_counter() - t0) * 1e6 / reps
     assert zs.control_read(ctl).error == 0
+    # The fused update alone, timed with HIP events: warm (its 32 MB of
+    # inputs are in the 256 MB MALL from the step before) and flushed (a
+    # 1 GiB fill between steps, outside the events, evicts them).  Warm and
+    # flushed steps alternate.
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    ctl, st = fresh()
+    stream = torch.cuda.current_stream()
+    times = {False: [], True: []}
+    for k in range(2 * reps + 4):
+        flushed = k % 2 == 1
+        if flushed:
+            flush.fill_(float(k))
+        st._rebase()
+        zs.zero_control_begin(ctl, stream=stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        zs.zero_shard_step_out_ctl(d["chunks"], copies, st.hp, ctl, stream=stream)
+        e[1].record(stream)
+        zs.zero_control_decide(ctl, 0.0, True, stream=stream)
+        st.since_base += 1
+        if k >= 4:
+            times[flushed].append(e)
+    torch.cuda.synchronize()
+    assert zs.control_read(ctl).error == 0
+    med = {f: sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2] * 1e3
+           for f, ev in times.items()}
+    step_bytes = w.bytes_per_param_step() * w.n
     return {"tiny_eager_us_per_step": eager_us, "tiny_graph_us_per_step": graph_us,
-            "tiny_graph_params_per_s": w.n / (graph_us * 1e-6)}
+            "tiny_graph_params_per_s": w.n / (graph_us * 1e-6),
+            "tiny_update_warm_us": med[False], "tiny_update_flushed_us": med[True],
+            "tiny_update_warm_gbps": step_bytes / (med[False] * 1e-6) / 1e9,
+            "tiny_update_flushed_gbps": step_bytes / (med[True] * 1e-6) / 1e9}
 
 
 def two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
