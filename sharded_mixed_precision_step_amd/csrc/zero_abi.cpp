@@ -486,6 +486,9 @@ int zero_reduce_mean_fp16(const void* const* grad_chunks, int32_t n_chunks, int6
     if (rc) return rc;
     if ((rc = check_flag_ptrs(d_overflow, d_sqnorm))) return rc;
     if (n == 0) return ok();
+    if (zero::mean_tiles(n) > zero::kMaxGridBlocks)
+        return fail(ZERO_EINVAL, "%s: n = %lld is longer than one launch covers", who,
+                    static_cast<long long>(n));
     if (!mean_fp16) return fail(ZERO_EINVAL, "%s: mean_fp16 is NULL", who);
     if (!aligned(mean_fp16, 16)) return fail(ZERO_EALIGN, "%s: mean_fp16 is not 16-byte aligned", who);
     for (int32_t c = 0; c < n_chunks; ++c)

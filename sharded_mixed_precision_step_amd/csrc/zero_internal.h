@@ -14,6 +14,8 @@ constexpr int kPack = 8;           // params per 16-byte fp16 vector ("pack")
 constexpr int kWaveSpan = 2;       // packs per lane in a step tile
 constexpr int kTilePacks = kBlock * kWaveSpan;  // packs per step tile (one block)
 constexpr int kCheckBlocksPerCU = 6;            // resident blocks of the check kernel
+constexpr int kMeanSpan = 4;       // packs per lane in an fp16-mean tile
+constexpr int kMeanTilePacks = kBlock * kMeanSpan;  // packs per fp16-mean tile (one block)
 constexpr int kFlattenBatch = 32;  // tensors per flatten launch (kernel-argument table)
 constexpr int kFlattenSpan = 4;    // packs per lane in a flatten tile
 constexpr int64_t kFlattenTile = static_cast<int64_t>(kBlock) * kFlattenSpan * kPack;  // elements
@@ -121,6 +123,7 @@ hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScal
                               double* d_sqnorm, hipStream_t stream);
 
 int64_t step_tiles(int64_t n);  // blocks of the fused step over n params
+int64_t mean_tiles(int64_t n);  // blocks of the fp16 mean over n params
 
 hipError_t launch_ctl_step(const ChunkTable& chunks, int n_chunks, int64_t n,
                            const GradScalars& gs, const AdamScalars& as, const BiasTable& tab,

@@ -4,6 +4,7 @@
 //                          -> mean -> unscale -> (flag, sum g^2) -> Adam/AdamW
 //                          moments -> fp32 master -> fp16 params, in place.
 //   overflow_check_kernel  the same front half, reductions only.
+//   reduce_mean_kernel     the replica mean stored as fp16 (page-literal split).
 //   bucket_flatten_kernel  whole tensors into 256-aligned, zero-padded slots.
 //
 // The update order is that of the ZeRO-1 update step of the ZeRO notes
@@ -446,47 +447,51 @@ __global__ void control_decide_kernel(zero_step_control* c, float max_norm, int 
 
 // The owner's gradient mean stored as fp16 (the page-literal split): mean16 =
 // fp16(sum / N), rounded to nearest even; with REDUCE, the flag and squared
-// norm of g = fp32(mean16) / S.  Read-heavy (N chunks in, one fp16 array out)
-// and reduced per block, so it runs the check's resident grid-stride loop.
+// norm of g = fp32(mean16) / S.  One-shot tiles of kMeanTilePacks packs; wave
+// w of a block sweeps the kMeanSpan * 64 consecutive packs from
+// w * kMeanSpan * 64, one pack per lane at a time, each read, reduced and
+// written before the next.  With an output stream beside the N chunk reads,
+// this shape sustains more bandwidth on MI355X than the check's resident
+// grid-stride loop.  The last block also handles the n % 8 params after the
+// last full pack.
+template <int NC, bool REDUCE>
+__device__ __forceinline__ uint16_t mean16_of(float s, const GradScalars& gs, bool& bad,
+                                              double& sq) {
+    const _Float16 h = static_cast<_Float16>(mean_of(s, gs));
+    if constexpr (REDUCE) {
+        const float g = unscaled(static_cast<float>(h), gs);
+        bad |= nonfinite(g);
+        sq += static_cast<double>(g) * static_cast<double>(g);
+    }
+    return __builtin_bit_cast(uint16_t, h);
+}
+
 template <int NC, bool REDUCE>
 __global__ __launch_bounds__(kBlock) void reduce_mean_kernel(
     ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs, uint16_t* __restrict__ mean16,
     int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm) {
     const int64_t packs = n / kPack;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    const int nc = NC > 0 ? NC : n_chunks;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t first =
+        static_cast<int64_t>(blockIdx.x) * kMeanTilePacks + wave * (kMeanSpan * 64) + lane;
     bool bad = false;
     double sq = 0.0;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < packs;
-         i += stride) {
-        f8 s = load_widen8_nt(chunks.p[0], i);
 #pragma unroll
-        for (int c = 1; c < nc; ++c) s += load_widen8_nt(chunks.p[c], i);
-        u16x8 out;
+    for (int u = 0; u < kMeanSpan; ++u) {
+        const int64_t i = first + u * 64;
+        if (i < packs) {
+            const f8 s = replica_sum8<NC>(chunks.p, n_chunks, i);
+            u16x8 out;
 #pragma unroll
-        for (int e = 0; e < kPack; ++e) {
-            const _Float16 h = static_cast<_Float16>(mean_of(s[e], gs));
-            out[e] = __builtin_bit_cast(uint16_t, h);
-            if constexpr (REDUCE) {
-                const float g = unscaled(static_cast<float>(h), gs);
-                bad |= nonfinite(g);
-                sq += static_cast<double>(g) * static_cast<double>(g);
-            }
+            for (int e = 0; e < kPack; ++e) out[e] = mean16_of<NC, REDUCE>(s[e], gs, bad, sq);
+            *reinterpret_cast<u16x8*>(mean16 + i * kPack) = out;
         }
-        *reinterpret_cast<u16x8*>(mean16 + i * kPack) = out;
     }
     if (blockIdx.x == gridDim.x - 1) {
         const int64_t j = packs * kPack + threadIdx.x;
-        if (j < n) {
-            const _Float16 h =
-                static_cast<_Float16>(mean_of(replica_sum1<NC>(chunks.p, n_chunks, j), gs));
-            mean16[j] = __builtin_bit_cast(uint16_t, h);
-            if constexpr (REDUCE) {
-                const float g = unscaled(static_cast<float>(h), gs);
-                bad |= nonfinite(g);
-                sq += static_cast<double>(g) * static_cast<double>(g);
-            }
-        }
+        if (j < n)
+            mean16[j] = mean16_of<NC, REDUCE>(replica_sum1<NC>(chunks.p, n_chunks, j), gs, bad, sq);
     }
     if constexpr (REDUCE) publish(bad, sq, d_overflow, d_sqnorm);
 }
@@ -675,7 +680,7 @@ template <int NC, bool REDUCE>
 hipError_t mean_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
                      uint16_t* mean16, int32_t* d_overflow, double* d_sqnorm,
                      hipStream_t stream) {
-    const int64_t grid = check_grid(n);
+    const int64_t grid = mean_tiles(n);
     hipLaunchKernelGGL((reduce_mean_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
                        dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, mean16, d_overflow,
                        d_sqnorm);
@@ -753,6 +758,11 @@ hipError_t launch_shard_step(const ChunkTable& chunks, int n_chunks, int64_t n,
 // (a shard shorter than one pack is all tail).
 int64_t step_tiles(int64_t n) {
     const int64_t tiles = (n / kPack + kTilePacks - 1) / kTilePacks;
+    return tiles < 1 ? 1 : tiles;
+}
+
+int64_t mean_tiles(int64_t n) {
+    const int64_t tiles = (n / kPack + kMeanTilePacks - 1) / kMeanTilePacks;
     return tiles < 1 ? 1 : tiles;
 }
 

@@ -68,6 +68,11 @@ int64_t step_tiles(int64_t n) {
     return t < 1 ? 1 : t;
 }
 
+int64_t mean_tiles(int64_t n) {
+    const int64_t t = (n / kPack + kMeanTilePacks - 1) / kMeanTilePacks;
+    return t < 1 ? 1 : t;
+}
+
 hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScalars&,
                               const AdamScalars&, const ShardState&, int32_t*, double*,
                               hipStream_t) {
@@ -344,6 +349,10 @@ static void launch_length_limits() {
                         nullptr, nullptr, nullptr);     // refused later, for overlapping arrays
     EXPECT(strstr(zero_last_error_string(), "longer than one launch") == nullptr);
     EXPECT(zero_accumulate_chunk(ch[0], too_long, 0, 2, st[0], nullptr, nullptr) == ZERO_EINVAL);
+    const int64_t mean_too_long = (zero::kMaxGridBlocks + 1) * zero::kMeanTilePacks * zero::kPack;
+    EXPECT(zero_reduce_mean_fp16(ch, 1, mean_too_long, 1.0f, st[0], nullptr, nullptr, nullptr) ==
+           ZERO_EINVAL);
+    EXPECT(strstr(zero_last_error_string(), "longer than one launch") != nullptr);
     zero_bucket_slice sl = {ch, too_long, 0};
     EXPECT(zero_shard_step_buckets(&sl, 1, 1, 1.0f, too_long, st[0], st[1], st[2], st[3], st[4],
                                    st[5], st[6], &p, nullptr, nullptr, nullptr) == ZERO_EINVAL);
