@@ -801,7 +801,8 @@ def two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
 def page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
     """The page-literal split on the same state, for comparison: the owner's
     gradient mean stored as fp16, then the single-pass update from it as a
-    one-chunk step (flag, read-back, loss scale, commit)."""
+    one-chunk step (flag, read-back, loss scale, commit).  Also the fp16 mean
+    built arrival by arrival (one zero_accumulate_chunk per replica chunk)."""
     import torch
     n, N = w.n, w.n_replicas
     mean16 = torch.empty(n, dtype=torch.float16, device=d["master"].device)
@@ -833,10 +834,34 @@ def page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
     ms = (time.perf_counter() - t0) * 1e3 / steps
     mean_ms = sum(a.elapsed_time(b) for a, b in ev_mean) / max(len(ev_mean), 1)
     step_ms = sum(a.elapsed_time(b) for a, b in ev_step) / max(len(ev_step), 1)
-    del mean16
-    return {"split_ms_per_step": ms, "split_params_per_s": n / (ms * 1e-3),
-            "mean_fp16_ms": mean_ms, "mean_fp16_gbps": (2 * N + 2) * n / (mean_ms * 1e-3) / 1e9,
-            "split_step_ms": step_ms, "split_step_gbps": 28 * n / (step_ms * 1e-3) / 1e9}
+    # the same fp16 mean built by folding the chunks in as they arrive: the
+    # first arrival writes the fp32 accumulator (2 + 4 B/param), the middle
+    # ones read and write it (2 + 4 + 4), the last writes the mean (2 + 4 + 2)
+    acc = torch.empty(n, dtype=torch.float32, device=mean16.device)
+    ev_acc = []
+    for k in range(steps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(N + 1)]
+        for i, c in enumerate(d["chunks"]):
+            e[i].record(stream)
+            zs.zero_accumulate_chunk(c, i, N, acc, mean16, stream=stream)
+        e[N].record(stream)
+        if k >= 1:
+            ev_acc.append(e)
+    torch.cuda.synchronize()
+    acc_ms = sum(e[0].elapsed_time(e[N]) for e in ev_acc) / len(ev_acc)
+    mid_ms = (sum(e[1].elapsed_time(e[N - 1]) for e in ev_acc) / len(ev_acc) / (N - 2)
+              if N > 2 else None)
+    acc_bytes = (6 + 10 * (N - 2) + 8) * n if N > 1 else 4 * n
+    del mean16, acc
+    out = {"split_ms_per_step": ms, "split_params_per_s": n / (ms * 1e-3),
+           "mean_fp16_ms": mean_ms, "mean_fp16_gbps": (2 * N + 2) * n / (mean_ms * 1e-3) / 1e9,
+           "split_step_ms": step_ms, "split_step_gbps": 28 * n / (step_ms * 1e-3) / 1e9,
+           "accumulate_all_ms": acc_ms,
+           "accumulate_all_gbps": acc_bytes / (acc_ms * 1e-3) / 1e9}
+    if mid_ms is not None:
+        out["accumulate_middle_ms"] = mid_ms
+        out["accumulate_middle_gbps"] = 10 * n / (mid_ms * 1e-3) / 1e9
+    return out
 
 
 def copy_ceiling(dev, stream, reps: int = 5):
