@@ -84,6 +84,12 @@ typedef struct zero_loss_scaler {
  * bytes, 8-byte aligned, fills a host copy with zero_control_init and copies
  * it to the device.  Calls that take it run on `stream` in order; calls on
  * one block must not overlap in time. */
+/* Partial sums of g^2 in a control block: the *_ctl kernels spread their
+ * per-block sums over ZERO_NORM_SLOTS slots, ZERO_NORM_STRIDE doubles (64
+ * bytes) apart, so that no single address takes one atomic add per block. */
+#define ZERO_NORM_SLOTS 16
+#define ZERO_NORM_STRIDE 8
+
 typedef struct zero_step_control {
     /* dynamic loss scale: the same state and rules as zero_loss_scaler */
     float scale;             /* S of the next step                              */
@@ -98,7 +104,8 @@ typedef struct zero_step_control {
     int64_t step;            /* t of the next applied update, >= 1               */
     /* the step in flight (zero_control_begin sets these) */
     int64_t step_used;       /* t this step's update uses                        */
-    double sqnorm;           /* sum of g^2 of this step                          */
+    double sqnorm;           /* sum of g^2 of this step, once decided: the sum
+                                of the slots in slot order                      */
     float scale_used;        /* S this step's gradients are unscaled by          */
     float clip_coef;         /* factor on g of this step's update (1: none)      */
     int32_t overflow;        /* non-finite flag of this step                     */
@@ -107,6 +114,11 @@ typedef struct zero_step_control {
                                 of bias corrections and nothing was updated;
                                 sticky until the host clears it                 */
     int32_t reserved;
+    /* this step's partial sums of g^2: block b of a *_ctl kernel adds its
+       sum into sqnorm_part[ZERO_NORM_STRIDE * (b % ZERO_NORM_SLOTS)];
+       zero_control_begin clears them, zero_control_decide folds them
+       into sqnorm; the other elements stay 0 */
+    double sqnorm_part[ZERO_NORM_SLOTS * ZERO_NORM_STRIDE];
 } zero_step_control;
 
 /*
@@ -361,14 +373,15 @@ int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_
  * scaler and the first update's t (>= 1); the in-flight fields are cleared,
  * cur = 0.  Returns ZERO_OK or ZERO_EINVAL.
  *
- * zero_control_begin: start a step: overflow = 0, sqnorm = 0, skip = 0,
- * clip_coef = 1, scale_used = scale, step_used = step.
+ * zero_control_begin: start a step: overflow = 0, sqnorm = 0 and its slots
+ * cleared, skip = 0, clip_coef = 1, scale_used = scale, step_used = step.
  *
  * zero_overflow_check_ctl: zero_overflow_check with S = d_ctl->scale_used,
- * accumulating into d_ctl->overflow and d_ctl->sqnorm.
+ * accumulating into d_ctl->overflow and the squared-norm slots.
  *
  * zero_control_decide: the decision, on the device, after the step's check
- * (two-pass) or fused update (single pass): skip = (overflow != 0); the
+ * (two-pass) or fused update (single pass): sqnorm = the sum of the slots
+ * (fp64, slot 0 first); skip = (overflow != 0); the
  * scale moves as zero_update_loss_scale moves it; on a clean step t advances
  * (step += 1), clip_coef = min(1, max_grad_norm / (sqrt(sqnorm) + 1e-6))
  * evaluated in fp64 and rounded to fp32 when max_grad_norm > 0 (else 1), and
@@ -383,7 +396,7 @@ int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_
  * copy cur into copy 1 - cur (masters[2], exp_avgs[2], exp_avg_sqs[2],
  * params_fp16[2]: HOST arrays of two DEVICE pointers each), with
  * S = scale_used and the bias corrections of t = step_used, accumulating the
- * flag and squared norm into d_ctl.  Follow it with zero_control_decide(...,
+ * flag and the squared-norm slots of d_ctl.  Follow it with zero_control_decide(...,
  * flip_copy = 1): a clean step then makes the written copy current.
  *
  * Bias corrections: hp->step is the base t0 of a table the call computes

@@ -37,6 +37,8 @@ EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
             "zero_shard_step_ctl", "zero_shard_step_out_ctl", "zero_shard_step_buckets_ctl",
             "zero_last_error_string")
 ZERO_CTL_STEPS = 64
+ZERO_NORM_SLOTS = 16
+ZERO_NORM_STRIDE = 8
 
 
 class ZeroStepError(RuntimeError):
@@ -75,7 +77,8 @@ class StepControl(ctypes.Structure):
                 ("step_used", ctypes.c_int64), ("sqnorm", ctypes.c_double),
                 ("scale_used", ctypes.c_float), ("clip_coef", ctypes.c_float),
                 ("overflow", ctypes.c_int32), ("skip", ctypes.c_int32),
-                ("error", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("error", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("sqnorm_part", ctypes.c_double * (ZERO_NORM_SLOTS * ZERO_NORM_STRIDE))]
 
 
 class BucketSliceC(ctypes.Structure):

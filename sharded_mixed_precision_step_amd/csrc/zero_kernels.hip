@@ -113,6 +113,13 @@ __device__ __forceinline__ void publish(bool bad, double sq, int32_t* d_overflow
     }
 }
 
+// The squared-norm slot of a control block that this block adds into: the
+// blocks of one launch spread over ZERO_NORM_SLOTS addresses 64 bytes apart,
+// so their fp64 atomics do not all queue on one address.
+__device__ __forceinline__ double* norm_slot(zero_step_control* ctl) {
+    return &ctl->sqnorm_part[ZERO_NORM_STRIDE * (blockIdx.x % ZERO_NORM_SLOTS)];
+}
+
 template <int NC>
 __device__ __forceinline__ float replica_sum1(const uint16_t* const* chunks, int n_chunks,
                                               int64_t j) {
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     if constexpr (CTL) {
         gs = with_scale(gs, ctl->scale_used);
         d_overflow = &ctl->overflow;
-        d_sqnorm = &ctl->sqnorm;
+        d_sqnorm = norm_slot(ctl);
     }
     const int64_t packs = n / kPack;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(kBlock) void ctl_step_kernel(ChunkTable chunks, int
     double sq = 0.0;
     step_block<NC, SINGLE, !SINGLE>(chunks.p, n_chunks, n, blockIdx.x, blockIdx.x == gridDim.x - 1,
                                     gs, as, st, bad, sq, SINGLE ? 1.0f : ctl->clip_coef);
-    if constexpr (SINGLE) publish(bad, sq, &ctl->overflow, &ctl->sqnorm);
+    if constexpr (SINGLE) publish(bad, sq, &ctl->overflow, norm_slot(ctl));
 }
 
 // The single-pass update over a bucket table under a control block: slice k
@@ -403,13 +410,14 @@ __global__ __launch_bounds__(kBlock) void bucket_ctl_step_kernel(BucketTable t, 
     double sq = 0.0;
     step_block<NC, true>(&t.chunk[k * n_chunks], n_chunks, t.n[k], b - t.tile_start[k],
                          b + 1 == t.tile_start[k + 1], gs, as, sk, bad, sq);
-    publish(bad, sq, &ctl->overflow, &ctl->sqnorm);
+    publish(bad, sq, &ctl->overflow, norm_slot(ctl));
 }
 
 // One thread: start a step.
 __global__ void control_begin_kernel(zero_step_control* c) {
     c->overflow = 0;
     c->sqnorm = 0.0;
+    for (int k = 0; k < ZERO_NORM_SLOTS; ++k) c->sqnorm_part[ZERO_NORM_STRIDE * k] = 0.0;
     c->skip = 0;
     c->clip_coef = 1.0f;
     c->scale_used = c->scale;
@@ -419,6 +427,9 @@ __global__ void control_begin_kernel(zero_step_control* c) {
 // One thread: the decision, the loss-scale move (the rules of the host's
 // zero_update_loss_scale, in fp32), the clip factor, t and the copy.
 __global__ void control_decide_kernel(zero_step_control* c, float max_norm, int flip) {
+    double sq = 0.0;
+    for (int k = 0; k < ZERO_NORM_SLOTS; ++k) sq += c->sqnorm_part[ZERO_NORM_STRIDE * k];
+    c->sqnorm = sq;
     const bool skip = c->overflow != 0;
     c->skip = skip ? 1 : 0;
     if (skip) {

@@ -337,3 +337,40 @@ def test_scaler_rejects(field, value):
     with pytest.raises(zs.ZeroStepError) as e:
         zs.zero_update_loss_scale(s, 1)
     assert e.value.code == zs.ZERO_EINVAL and bytes(s) == before
+
+
+def test_ctypes_structs_and_constants_match_the_header(tmp_path):
+    """The binding's ctypes structures have the C header's sizes and field
+    offsets, and its constants the header's values, as a C compiler sees
+    them."""
+    import subprocess
+    structs = {"zero_adamw_params": zs.AdamWParams, "zero_loss_scaler": zs.LossScaler,
+               "zero_bucket_slice": zs.BucketSliceC, "zero_step_control": zs.StepControl}
+    consts = ("ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ERANGE", "ZERO_EHIP",
+              "ZERO_MAX_CHUNKS", "ZERO_CTL_STEPS", "ZERO_NORM_SLOTS", "ZERO_NORM_STRIDE")
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "zero_step.h"',
+             "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    for c in consts:
+        lines.append(f'printf("const {c} %d\\n", (int)({c}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    seen = 0
+    for line in out.splitlines():
+        a, b, v = line.split()
+        if a == "const":
+            assert getattr(zs, b) == int(v), b
+        elif b == "sizeof":
+            assert ctypes.sizeof(structs[a]) == int(v), a
+        else:
+            assert getattr(structs[a], b).offset == int(v), (a, b)
+        seen += 1
+    assert seen == len(consts) + sum(1 + len(py._fields_) for py in structs.values())

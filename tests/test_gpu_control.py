@@ -213,11 +213,15 @@ def test_graph_of_one_step_replays_like_eager_calls():
         assert torch.isfinite(junk)
         gc, ec = zs.control_read(g_ctl), zs.control_read(e_ctl)
         print(f"case: graph replay {r}: t={gc.step} cur={gc.cur}", flush=True)
-        # every field equal, except the squared norm: its fp64 sum takes one
-        # atomic add per block, in whatever order the blocks finish
+        # every field equal, except the squared norm and its slots: each slot
+        # takes one fp64 atomic add per block, in whatever order the blocks
+        # finish
         for name, _ in zs.StepControl._fields_:
             if name == "sqnorm":
                 assert abs(gc.sqnorm - ec.sqnorm) <= 1e-12 * ec.sqnorm
+            elif name == "sqnorm_part":
+                for a, b in zip(gc.sqnorm_part, ec.sqnorm_part):
+                    assert abs(a - b) <= 1e-12 * abs(b)
             else:
                 assert getattr(gc, name) == getattr(ec, name), name
         assert gc.step == w.hyper.step + r + 1

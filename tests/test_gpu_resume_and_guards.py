@@ -98,6 +98,9 @@ def test_resume_from_checkpoint_is_bit_identical(tmp_path):
     for name, _ in zs.StepControl._fields_:
         if name == "sqnorm":
             assert abs(a.sqnorm - b.sqnorm) <= 1e-12 * a.sqnorm
+        elif name == "sqnorm_part":
+            for x, y in zip(a.sqnorm_part, b.sqnorm_part):
+                assert abs(x - y) <= 1e-12 * abs(y)
         else:
             assert getattr(a, name) == getattr(b, name), name
     # and the 2K steps are the oracle's 2K steps
