@@ -685,9 +685,11 @@ def host_single_pass(zs, d, shard, scaler, hp, flag, sq, stream, steps: int, n: 
 
 def tiny_graph(dev, steps: int = 200):
     """The tiny workload (1,000,003 params, N = 3), launch-bound: one
-    device-controlled single-pass step as eager launches versus the same step
-    captured once in a HIP graph and replayed; and the fused update alone,
-    warm in the MALL and flushed from it (medians of HIP-event timings)."""
+    device-controlled single-pass step as eager launches (arguments
+    marshalled once by DeviceStepper.prepare_single_pass, and per call by
+    DeviceStepper.single_pass) versus the same step captured once in a HIP
+    graph and replayed; and the fused update alone, warm in the MALL and
+    flushed from it (medians of HIP-event timings)."""
     import torch
 
     import sharded_mixed_precision_step_amd as zs
@@ -702,15 +704,22 @@ def tiny_graph(dev, steps: int = 200):
         ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
         return ctl, zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
 
-    ctl, st = fresh()
-    for _ in range(3):
-        st.single_pass(d["chunks"], copies)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        st.single_pass(d["chunks"], copies)
-    torch.cuda.synchronize()
-    eager_us = (time.perf_counter() - t0) * 1e6 / steps
+    def eager(prepared: bool) -> float:
+        ctl, st = fresh()
+        step = (st.prepare_single_pass(d["chunks"], copies) if prepared
+                else lambda: st.single_pass(d["chunks"], copies))
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        assert zs.control_read(ctl).error == 0
+        return (time.perf_counter() - t0) * 1e6 / steps
+
+    eager_us = eager(True)
+    unprepared_us = eager(False)
     ctl, st = fresh()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -753,7 +762,8 @@ def tiny_graph(dev, steps: int = 200):
     med = {f: sorted(a.elapsed_time(b) for a, b in ev)[len(ev) // 2] * 1e3
            for f, ev in times.items()}
     step_bytes = w.bytes_per_param_step() * w.n
-    return {"tiny_eager_us_per_step": eager_us, "tiny_graph_us_per_step": graph_us,
+    return {"tiny_eager_us_per_step": eager_us, "tiny_eager_unprepared_us_per_step": unprepared_us,
+            "tiny_graph_us_per_step": graph_us,
             "tiny_graph_params_per_s": w.n / (graph_us * 1e-6),
             "tiny_update_warm_us": med[False], "tiny_update_flushed_us": med[True],
             "tiny_update_warm_gbps": step_bytes / (med[False] * 1e-6) / 1e9,

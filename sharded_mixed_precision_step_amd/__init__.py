@@ -574,6 +574,12 @@ class DeviceStepper:
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
 
+    def prepare_single_pass(self, grad_chunks, copies, stream=None) -> "PreparedSinglePass":
+        """single_pass with its arguments marshalled once: for short steps,
+        where the per-call argument checks and pointer tables cost host time
+        comparable to the kernels.  See PreparedSinglePass."""
+        return PreparedSinglePass(self, grad_chunks, copies, stream)
+
     def single_pass_streamed(self, arrivals, copies, stream=None) -> None:
         """single_pass over a shard whose gradients arrive bucket by bucket.
         `arrivals` yields (grad_chunks, offset) in arrival order; each bucket
@@ -597,6 +603,43 @@ class DeviceStepper:
             raise ValueError(f"the buckets cover {covered} elements of a {n}-element state")
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
+
+
+class PreparedSinglePass:
+    """One device-controlled single-pass step (begin, fused update from copy
+    cur into the other, decide and commit) over fixed tensors, with the
+    dtype, device, layout and length checks done and the pointer tables built
+    once.  Each call then makes the three library calls, which still
+    validate their arguments.  The tensors are kept referenced; their storage
+    must not be resized or replaced while the object is in use."""
+
+    def __init__(self, stepper: DeviceStepper, grad_chunks, copies, stream=None):
+        n = copies[0][0].numel()
+        for k, cp in enumerate(copies):
+            for j, t in enumerate(cp):
+                if t.numel() != n:
+                    raise ValueError(f"copy {k} array {j} has {t.numel()} elements, expected {n}")
+        for i, c in enumerate(grad_chunks):
+            if c.numel() != n:
+                raise ValueError(f"grad_chunks[{i}] has {c.numel()} elements, expected {n}")
+        ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+        dts = (torch.float32, torch.float32, torch.float32, torch.float16)
+        tables = [_ptr_array([_dev(copies[k][j], dts[j], f"copy {k} array {j}")
+                              for k in range(2)]) for j in range(4)]
+        self.stepper = stepper
+        self._keep = (list(grad_chunks), [tuple(cp) for cp in copies])
+        self._ctl = _ctl(stepper.ctl)
+        self._stream = _stream(stream)
+        self._args = (_ptr_array(ptrs), len(ptrs), n, *tables, ctypes.byref(stepper.hp),
+                      self._ctl, self._stream)
+
+    def __call__(self) -> None:
+        st = self.stepper
+        st._rebase()
+        _check(lib.zero_control_begin(self._ctl, self._stream))
+        _check(lib.zero_shard_step_out_ctl(*self._args))
+        _check(lib.zero_control_decide(self._ctl, 0.0, 1, self._stream))
+        st.since_base += 1
 
 
 # ---------------------------------------------------------------------------

@@ -198,12 +198,38 @@ int check_ctl_ptr(const zero_step_control* d_ctl, const char* who) {
 }
 
 // The table of bias corrections for t = hp->step .. + ZERO_CTL_STEPS - 1.
+// Its 2 * ZERO_CTL_STEPS fp64 powers cost more host time than the rest of a
+// small step's call, and a caller stepping under a control block passes the
+// same base t0 for ZERO_CTL_STEPS calls in a row, so each thread keeps the
+// last table it built and reuses it while (beta1, beta2, t0, bias
+// correction) are unchanged (compared bit for bit).
 void bias_table(const zero_adamw_params* hp, zero::BiasTable* tab) {
-    tab->t0 = hp->step;
-    for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
-        tab->bc1[k] = hp->bias_correction ? bias_correction(hp->beta1, hp->step + k) : 1.0f;
-        tab->bc2[k] = hp->bias_correction ? bias_correction(hp->beta2, hp->step + k) : 1.0f;
+    struct Memo {
+        bool valid;
+        uint32_t beta1_bits, beta2_bits;
+        int64_t t0;
+        int32_t bias_correction;
+        zero::BiasTable table;
+    };
+    thread_local Memo memo = {};
+    uint32_t b1, b2;
+    memcpy(&b1, &hp->beta1, sizeof b1);
+    memcpy(&b2, &hp->beta2, sizeof b2);
+    const int32_t bc = hp->bias_correction ? 1 : 0;
+    if (!(memo.valid && memo.beta1_bits == b1 && memo.beta2_bits == b2 && memo.t0 == hp->step &&
+          memo.bias_correction == bc)) {
+        memo.table.t0 = hp->step;
+        for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
+            memo.table.bc1[k] = bc ? bias_correction(hp->beta1, hp->step + k) : 1.0f;
+            memo.table.bc2[k] = bc ? bias_correction(hp->beta2, hp->step + k) : 1.0f;
+        }
+        memo.beta1_bits = b1;
+        memo.beta2_bits = b2;
+        memo.t0 = hp->step;
+        memo.bias_correction = bc;
+        memo.valid = true;
     }
+    *tab = memo.table;
 }
 
 // Scalars and slices of a bucket-table call: every slice inside the state,

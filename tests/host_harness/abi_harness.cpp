@@ -262,13 +262,35 @@ static void bias_tables() {
     p.bias_correction = 0;
     EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
                                (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
-    EXPECT(g_bias.size() == 2);
-    EXPECT(g_bias[0].t0 == 1000 && g_bias[1].t0 == 1000);
-    for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
-        const double t = 1000.0 + k;
-        EXPECT(g_bias[0].bc1[k] == float(1.0 - pow(double(0.9f), t)));
-        EXPECT(g_bias[0].bc2[k] == float(1.0 - pow(double(0.999f), t)));
-        EXPECT(g_bias[1].bc1[k] == 1.0f && g_bias[1].bc2[k] == 1.0f);
+    // the per-thread table cache: back to the first key, then a new t0, then
+    // a new beta1 and a new beta2, each must give that key's own table
+    p.bias_correction = 1;
+    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
+                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    p.step = 1001;
+    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
+                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    p.beta1 = 0.8f;
+    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
+                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    p.beta2 = 0.99f;
+    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
+                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    EXPECT(g_bias.size() == 6);
+    EXPECT(g_bias[0].t0 == 1000 && g_bias[1].t0 == 1000 && g_bias[2].t0 == 1000);
+    EXPECT(g_bias[3].t0 == 1001 && g_bias[4].t0 == 1001 && g_bias[5].t0 == 1001);
+    const float b1[6] = {0.9f, 0.9f, 0.9f, 0.9f, 0.8f, 0.8f};
+    const float b2[6] = {0.999f, 0.999f, 0.999f, 0.999f, 0.999f, 0.99f};
+    for (int i = 0; i < 6; ++i) {
+        for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
+            const double t = double(g_bias[i].t0) + k;
+            if (i == 1) {
+                EXPECT(g_bias[i].bc1[k] == 1.0f && g_bias[i].bc2[k] == 1.0f);
+                continue;
+            }
+            EXPECT(g_bias[i].bc1[k] == float(1.0 - pow(double(b1[i]), t)));
+            EXPECT(g_bias[i].bc2[k] == float(1.0 - pow(double(b2[i]), t)));
+        }
     }
 }
 

@@ -355,3 +355,43 @@ def test_streamed_buckets_that_miss_the_state_commit_nothing():
     for x, k in zip(a, ("master", "m", "v", "p16")):
         bits = np.uint16 if h[k].dtype == np.float16 else np.uint32
         assert np.array_equal(x.cpu().numpy().view(bits), h[k].view(bits))
+
+
+def test_prepared_single_pass_equals_single_pass():
+    """The prepared step (arguments marshalled once) walks the same states as
+    DeviceStepper.single_pass over clean and overflowing steps, and past a
+    rebase of the bias-correction table."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=909)
+
+    def setup():
+        a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+        copies = (a, tuple(torch.empty_like(x) for x in a))
+        ctl = zs.control_new(_scaler()[0], w.hyper.step, dev)
+        return copies, ctl, zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+
+    pc, p_ctl, p_st = setup()
+    ec, e_ctl, e_st = setup()
+    chunks = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(N)]
+    step = p_st.prepare_single_pass(chunks, pc)
+    plan = PLAN + [False] * (zs.ZERO_CTL_STEPS + 3)        # runs past one rebase
+    for k, plant in enumerate(plan):
+        S = zs.control_read(e_ctl).scale
+        for c, src in zip(chunks, _grads(w, k % 50, S, plant)):
+            c.copy_(torch.from_numpy(src))
+        step()
+        e_st.single_pass(chunks, ec)
+        if k < len(PLAN) or k % 16 == 0 or k == len(plan) - 1:
+            a, b = zs.control_read(p_ctl), zs.control_read(e_ctl)
+            print(f"case: prepared single pass step {k} plant={plant}", flush=True)
+            for name in ("scale", "good_steps", "skipped_steps", "step", "cur", "skip",
+                         "overflow", "error"):
+                assert getattr(a, name) == getattr(b, name), (k, name)
+            if np.isfinite(b.sqnorm):
+                assert abs(a.sqnorm - b.sqnorm) <= 1e-12 * abs(b.sqnorm)
+            else:                   # an overflow step: inf or NaN on both sides
+                assert np.isnan(a.sqnorm) == np.isnan(b.sqnorm) and not np.isfinite(a.sqnorm)
+            for x, y in zip(pc[a.cur], ec[b.cur]):
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), k
+    assert zs.control_read(p_ctl).step > w.hyper.step + zs.ZERO_CTL_STEPS
