@@ -2,7 +2,8 @@
 enqueued with no read-back (two-pass with and without gradient-norm
 clipping, and single pass with the commit on the device) walk the same
 states as the oracle's step, loss scaler and t over clean and overflowing
-steps (whole shard, a bucket table, and buckets streamed as they arrive); a
+steps (whole shard, a bucket table, and buckets streamed as they arrive,
+at N = 1 .. 64); a
 stale bias-correction table is refused on the device; and a HIP
 graph of one step replays like the eager calls."""
 import numpy as np
@@ -395,3 +396,78 @@ def test_prepared_single_pass_equals_single_pass():
             for x, y in zip(pc[a.cur], ec[b.cur]):
                 assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), k
     assert zs.control_read(p_ctl).step > w.hyper.step + zs.ZERO_CTL_STEPS
+
+
+def _state(h, dev):
+    a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+    return a, tuple(torch.full_like(x, float("nan")) for x in a)
+
+
+def _assert_state(got, want, label):
+    for name, g, ref in zip(("master", "m", "v", "p16"), got,
+                            (want.master, want.m, want.v, want.p16)):
+        bits = np.uint16 if ref.dtype == np.float16 else np.uint32
+        assert np.array_equal(g.cpu().numpy().view(bits), ref.view(bits)), (label, name)
+
+
+@pytest.mark.parametrize("NN", [1, 2, 3, 16, 17, 64])
+def test_control_flows_at_any_replica_count(NN):
+    """Both device-controlled flows at N = 1 .. 64 (the unrolled and the
+    runtime-loop kernels), on a ragged shard, against the oracle: the single
+    pass, and the two-pass check, decision and in-place update."""
+    dev = device()
+    nn = 9_011
+    base = wl.LLAMA3_8B_SHARD
+    w = wl.ShardWorkload(name="ctl_n", wid=base.wid, n=nn, n_replicas=NN, grad_sigma=1e-4,
+                         loss_scale=1024.0, hyper=base.hyper.replace(step=5),
+                         m_sigma=1e-4, v_sigma=1e-8)
+    h = wl.host_shard(w, n=nn, offset_seed=910 + NN)
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    want = ozs.shard_step(h["chunks"], h["master"], h["m"], h["v"], h["p16"], w.hyper,
+                          w.loss_scale)
+    print(f"case: control flows N={NN} n={nn}", flush=True)
+    # single pass
+    copies = _state(h, dev)
+    ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+    zs.DeviceStepper(ctl, zs.adamw_params(w.hyper)).single_pass(chunks, copies)
+    c = zs.control_read(ctl)
+    assert c.cur == 1 and c.skip == 0 and c.overflow == 0 and c.error == 0
+    assert abs(c.sqnorm - want.sqnorm) <= 1e-6 * want.sqnorm
+    _assert_state(copies[1], want, f"single pass N={NN}")
+    # two-pass, in place
+    state, _ = _state(h, dev)
+    ctl2 = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+    zs.DeviceStepper(ctl2, zs.adamw_params(w.hyper)).two_pass(chunks, *state)
+    c2 = zs.control_read(ctl2)
+    assert c2.skip == 0 and c2.overflow == 0 and c2.error == 0 and c2.step == w.hyper.step + 1
+    assert abs(c2.sqnorm - want.sqnorm) <= 1e-6 * want.sqnorm
+    _assert_state(state, want, f"two-pass N={NN}")
+
+
+@pytest.mark.parametrize("NN", [1, 17, 64])
+def test_bucket_table_under_control_at_any_replica_count(NN):
+    """The bucket table under the control block at N = 1, 17 and 64: at
+    N = 64 the 9 slices take 3 launches (4 slices of 64 chunk pointers per
+    launch), all sharing one decision."""
+    dev = device()
+    sizes = [8 * s for s in (1, 511, 512, 513, 7, 64, 100, 3)]
+    sizes.append(4001)
+    nn = sum(sizes)
+    base = wl.LLAMA3_8B_SHARD
+    w = wl.ShardWorkload(name="ctl_b", wid=base.wid, n=nn, n_replicas=NN, grad_sigma=1e-4,
+                         loss_scale=65536.0, hyper=base.hyper.replace(step=9),
+                         m_sigma=1e-4, v_sigma=1e-8)
+    h = wl.host_shard(w, n=nn, offset_seed=930 + NN)
+    full = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int)
+    table = zs.BucketSlices([([f[o:o + s] for f in full], int(o)) for o, s in zip(offs, sizes)])
+    copies = _state(h, dev)
+    ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+    print(f"case: control bucket table N={NN} slices={len(sizes)}", flush=True)
+    zs.DeviceStepper(ctl, zs.adamw_params(w.hyper)).single_pass_buckets(table, copies)
+    want = ozs.shard_step(h["chunks"], h["master"], h["m"], h["v"], h["p16"], w.hyper,
+                          w.loss_scale)
+    c = zs.control_read(ctl)
+    assert c.cur == 1 and c.skip == 0 and c.overflow == 0 and c.error == 0
+    assert abs(c.sqnorm - want.sqnorm) <= 1e-6 * want.sqnorm
+    _assert_state(copies[1], want, f"bucket table N={NN}")
