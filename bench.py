@@ -189,7 +189,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    k1_ms = sum(a.elapsed_time(b) for a, b in fused_events) / max(len(fused_events), 1)
+    k1_times = sorted(a.elapsed_time(b) for a, b in fused_events)
+    k1_ms = sum(k1_times) / max(len(k1_times), 1)
+    k1_median_ms = k1_times[len(k1_times) // 2] if k1_times else float("nan")
     c = zs.control_read(ctl)
     if c.error:
         raise RuntimeError(f"step control reported error {c.error}")
@@ -219,6 +221,7 @@ def main():
                 "zero_shard_step_out_ctl (flag and squared norm), zero_control_decide "
                 "(skip, loss scale, t, commit); no read-back inside the loop",
         "fused_step_ms": k1_ms, "fused_step_params_per_s": n / (k1_ms * 1e-3),
+        "fused_step_median_ms": k1_median_ms,
         "fused_step_gbps": k1_gbps, "fused_step_pct_peak": 100 * k1_gbps / HBM_PEAK_GBPS,
         "step_gbps": k1_bytes / (ms_per_step * 1e-3) / 1e9,
         "skipped_steps": skipped,
@@ -230,6 +233,7 @@ def main():
     if not args.no_flatten:
         extra.update(bench_flatten(zs, wl, dev, stream))
     extra.update(copy_ceiling(dev, stream))
+    extra["fused_step_pct_copy_ceiling"] = 100 * k1_gbps / extra["copy_ceiling_gbps"]
     extra.update(tiny_graph(dev))
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
