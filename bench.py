@@ -236,12 +236,7 @@ def main():
     extra["fused_step_pct_copy_ceiling"] = 100 * k1_gbps / extra["copy_ceiling_gbps"]
     extra.update(tiny_graph(dev))
     if args.calibrate_copy:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(dev)
 
     out = {
         "metric": METRIC,
@@ -266,6 +261,18 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def calibration_copy(dev):
+    """Three plain 1 GiB fp32 copies (torch's elementwise dst = -src), whose
+    known bytes calibrate the rocprofv3 FETCH_SIZE and WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def _timed(fn, steps: int, warmup: int = 2):
@@ -489,6 +496,8 @@ def bench_streamed(args, dev):
             "skipped_steps": c.skipped_steps,
         },
     }
+    if args.calibrate_copy:
+        calibration_copy(dev)
     print(json.dumps(out), flush=True)
 
 
