@@ -1,10 +1,11 @@
 // Host-only harness of the C-ABI layer, built with g++ and AddressSanitizer
-// plus UndefinedBehaviorSanitizer (tests/test_host_sanitizers.py).  The
-// device side is replaced by stubs that record what each launch would
-// receive, so the validation paths and the launch tables (bucket batching,
-// flatten batching, bias tables, accumulate modes) run under the sanitizers
-// with no GPU.  Device pointers are fake addresses: any dereference by the
-// host layer would fault here.
+// plus UndefinedBehaviorSanitizer, and separately with ThreadSanitizer for
+// the threaded scenario (tests/test_host_sanitizers.py).  The device side is
+// replaced by stubs that record what each launch would receive, so the
+// validation paths and the launch tables (bucket batching, flatten batching,
+// bias tables, accumulate modes) run under the sanitizers with no GPU.
+// Device pointers are fake addresses: any dereference by the host layer
+// would fault here.
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -12,6 +13,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <string>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -36,6 +40,9 @@ std::vector<FlattenLaunch> g_flatten;
 std::vector<zero::BiasTable> g_bias;
 std::vector<int> g_accumulate_mode;
 int g_other_launches = 0;
+// Threaded scenario: the stubs check instead of recording (no shared vectors).
+std::atomic<int> g_threaded{0};
+std::atomic<long> g_table_checks{0}, g_table_bad{0};
 
 void reset() {
     g_bucket.clear();
@@ -106,8 +113,21 @@ hipError_t launch_bucket_flatten(const FlattenTable& table, int count, int64_t m
 }
 
 hipError_t launch_ctl_step(const ChunkTable&, int, int64_t, const GradScalars&,
-                           const AdamScalars&, const BiasTable& tab, const ShardCopies&, bool,
+                           const AdamScalars& as, const BiasTable& tab, const ShardCopies&, bool,
                            zero_step_control*, hipStream_t) {
+    if (g_threaded.load()) {
+        // the table belongs to this call's betas and t0: its first entries
+        // are the corrections adam_scalars computed for hp->step itself
+        bool ok = tab.bc1[0] == as.bc1 && tab.bc2[0] == as.bc2;
+        for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
+            const double t = double(tab.t0) + k;
+            ok = ok && tab.bc1[k] == float(1.0 - pow(double(as.beta1), t)) &&
+                 tab.bc2[k] == float(1.0 - pow(double(as.beta2), t));
+        }
+        ++g_table_checks;
+        if (!ok) ++g_table_bad;
+        return hipSuccess;
+    }
     g_bias.push_back(tab);
     return hipSuccess;
 }
@@ -424,7 +444,55 @@ static void bucket_tables_ctl() {
            ZERO_EINVAL);
 }
 
-int main() {
+// Calls from several threads at once: each thread steps with its own betas
+// and a t0 that keeps changing (so the per-thread bias-table cache both hits
+// and rebuilds), and provokes its own validation errors, whose text must be
+// its own (the error buffer is per thread).
+static void threaded_calls(int n_threads, int iters) {
+    g_threaded = 1;
+    g_table_checks = 0;
+    g_table_bad = 0;
+    std::atomic<long> wrong_error{0};
+    std::vector<std::thread> pool;
+    for (int th = 0; th < n_threads; ++th) {
+        pool.emplace_back([th, iters, &wrong_error] {
+            const void* ch[2] = {fake(kBase + 0x100000ull * th), fake(kBase + 0x100000ull * th + 65536)};
+            const uint64_t base = 0x300000000000ull + 0x10000000000ull * th;
+            float* st[4] = {(float*)fake(base), (float*)fake(base + 0x100000000ull),
+                            (float*)fake(base + 0x200000000ull), (float*)fake(base + 0x300000000ull)};
+            zero_adamw_params p = hp(100);
+            p.beta1 = 0.9f - 0.01f * th;
+            p.beta2 = 0.999f - 0.0001f * th;
+            zero_step_control* ctl = (zero_step_control*)fake(0x500000000000ull + 4096 * th);
+            for (int i = 0; i < iters; ++i) {
+                p.step = 100 + (i / 3 % 5) * 7;
+                if (zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p, ctl,
+                                        nullptr) != ZERO_OK)
+                    ++wrong_error;
+                if (i % 10 == 0) {
+                    const int32_t bad_n = -1 - th;
+                    if (zero_shard_step_ctl(ch, bad_n, 4096, st[0], st[1], st[2], st[3], &p, ctl,
+                                            nullptr) != ZERO_EINVAL)
+                        ++wrong_error;
+                    const std::string want = "n_chunks = " + std::to_string(bad_n);
+                    if (strstr(zero_last_error_string(), want.c_str()) == nullptr) ++wrong_error;
+                }
+            }
+        });
+    }
+    for (auto& t : pool) t.join();
+    g_threaded = 0;
+    EXPECT(wrong_error.load() == 0);
+    EXPECT(g_table_bad.load() == 0);
+    EXPECT(g_table_checks.load() == static_cast<long>(n_threads) * iters);
+}
+
+int main(int argc, char** argv) {
+    if (argc > 1 && strcmp(argv[1], "threads") == 0) {
+        threaded_calls(8, 400);
+        printf("abi harness: ok\n");
+        return 0;
+    }
     launch_length_limits();
     bucket_tables_ctl();
     bucket_tables();
@@ -433,6 +501,7 @@ int main() {
     accumulate_modes();
     scaler_and_control();
     empty_and_errors();
+    threaded_calls(4, 100);
     printf("abi harness: ok\n");
     return 0;
 }
