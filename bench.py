@@ -14,7 +14,10 @@ written copy if the step is clean).  Nothing is read back between steps.
 The host-decided single pass (flag read-back, host loss scale, swap) is
 timed afterwards and reported under "extra".  The two-pass form (overflow check, then the in-place update) and
 the page-literal split (the gradient mean stored as fp16, then the update
-from it) are timed afterwards on the same state and reported under "extra".
+from it) are timed afterwards on the same state and reported under "extra",
+and so is the step's traffic twin (the same loads and stores with XORs for
+arithmetic), whose rate is the ceiling of the step's access pattern on the
+device at hand.
 
 Prints one JSON line.  `value` is params/s of the whole step.  `roofline`
 rates the fused update kernel, the dominant one, by its algorithmic bytes
@@ -204,6 +207,8 @@ def main():
     hp = zs.adamw_params(w.hyper.replace(step=int(c.step)))
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     sq = torch.zeros(1, dtype=torch.float64, device=dev)
+    twin = traffic_twin(zs, d, shard, w, stream)
+    log(f"bench: traffic twin {twin['twin_ms']:.3f} ms ({twin['twin_gbps']:.0f} GB/s)")
     host = host_single_pass(zs, d, shard, scaler, hp, flag, sq, stream, args.two_pass_steps, n)
     log(f"bench: host-synced single pass {host['host_single_pass_ms_per_step']:.3f} ms/step")
     two = two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, args.two_pass_steps)
@@ -226,6 +231,8 @@ def main():
         "step_gbps": k1_bytes / (ms_per_step * 1e-3) / 1e9,
         "skipped_steps": skipped,
     }
+    extra.update(twin)
+    extra["fused_step_pct_twin"] = 100 * k1_gbps / twin["twin_gbps"]
     extra.update(host)
     extra.update(two)
     extra.update(lit)
@@ -678,6 +685,30 @@ def cpu_baseline_buckets(w, items, state, sampled):
                        f"({params} params, N={w.n_replicas} replicas, 2^22-param slices): "
                        f"overflow check and AdamW update; the whole-shard time is "
                        f"extrapolated at this rate")}
+
+
+def traffic_twin(zs, d, shard, w, stream, reps: int = 20):
+    """zero_traffic_twin on the fused step's own arrays (current copy in,
+    other copy out): the same loads and stores with XORs for arithmetic, so
+    its rate is what the step's access pattern reaches on this device.
+    Average and median of HIP-event timings of single launches."""
+    import torch
+    src, dst = shard.current, shard.other
+    for _ in range(3):
+        zs.zero_traffic_twin(d["chunks"], *src[:3], *dst, stream=stream)
+    ev = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        zs.zero_traffic_twin(d["chunks"], *src[:3], *dst, stream=stream)
+        e[1].record(stream)
+        ev.append(e)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = sum(t) / len(t)
+    nbytes = w.bytes_per_param_step() * w.n
+    return {"twin_ms": ms, "twin_median_ms": t[len(t) // 2],
+            "twin_gbps": nbytes / (ms * 1e-3) / 1e9}
 
 
 def host_single_pass(zs, d, shard, scaler, hp, flag, sq, stream, steps: int, n: int):

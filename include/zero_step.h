@@ -436,6 +436,26 @@ int zero_shard_step_buckets_ctl(const zero_bucket_slice* slices, int32_t n_slice
                                 void* const* params_fp16, const zero_adamw_params* hp,
                                 zero_step_control* d_ctl, void* stream);
 
+/*
+ * zero_traffic_twin -- a measurement aid, not part of the step: the memory
+ * accesses of zero_shard_step_out with the same arguments (the same vector
+ * loads and stores of the same arrays, in the same tiles and launch shape),
+ * with integer XORs in place of the step's arithmetic.  Timed beside the step,
+ * it gives the bandwidth that access pattern reaches on the device.  Per
+ * element j, with h = chunk_0[j] ^ ... ^ chunk_{N-1}[j] (binary16 bit
+ * patterns) zero-extended to 32 bits against fp32 bit patterns:
+ *   master_out[j] = master_in[j] ^ exp_avg_in[j] ^ exp_avg_sq_in[j] ^ h,
+ *   exp_avg_out[j] = exp_avg_in[j] ^ h, exp_avg_sq_out[j] = exp_avg_sq_in[j] ^ h,
+ *   param_fp16_out[j] = h ^ (low 16 bits of master_in[j]).
+ * Arguments, alignment and overlap rules are those of zero_shard_step_out
+ * (no loss scale, hyperparameters or flags).  Returns ZERO_OK, ZERO_EINVAL,
+ * ZERO_EALIGN or ZERO_EHIP.
+ */
+int zero_traffic_twin(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                      const float* master_in, const float* exp_avg_in,
+                      const float* exp_avg_sq_in, float* master_out, float* exp_avg_out,
+                      float* exp_avg_sq_out, void* param_fp16_out, void* stream);
+
 /* Text of the last error reported by a call on this thread ("" if none). */
 const char* zero_last_error_string(void);
 

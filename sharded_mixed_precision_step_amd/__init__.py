@@ -35,7 +35,7 @@ EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
             "zero_bucket_flatten", "zero_update_loss_scale", "zero_control_init",
             "zero_control_begin", "zero_overflow_check_ctl", "zero_control_decide",
             "zero_shard_step_ctl", "zero_shard_step_out_ctl", "zero_shard_step_buckets_ctl",
-            "zero_last_error_string")
+            "zero_traffic_twin", "zero_last_error_string")
 ZERO_CTL_STEPS = 64
 ZERO_NORM_SLOTS = 16
 ZERO_NORM_STRIDE = 8
@@ -126,6 +126,7 @@ def _load() -> ctypes.CDLL:
                                             ctypes.POINTER(AdamWParams), vp, vp]
     lib.zero_shard_step_buckets_ctl.argtypes = [ctypes.POINTER(BucketSliceC), i32, i32, i64, pp,
                                                 pp, pp, pp, ctypes.POINTER(AdamWParams), vp, vp]
+    lib.zero_traffic_twin.argtypes = [pp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.zero_last_error_string.argtypes = []
     lib.zero_last_error_string.restype = ctypes.c_char_p
     for name in EXPORTED[:-1]:
@@ -332,6 +333,31 @@ def zero_accumulate_chunk(chunk: torch.Tensor, index: int, n_chunks: int,
                                      int(n_chunks), _opt(acc, torch.float32, "acc"),
                                      _opt(mean_fp16, torch.float16, "mean_fp16"),
                                      _stream(stream)))
+
+
+def zero_traffic_twin(grad_chunks: Sequence[torch.Tensor], master_in: torch.Tensor,
+                      exp_avg_in: torch.Tensor, exp_avg_sq_in: torch.Tensor,
+                      master_out: torch.Tensor, exp_avg_out: torch.Tensor,
+                      exp_avg_sq_out: torch.Tensor, param_fp16_out: torch.Tensor,
+                      stream=None) -> None:
+    """The fused step's memory accesses with XORs for arithmetic: a bandwidth
+    reference for the step's access pattern (see zero_step.h)."""
+    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
+    n = master_in.numel()
+    for name, t in (("exp_avg_in", exp_avg_in), ("exp_avg_sq_in", exp_avg_sq_in),
+                    ("master_out", master_out), ("exp_avg_out", exp_avg_out),
+                    ("exp_avg_sq_out", exp_avg_sq_out), ("param_fp16_out", param_fp16_out),
+                    *((f"grad_chunks[{i}]", c) for i, c in enumerate(grad_chunks))):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    _check(lib.zero_traffic_twin(
+        _ptr_array(ptrs), len(ptrs), n, _dev(master_in, torch.float32, "master_in"),
+        _dev(exp_avg_in, torch.float32, "exp_avg_in"),
+        _dev(exp_avg_sq_in, torch.float32, "exp_avg_sq_in"),
+        _dev(master_out, torch.float32, "master_out"),
+        _dev(exp_avg_out, torch.float32, "exp_avg_out"),
+        _dev(exp_avg_sq_out, torch.float32, "exp_avg_sq_out"),
+        _dev(param_fp16_out, torch.float16, "param_fp16_out"), _stream(stream)))
 
 
 def zero_bucket_flatten(tensors: Sequence[torch.Tensor], bucket: torch.Tensor,

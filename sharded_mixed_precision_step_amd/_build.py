@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzerostep.so")
-SOURCES = [os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_twin.hip"),
+           os.path.join(CSRC, "zero_abi.cpp")]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -12,6 +12,12 @@
 #include "zero_internal.h"
 #include "zero_step.h"
 
+namespace zero {
+// zero_twin.hip: the fused step's traffic twin (a measurement aid).
+hipError_t launch_traffic_twin(const ChunkTable& chunks, int n_chunks, int64_t n,
+                               const ShardState& st, hipStream_t stream);
+}  // namespace zero
+
 namespace {
 
 float bias_correction(float beta, int64_t t);
@@ -691,6 +697,32 @@ int zero_shard_step_out_ctl(const void* const* grad_chunks, int32_t n_chunks, in
     }
     const hipError_t e = zero::launch_ctl_step(table, n_chunks, n, gs, as, tab, sc, true, d_ctl,
                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
+int zero_traffic_twin(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                      const float* master_in, const float* exp_avg_in, const float* exp_avg_sq_in,
+                      float* master_out, float* exp_avg_out, float* exp_avg_sq_out,
+                      void* param_fp16_out, void* stream) {
+    static const char* who = "zero_traffic_twin";
+    zero::ChunkTable table;
+    zero::GradScalars gs;
+    int rc = check_chunks(grad_chunks, n_chunks, n, 1.0f, &table, &gs);
+    if (rc) return rc;
+    if (n == 0) return ok();
+    if ((rc = check_step_length(n, who))) return rc;
+    if ((rc = check_state(n, master_in, exp_avg_in, exp_avg_sq_in, master_out, exp_avg_out,
+                          exp_avg_sq_out, param_fp16_out, who)))
+        return rc;
+    for (int32_t c = 0; c < n_chunks; ++c)
+        if ((rc = check_outputs_clear_of(n, master_out, exp_avg_out, exp_avg_sq_out,
+                                         param_fp16_out, grad_chunks[c], 2 * n, who, c)))
+            return rc;
+    const zero::ShardState st = {master_in,  exp_avg_in,  exp_avg_sq_in,
+                                 master_out, exp_avg_out, exp_avg_sq_out,
+                                 static_cast<uint16_t*>(param_fp16_out)};
+    const hipError_t e =
+        zero::launch_traffic_twin(table, n_chunks, n, st, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, who);
 }
 

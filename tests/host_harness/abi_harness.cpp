@@ -154,6 +154,8 @@ hipError_t launch_reduce_mean(const ChunkTable&, int, int64_t, const GradScalars
                               int32_t*, double*, hipStream_t) ZERO_STUB
 hipError_t launch_control_begin(zero_step_control*, hipStream_t) ZERO_STUB
 hipError_t launch_control_decide(zero_step_control*, float, int, hipStream_t) ZERO_STUB
+hipError_t launch_traffic_twin(const ChunkTable&, int, int64_t, const ShardState&,
+                               hipStream_t) ZERO_STUB
 
 }  // namespace zero
 
@@ -391,6 +393,8 @@ static void launch_length_limits() {
                         nullptr, nullptr, nullptr);     // refused later, for overlapping arrays
     EXPECT(strstr(zero_last_error_string(), "longer than one launch") == nullptr);
     EXPECT(zero_accumulate_chunk(ch[0], too_long, 0, 2, st[0], nullptr, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_traffic_twin(ch, 1, too_long, st[0], st[1], st[2], st[3], st[4], st[5], st[6],
+                             nullptr) == ZERO_EINVAL);
     const int64_t mean_too_long = (zero::kMaxGridBlocks + 1) * zero::kMeanTilePacks * zero::kPack;
     EXPECT(zero_reduce_mean_fp16(ch, 1, mean_too_long, 1.0f, st[0], nullptr, nullptr, nullptr) ==
            ZERO_EINVAL);

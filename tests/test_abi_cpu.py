@@ -156,6 +156,25 @@ def test_shard_step_out_rejects_bad_state():
     assert _step_out(_ptrs(0), 1, 0, (None, None, None), (None,) * 4, _hp()) == zs.ZERO_OK
 
 
+def test_traffic_twin_rejects_what_the_step_rejects():
+    """The traffic twin takes the out-of-place step's arrays under its rules."""
+    B = A + (1 << 20)
+    n = 1000
+    ins = (B, B + 4 * n, B + 8 * n)
+    C = B + (1 << 20)
+    outs = (C, C + 4 * n, C + 8 * n, C + 12 * n)
+    twin = lambda ch, nc, nn, i, o: zs.lib.zero_traffic_twin(ch, nc, nn, *i, *o, None)
+    assert twin(_ptrs(A), 0, n, ins, outs) == zs.ZERO_EINVAL
+    assert twin(_ptrs(A + 2), 1, n, ins, outs) == zs.ZERO_EALIGN
+    assert twin(_ptrs(A), 1, -1, ins, outs) == zs.ZERO_EINVAL
+    assert twin(_ptrs(A), 1, n, (None,) + ins[1:], outs) == zs.ZERO_EINVAL
+    assert twin(_ptrs(A), 1, n, ins, (outs[0] + 8,) + outs[1:]) == zs.ZERO_EALIGN
+    assert twin(_ptrs(A), 1, n, ins, (ins[1],) + outs[1:]) == zs.ZERO_EINVAL
+    assert twin(_ptrs(C + 64), 1, n, ins, outs) == zs.ZERO_EINVAL          # chunk on an output
+    assert "zero_traffic_twin" in _last()
+    assert twin(_ptrs(0), 1, 0, (None,) * 3, (None,) * 4) == zs.ZERO_OK    # n == 0: no-op
+
+
 def _buckets(specs, n_chunks, n_state, ins, outs, hp, flag=None):
     """specs: (chunk pointers, n, offset) per slice."""
     keep = []
