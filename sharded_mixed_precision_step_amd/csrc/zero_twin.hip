@@ -69,20 +69,29 @@ __device__ __forceinline__ void twin_tile(const uint16_t* const* chunks, int n_c
     for (int u = 0; u < kWaveSpan; ++u) {
         const int64_t i = first + u * 64;
         if (!FULL && i >= packs) continue;
-        u32x4* pm = reinterpret_cast<u32x4*>(st.master_out) + 2 * i;
-        u32x4* mm = reinterpret_cast<u32x4*>(st.exp_avg_out) + 2 * i;
-        u32x4* vm = reinterpret_cast<u32x4*>(st.exp_avg_sq_out) + 2 * i;
+        u32x4 po[2], mo[2], vo[2];
         u16x8 out;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const u32x4 hw = widen4(h[u], q);
-            pm[q] = p[u][q] ^ m[u][q] ^ v[u][q] ^ hw;
-            mm[q] = m[u][q] ^ hw;
-            vm[q] = v[u][q] ^ hw;
+            po[q] = p[u][q] ^ m[u][q] ^ v[u][q] ^ hw;
+            mo[q] = m[u][q] ^ hw;
+            vo[q] = v[u][q] ^ hw;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 out[4 * q + e] = static_cast<uint16_t>(h[u][4 * q + e] ^ (p[u][q][e] & 0xffffu));
         }
+        // the step's store order: both halves of an array's 32 bytes per lane
+        // back to back, array after array, then the fp16 params
+        u32x4* pm = reinterpret_cast<u32x4*>(st.master_out) + 2 * i;
+        u32x4* mm = reinterpret_cast<u32x4*>(st.exp_avg_out) + 2 * i;
+        u32x4* vm = reinterpret_cast<u32x4*>(st.exp_avg_sq_out) + 2 * i;
+        pm[0] = po[0];
+        pm[1] = po[1];
+        mm[0] = mo[0];
+        mm[1] = mo[1];
+        vm[0] = vo[0];
+        vm[1] = vo[1];
         *reinterpret_cast<u16x8*>(st.param_fp16_out + i * kPack) = out;
     }
 }
