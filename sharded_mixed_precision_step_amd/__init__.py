@@ -600,6 +600,20 @@ class DeviceStepper:
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
 
+    def single_pass_page_literal(self, grad_chunks, mean_fp16: torch.Tensor, copies,
+                                 stream=None) -> None:
+        """The page-literal split under the control block: the owner's
+        gradient mean stored as fp16 in mean_fp16 (it does not depend on the
+        loss scale), then the single-pass update from it as a one-chunk step,
+        which unscales by the block's S and fuses the flag and squared norm
+        of g = fp32(mean16) / S; then decide and commit."""
+        self._rebase()
+        zero_control_begin(self.ctl, stream=stream)
+        zero_reduce_mean_fp16(grad_chunks, mean_fp16, stream=stream)
+        zero_shard_step_out_ctl([mean_fp16], copies, self.hp, self.ctl, stream=stream)
+        zero_control_decide(self.ctl, 0.0, True, stream=stream)
+        self.since_base += 1
+
     def prepare_single_pass(self, grad_chunks, copies, stream=None) -> "PreparedSinglePass":
         """single_pass with its arguments marshalled once: for short steps,
         where the per-call argument checks and pointer tables cost host time

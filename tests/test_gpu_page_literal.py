@@ -1,6 +1,7 @@
 """The page-literal split against the CPU oracle: the owner's gradient mean
 stored as fp16 (all chunks at once, or one arriving chunk at a time), then
-the update from it as a one-chunk step, element by element and bit for bit."""
+the update from it as a one-chunk step, element by element and bit for bit;
+also the whole split enqueued under the device control block."""
 import numpy as np
 import pytest
 import torch
@@ -123,3 +124,55 @@ def test_split_flag_from_planted_nan():
     torch.cuda.synchronize()
     assert int(fl.item()) == 1
     assert np.isnan(float(mean[8999].item()))
+
+
+def test_split_under_the_control_block_walks_the_oracle():
+    """The page-literal split enqueued under the device control block (fp16
+    mean, one-chunk single pass, decision on the device) over clean and
+    overflowing steps: the oracle's split, loss scaler and t, bit for bit."""
+    import oracle.loss_scale as ols
+    dev = device()
+    n, N = 30_011, 8
+    base = wl.LLAMA3_8B_SHARD
+    w = wl.ShardWorkload(name="split_ctl", wid=base.wid, n=n, n_replicas=N, grad_sigma=1e-4,
+                         loss_scale=65536.0, hyper=base.hyper.replace(step=20),
+                         m_sigma=1e-4, v_sigma=1e-8)
+    h = wl.host_shard(w, n=n, offset_seed=840)
+    a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+    copies = (a, tuple(torch.full_like(x, float("nan")) for x in a))
+    ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale, growth_interval=2),
+                         w.hyper.step, dev)
+    os_ = ols.ScalerState(scale=w.loss_scale, growth_interval=2)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+    chunks = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(N)]
+    mean16 = torch.empty(n, dtype=torch.float16, device=dev)
+    state, t, cur = (h["master"], h["m"], h["v"], h["p16"]), w.hyper.step, 0
+    for k, plant in enumerate([False, True, False, False, True, False]):
+        S = os_.scale
+        g = [wl.host_fp16_grad(wl.seed_of(w.wid, 850 + k, i), n, w.grad_sigma, S)
+             for i in range(N)]
+        if plant:
+            g[(3 * k) % N][(101 * k) % n] = np.float16(np.inf if k % 2 else np.nan)
+        for c, src in zip(chunks, g):
+            c.copy_(torch.from_numpy(src))
+        stepper.single_pass_page_literal(chunks, mean16, copies)
+        m16 = ozs.replica_mean_fp16(g)
+        want = ozs.shard_step_from_fp16_mean(m16, *state, w.hyper.replace(step=t), S)
+        skip = ols.update_loss_scale(os_, want.overflow)
+        t += 0 if skip else 1
+        c = zs.control_read(ctl)
+        print(f"case: page-literal split under control, step {k} plant={plant} S={S}",
+              flush=True)
+        assert np.array_equal(mean16.cpu().numpy().view(np.uint16), m16.view(np.uint16))
+        assert c.overflow == int(want.overflow) and c.skip == int(skip) and c.error == 0
+        assert c.scale == np.float32(os_.scale) and c.step == t
+        if skip:
+            assert c.cur == cur
+            continue
+        assert abs(c.sqnorm - want.sqnorm) <= 1e-6 * want.sqnorm
+        cur = 1 - cur
+        assert c.cur == cur
+        for x, ref in zip(copies[cur], (want.master, want.m, want.v, want.p16)):
+            bits = np.uint16 if ref.dtype == np.float16 else np.uint32
+            assert np.array_equal(x.cpu().numpy().view(bits), ref.view(bits)), k
+        state = (want.master, want.m, want.v, want.p16)
