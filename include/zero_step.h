@@ -89,6 +89,10 @@ typedef struct zero_loss_scaler {
  * bytes) apart, so that no single address takes one atomic add per block. */
 #define ZERO_NORM_SLOTS 16
 #define ZERO_NORM_STRIDE 8
+/* zero_overflow_check_ctl runs on a fixed grid of ZERO_CHECK_PARTS blocks;
+ * each block adds its partial sum of g^2 to its own element of a control
+ * block, with no atomics. */
+#define ZERO_CHECK_PARTS 1536
 
 typedef struct zero_step_control {
     /* dynamic loss scale: the same state and rules as zero_loss_scaler */
@@ -114,11 +118,17 @@ typedef struct zero_step_control {
                                 of bias corrections and nothing was updated;
                                 sticky until the host clears it                 */
     int32_t reserved;
-    /* this step's partial sums of g^2: block b of a *_ctl kernel adds its
-       sum into sqnorm_part[ZERO_NORM_STRIDE * (b % ZERO_NORM_SLOTS)];
-       zero_control_begin clears them, zero_control_decide folds them
-       into sqnorm; the other elements stay 0 */
+    /* this step's partial sums of g^2 from the fused update kernels: block b
+       adds its sum into sqnorm_part[ZERO_NORM_STRIDE * (b % ZERO_NORM_SLOTS)];
+       the other elements stay 0 */
     double sqnorm_part[ZERO_NORM_SLOTS * ZERO_NORM_STRIDE];
+    /* this step's partial sums of g^2 from zero_overflow_check_ctl: block b
+       of its fixed grid adds the sum over its own elements, in a fixed
+       order, to check_part[b].  zero_control_begin clears both arrays and
+       zero_control_decide folds them into sqnorm in a fixed order, so a
+       two-pass step's sqnorm (and its clip factor) has the same bits on
+       every run */
+    double check_part[ZERO_CHECK_PARTS];
 } zero_step_control;
 
 /*
@@ -373,15 +383,21 @@ int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_
  * scaler and the first update's t (>= 1); the in-flight fields are cleared,
  * cur = 0.  Returns ZERO_OK or ZERO_EINVAL.
  *
- * zero_control_begin: start a step: overflow = 0, sqnorm = 0 and its slots
- * cleared, skip = 0, clip_coef = 1, scale_used = scale, step_used = step.
+ * zero_control_begin: start a step: overflow = 0, sqnorm = 0 and its
+ * partial sums cleared, skip = 0, clip_coef = 1, scale_used = scale,
+ * step_used = step.
  *
  * zero_overflow_check_ctl: zero_overflow_check with S = d_ctl->scale_used,
- * accumulating into d_ctl->overflow and the squared-norm slots.
+ * the flag into d_ctl->overflow and the squared norm into d_ctl->check_part:
+ * block b of a fixed grid adds the sum over its own elements, taken in a
+ * fixed order, to check_part[b] (no atomics: only block b writes it, and
+ * calls on the block are ordered).  Several calls in one step (one per
+ * bucket) accumulate in call order, and the result has the same bits on
+ * every run.
  *
  * zero_control_decide: the decision, on the device, after the step's check
- * (two-pass) or fused update (single pass): sqnorm = the sum of the slots
- * (fp64, slot 0 first); skip = (overflow != 0); the
+ * (two-pass) or fused update (single pass): sqnorm = the sum of the
+ * partial sums (fp64, in a fixed order); skip = (overflow != 0); the
  * scale moves as zero_update_loss_scale moves it; on a clean step t advances
  * (step += 1), clip_coef = min(1, max_grad_norm / (sqrt(sqnorm) + 1e-6))
  * evaluated in fp64 and rounded to fp32 when max_grad_norm > 0 (else 1), and
@@ -396,7 +412,7 @@ int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_
  * copy cur into copy 1 - cur (masters[2], exp_avgs[2], exp_avg_sqs[2],
  * params_fp16[2]: HOST arrays of two DEVICE pointers each), with
  * S = scale_used and the bias corrections of t = step_used, accumulating the
- * flag and the squared-norm slots of d_ctl.  Follow it with zero_control_decide(...,
+ * flag and the squared-norm slots (sqnorm_part) of d_ctl.  Follow it with zero_control_decide(...,
  * flip_copy = 1): a clean step then makes the written copy current.
  *
  * Bias corrections: hp->step is the base t0 of a table the call computes

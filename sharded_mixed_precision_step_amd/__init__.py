@@ -39,6 +39,7 @@ EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
 ZERO_CTL_STEPS = 64
 ZERO_NORM_SLOTS = 16
 ZERO_NORM_STRIDE = 8
+ZERO_CHECK_PARTS = 1536
 
 
 class ZeroStepError(RuntimeError):
@@ -78,7 +79,8 @@ class StepControl(ctypes.Structure):
                 ("scale_used", ctypes.c_float), ("clip_coef", ctypes.c_float),
                 ("overflow", ctypes.c_int32), ("skip", ctypes.c_int32),
                 ("error", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("sqnorm_part", ctypes.c_double * (ZERO_NORM_SLOTS * ZERO_NORM_STRIDE))]
+                ("sqnorm_part", ctypes.c_double * (ZERO_NORM_SLOTS * ZERO_NORM_STRIDE)),
+                ("check_part", ctypes.c_double * ZERO_CHECK_PARTS)]
 
 
 class BucketSliceC(ctypes.Structure):

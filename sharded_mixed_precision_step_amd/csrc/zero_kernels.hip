@@ -84,8 +84,13 @@ __device__ __forceinline__ uint16_t to_fp16_bits(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));  // nearest-even
 }
 
-// Block-wide OR of `bad` and sum of `sq`; one atomic of each per block.
-// Every thread of the block must call it.
+// Block-wide OR of `bad` and sum of `sq`, published by one thread: an
+// atomic OR of the flag (only if set), and an atomic add of the sum into
+// *d_sqnorm; with OWN_PART, *d_sqnorm is this block's own partial and takes
+// a plain add instead (no other block writes it).  The sum is the same bits
+// for the same per-thread values: a fixed butterfly across the wave, then
+// the four waves in order.  Every thread of the block must call it.
+template <bool OWN_PART = false>
 __device__ __forceinline__ void publish(bool bad, double sq, int32_t* d_overflow,
                                         double* d_sqnorm) {
     __shared__ double wave_sq[kBlock / 64];
@@ -109,7 +114,12 @@ __device__ __forceinline__ void publish(bool bad, double sq, int32_t* d_overflow
             b |= wave_bad[w];
         }
         if (b && d_overflow) atomicOr(d_overflow, 1);
-        if (d_sqnorm) atomicAdd(d_sqnorm, total);
+        if (d_sqnorm) {
+            if constexpr (OWN_PART)
+                *d_sqnorm += total;
+            else
+                atomicAdd(d_sqnorm, total);
+        }
     }
 }
 
@@ -307,8 +317,10 @@ __device__ __forceinline__ GradScalars with_scale(GradScalars gs, float S) {
     return gs;
 }
 
-// CTL: S is the control block's scale_used, and the flag and squared norm go
-// to its overflow and sqnorm fields.
+// CTL: S is the control block's scale_used, the flag goes to its overflow
+// field, and block b adds its partial sum to its check_part[b].  The grid is
+// then the fixed ZERO_CHECK_PARTS blocks, so each thread's elements, and so
+// every partial, are the same from run to run.
 template <int NC, bool CTL = false>
 __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs,
@@ -316,7 +328,7 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     if constexpr (CTL) {
         gs = with_scale(gs, ctl->scale_used);
         d_overflow = &ctl->overflow;
-        d_sqnorm = norm_slot(ctl);
+        d_sqnorm = &ctl->check_part[blockIdx.x];
     }
     const int64_t packs = n / kPack;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
@@ -343,7 +355,7 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
             sq += static_cast<double>(g) * static_cast<double>(g);
         }
     }
-    publish(bad, sq, d_overflow, d_sqnorm);
+    publish<CTL>(bad, sq, d_overflow, d_sqnorm);
 }
 
 // The update under a device control block.  SINGLE = false: the two-pass
@@ -413,23 +425,45 @@ __global__ __launch_bounds__(kBlock) void bucket_ctl_step_kernel(BucketTable t, 
     publish(bad, sq, &ctl->overflow, norm_slot(ctl));
 }
 
-// One thread: start a step.
-__global__ void control_begin_kernel(zero_step_control* c) {
+static_assert(ZERO_CHECK_PARTS % kBlock == 0, "check partials fold kBlock-wide");
+static_assert(ZERO_NORM_SLOTS <= kBlock, "norm slots fold kBlock-wide");
+
+// One block: start a step (clear the partial sums, then the fields).
+__global__ __launch_bounds__(kBlock) void control_begin_kernel(zero_step_control* c) {
+    for (int k = threadIdx.x; k < ZERO_CHECK_PARTS; k += kBlock) c->check_part[k] = 0.0;
+    if (threadIdx.x < ZERO_NORM_SLOTS) c->sqnorm_part[ZERO_NORM_STRIDE * threadIdx.x] = 0.0;
+    if (threadIdx.x != 0) return;
     c->overflow = 0;
     c->sqnorm = 0.0;
-    for (int k = 0; k < ZERO_NORM_SLOTS; ++k) c->sqnorm_part[ZERO_NORM_STRIDE * k] = 0.0;
     c->skip = 0;
     c->clip_coef = 1.0f;
     c->scale_used = c->scale;
     c->step_used = c->step;
 }
 
-// One thread: the decision, the loss-scale move (the rules of the host's
-// zero_update_loss_scale, in fp32), the clip factor, t and the copy.
-__global__ void control_decide_kernel(zero_step_control* c, float max_norm, int flip) {
+// One block: the step's squared norm folded from its partial sums in a
+// fixed order; then, on one thread, the decision, the loss-scale move (the
+// rules of the host's zero_update_loss_scale, in fp32), the clip factor, t
+// and the copy.
+__global__ __launch_bounds__(kBlock) void control_decide_kernel(zero_step_control* c,
+                                                                float max_norm, int flip) {
+    // sqnorm: thread t sums its ZERO_CHECK_PARTS / kBlock consecutive check
+    // partials in order (and slot t), then a fixed pairwise tree in LDS
+    __shared__ double part[kBlock];
+    constexpr int kPer = ZERO_CHECK_PARTS / kBlock;
     double sq = 0.0;
-    for (int k = 0; k < ZERO_NORM_SLOTS; ++k) sq += c->sqnorm_part[ZERO_NORM_STRIDE * k];
-    c->sqnorm = sq;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) sq += c->check_part[threadIdx.x * kPer + k];
+    if (threadIdx.x < ZERO_NORM_SLOTS) sq += c->sqnorm_part[ZERO_NORM_STRIDE * threadIdx.x];
+    part[threadIdx.x] = sq;
+    __syncthreads();
+#pragma unroll
+    for (int w = kBlock / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
+    c->sqnorm = part[0];
     const bool skip = c->overflow != 0;
     c->skip = skip ? 1 : 0;
     if (skip) {
@@ -721,7 +755,7 @@ hipError_t bucket_ctl_impl(const BucketTable& t, int n_chunks, const GradScalars
 template <int NC>
 hipError_t check_ctl_impl(const ChunkTable& chunks, int n_chunks, int64_t n,
                           const GradScalars& gs, zero_step_control* ctl, hipStream_t stream) {
-    const int64_t grid = check_grid(n);
+    const int64_t grid = ZERO_CHECK_PARTS;  // fixed: one partial per block, same every run
     hipLaunchKernelGGL((overflow_check_kernel<NC, true>), dim3(static_cast<unsigned>(grid)),
                        dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, nullptr, nullptr, ctl);
     return hipGetLastError();
@@ -895,13 +929,14 @@ hipError_t launch_overflow_check_ctl(const ChunkTable& chunks, int n_chunks, int
 }
 
 hipError_t launch_control_begin(zero_step_control* ctl, hipStream_t stream) {
-    hipLaunchKernelGGL(control_begin_kernel, dim3(1), dim3(1), 0, stream, ctl);
+    hipLaunchKernelGGL(control_begin_kernel, dim3(1), dim3(kBlock), 0, stream, ctl);
     return hipGetLastError();
 }
 
 hipError_t launch_control_decide(zero_step_control* ctl, float max_norm, int flip,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(control_decide_kernel, dim3(1), dim3(1), 0, stream, ctl, max_norm, flip);
+    hipLaunchKernelGGL(control_decide_kernel, dim3(1), dim3(kBlock), 0, stream, ctl, max_norm,
+                       flip);
     return hipGetLastError();
 }
 

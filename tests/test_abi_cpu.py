@@ -366,7 +366,8 @@ def test_ctypes_structs_and_constants_match_the_header(tmp_path):
     structs = {"zero_adamw_params": zs.AdamWParams, "zero_loss_scaler": zs.LossScaler,
                "zero_bucket_slice": zs.BucketSliceC, "zero_step_control": zs.StepControl}
     consts = ("ZERO_OK", "ZERO_EINVAL", "ZERO_EALIGN", "ZERO_ERANGE", "ZERO_EHIP",
-              "ZERO_MAX_CHUNKS", "ZERO_CTL_STEPS", "ZERO_NORM_SLOTS", "ZERO_NORM_STRIDE")
+              "ZERO_MAX_CHUNKS", "ZERO_CTL_STEPS", "ZERO_NORM_SLOTS", "ZERO_NORM_STRIDE",
+              "ZERO_CHECK_PARTS")
     lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "zero_step.h"',
              "int main(void) {"]
     for cname, py in structs.items():

@@ -220,8 +220,8 @@ def test_graph_of_one_step_replays_like_eager_calls():
         for name, _ in zs.StepControl._fields_:
             if name == "sqnorm":
                 assert abs(gc.sqnorm - ec.sqnorm) <= 1e-12 * ec.sqnorm
-            elif name == "sqnorm_part":
-                for a, b in zip(gc.sqnorm_part, ec.sqnorm_part):
+            elif name in ("sqnorm_part", "check_part"):
+                for a, b in zip(getattr(gc, name), getattr(ec, name)):
                     assert abs(a - b) <= 1e-12 * abs(b)
             else:
                 assert getattr(gc, name) == getattr(ec, name), name
@@ -471,3 +471,59 @@ def test_bucket_table_under_control_at_any_replica_count(NN):
     assert c.cur == 1 and c.skip == 0 and c.overflow == 0 and c.error == 0
     assert abs(c.sqnorm - want.sqnorm) <= 1e-6 * want.sqnorm
     _assert_state(copies[1], want, f"bucket table N={NN}")
+
+
+def test_two_pass_norm_and_clip_repeat_bit_for_bit():
+    """The two-pass flow's squared norm comes from the check's fixed-grid
+    partials folded in a fixed order, so two runs from the same state give
+    the same norm, clip factor and clipped state, bit for bit."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=911)
+
+    def run():
+        state = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+        ctl = zs.control_new(_scaler()[0], w.hyper.step, dev)
+        stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+        chunks = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(N)]
+        seen = []
+        for k in range(4):
+            for c, src in zip(chunks, _grads(w, 20 + k, zs.control_read(ctl).scale, False)):
+                c.copy_(torch.from_numpy(src))
+            stepper.two_pass(chunks, *state, max_grad_norm=2e-3)
+            c = zs.control_read(ctl)
+            seen.append((c.sqnorm, c.clip_coef, c.skip, c.step))
+        return seen, [x.clone() for x in state]
+
+    print("case: two-pass clipped norm repeats", flush=True)
+    a, sa = run()
+    b, sb = run()
+    assert a == b                       # fp64 norm and fp32 clip factor, bit for bit
+    assert any(coef < 1.0 for _, coef, _, _ in a)
+    for x, y in zip(sa, sb):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+def test_check_partials_accumulate_over_buckets():
+    """Two zero_overflow_check_ctl calls on the two halves of a shard (one per
+    bucket) fold to the squared norm of the whole shard, the same bits on
+    every run, and within 1e-12 of the oracle's ascending-order sum."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=912)
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    half = (n // 2) // 8 * 8
+    want_flag, want_sq = ozs.check_only(h["chunks"], w.loss_scale)
+    got = []
+    for rep in range(2):
+        ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+        zs.zero_control_begin(ctl)
+        zs.zero_overflow_check_ctl([c[:half] for c in chunks], ctl)
+        zs.zero_overflow_check_ctl([c[half:] for c in chunks], ctl)
+        zs.zero_control_decide(ctl, 0.0, False)
+        c = zs.control_read(ctl)
+        print(f"case: check partials over two buckets, run {rep}", flush=True)
+        assert c.overflow == int(want_flag) == 0
+        got.append(c.sqnorm)
+    assert got[0] == got[1]
+    assert abs(got[0] - want_sq) <= 1e-12 * want_sq
