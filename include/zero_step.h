@@ -117,17 +117,19 @@ typedef struct zero_step_control {
     int32_t error;           /* bit 0: step_used was outside the update's table
                                 of bias corrections and nothing was updated;
                                 sticky until the host clears it                 */
-    int32_t reserved;
+    int32_t check_ran;       /* set by zero_overflow_check_ctl: check_part
+                                holds partials to fold and later to clear     */
     /* this step's partial sums of g^2 from the fused update kernels: block b
        adds its sum into sqnorm_part[ZERO_NORM_STRIDE * (b % ZERO_NORM_SLOTS)];
        the other elements stay 0 */
     double sqnorm_part[ZERO_NORM_SLOTS * ZERO_NORM_STRIDE];
     /* this step's partial sums of g^2 from zero_overflow_check_ctl: block b
        of its fixed grid adds the sum over its own elements, in a fixed
-       order, to check_part[b].  zero_control_begin clears both arrays and
-       zero_control_decide folds them into sqnorm in a fixed order, so a
-       two-pass step's sqnorm (and its clip factor) has the same bits on
-       every run */
+       order, to check_part[b], and check_ran is set.  zero_control_begin
+       clears both arrays (check_part only when check_ran is set, which it
+       then clears) and zero_control_decide folds them into sqnorm in a
+       fixed order, so a two-pass step's sqnorm (and its clip factor) has
+       the same bits on every run */
     double check_part[ZERO_CHECK_PARTS];
 } zero_step_control;
 

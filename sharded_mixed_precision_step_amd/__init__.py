@@ -78,7 +78,7 @@ class StepControl(ctypes.Structure):
                 ("step_used", ctypes.c_int64), ("sqnorm", ctypes.c_double),
                 ("scale_used", ctypes.c_float), ("clip_coef", ctypes.c_float),
                 ("overflow", ctypes.c_int32), ("skip", ctypes.c_int32),
-                ("error", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("error", ctypes.c_int32), ("check_ran", ctypes.c_int32),
                 ("sqnorm_part", ctypes.c_double * (ZERO_NORM_SLOTS * ZERO_NORM_STRIDE)),
                 ("check_part", ctypes.c_double * ZERO_CHECK_PARTS)]
 

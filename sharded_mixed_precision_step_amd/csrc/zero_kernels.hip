@@ -329,6 +329,7 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
         gs = with_scale(gs, ctl->scale_used);
         d_overflow = &ctl->overflow;
         d_sqnorm = &ctl->check_part[blockIdx.x];
+        if (blockIdx.x == 0 && threadIdx.x == 0) ctl->check_ran = 1;
     }
     const int64_t packs = n / kPack;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
@@ -428,11 +429,17 @@ __global__ __launch_bounds__(kBlock) void bucket_ctl_step_kernel(BucketTable t, 
 static_assert(ZERO_CHECK_PARTS % kBlock == 0, "check partials fold kBlock-wide");
 static_assert(ZERO_NORM_SLOTS <= kBlock, "norm slots fold kBlock-wide");
 
-// One block: start a step (clear the partial sums, then the fields).
+// One block: start a step (clear the partial sums, then the fields).  The
+// check's partials are cleared only if a check wrote them since the last
+// clear, so flows without the check do not pay for them.
 __global__ __launch_bounds__(kBlock) void control_begin_kernel(zero_step_control* c) {
-    for (int k = threadIdx.x; k < ZERO_CHECK_PARTS; k += kBlock) c->check_part[k] = 0.0;
+    const bool check_ran = c->check_ran != 0;
+    if (check_ran)
+        for (int k = threadIdx.x; k < ZERO_CHECK_PARTS; k += kBlock) c->check_part[k] = 0.0;
     if (threadIdx.x < ZERO_NORM_SLOTS) c->sqnorm_part[ZERO_NORM_STRIDE * threadIdx.x] = 0.0;
+    __syncthreads();  // every thread has read check_ran before it is cleared
     if (threadIdx.x != 0) return;
+    c->check_ran = 0;
     c->overflow = 0;
     c->sqnorm = 0.0;
     c->skip = 0;
@@ -452,8 +459,10 @@ __global__ __launch_bounds__(kBlock) void control_decide_kernel(zero_step_contro
     __shared__ double part[kBlock];
     constexpr int kPer = ZERO_CHECK_PARTS / kBlock;
     double sq = 0.0;
+    if (c->check_ran) {  // uniform across the block
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) sq += c->check_part[threadIdx.x * kPer + k];
+        for (int k = 0; k < kPer; ++k) sq += c->check_part[threadIdx.x * kPer + k];
+    }
     if (threadIdx.x < ZERO_NORM_SLOTS) sq += c->sqnorm_part[ZERO_NORM_STRIDE * threadIdx.x];
     part[threadIdx.x] = sq;
     __syncthreads();
