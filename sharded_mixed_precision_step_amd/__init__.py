@@ -586,6 +586,32 @@ class DeviceStepper:
                             self.ctl, stream=stream)
         self.since_base += 1
 
+    def two_pass_buckets(self, buckets, master, exp_avg, exp_avg_sq, param_fp16,
+                         max_grad_norm: float = 0.0, stream=None) -> None:
+        """two_pass over a ZeRO-2 shard held as bucket slices: `buckets` is a
+        sequence of (grad_chunks, offset) that covers the state exactly once.
+        One check per bucket (their partial sums accumulate in a fixed order),
+        one decision for the whole shard (skip, loss scale, clip factor from
+        the whole shard's norm, t), then one in-place update per bucket."""
+        n = master.numel()
+        covered = sum(chunks[0].numel() for chunks, _ in buckets)
+        if covered != n:
+            raise ValueError(f"the buckets cover {covered} elements of a {n}-element state")
+        for chunks, off in buckets:
+            if off < 0 or off + chunks[0].numel() > n:
+                raise ValueError(f"bucket at {off} lies outside the {n}-element state")
+        self._rebase()
+        zero_control_begin(self.ctl, stream=stream)
+        for chunks, _ in buckets:
+            zero_overflow_check_ctl(chunks, self.ctl, stream=stream)
+        zero_control_decide(self.ctl, max_grad_norm, False, stream=stream)
+        for chunks, off in buckets:
+            nb = chunks[0].numel()
+            zero_shard_step_ctl(chunks, *(t[off:off + nb] for t in
+                                          (master, exp_avg, exp_avg_sq, param_fp16)),
+                                self.hp, self.ctl, stream=stream)
+        self.since_base += 1
+
     def single_pass(self, grad_chunks, copies, stream=None) -> None:
         """Fused update from copy cur into the other, then decide and commit."""
         self._rebase()

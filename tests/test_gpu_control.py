@@ -2,10 +2,13 @@
 enqueued with no read-back (two-pass with and without gradient-norm
 clipping, and single pass with the commit on the device) walk the same
 states as the oracle's step, loss scaler and t over clean and overflowing
-steps (whole shard, a bucket table, and buckets streamed as they arrive,
+steps (whole shard, a bucket table, buckets streamed as they arrive, and the
+two-pass flow over buckets, with clipping,
 at N = 1 .. 64); a
 stale bias-correction table is refused on the device; and a HIP
 graph of one step replays like the eager calls."""
+import struct
+
 import numpy as np
 import pytest
 import torch
@@ -82,8 +85,8 @@ def test_two_pass_sequence_matches_oracle(clip):
         if clip == 2e-3 and not skip:
             assert c.clip_coef < 0.5
         if clip == 2e-3:
-            # The clip factor comes from the squared norm, summed in fp64 in
-            # atomic order on the device and in index order by the oracle; the
+            # The clip factor comes from the squared norm, summed in fp64 in a
+            # fixed tree order on the device and in index order by the oracle; the
             # factor can then differ by an fp32 ulp, and where the moment
             # update cancels to near zero a tiny absolute difference is many
             # ulps.  The bar here is the stated one: 1e-6 relative or 1e-9
@@ -527,3 +530,63 @@ def test_check_partials_accumulate_over_buckets():
         got.append(c.sqnorm)
     assert got[0] == got[1]
     assert abs(got[0] - want_sq) <= 1e-12 * want_sq
+
+
+@pytest.mark.parametrize("clip", [0.0, 2e-3])
+def test_two_pass_over_buckets_matches_oracle(clip):
+    """A ZeRO-2 shard held as ragged bucket slices, stepped by the two-pass
+    flow: one check per bucket, one decision (and clip factor) for the whole
+    shard, one in-place update per bucket.  Against the oracle's step of the
+    whole shard over clean and overflowing steps; bit for bit without
+    clipping, to the tolerance with it (the norm's summation order differs
+    from the oracle's); and the same bits on a second run."""
+    dev = device()
+    w = _workload()
+    sizes = [8 * s for s in (1, 511, 513, 2048, 7)]
+    sizes.append(n - sum(sizes))
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int)
+    h = wl.host_shard(w, n=n, offset_seed=913)
+
+    def run():
+        state = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+        ctl = zs.control_new(_scaler()[0], w.hyper.step, dev)
+        stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+        full = [torch.empty(n, dtype=torch.float16, device=dev) for _ in range(N)]
+        buckets = [([f[o:o + s] for f in full], int(o)) for o, s in zip(offs, sizes)]
+        log = []
+        for k, plant in enumerate(PLAN[:5]):
+            S = zs.control_read(ctl).scale
+            g = _grads(w, 30 + k, S, plant)
+            for f, src in zip(full, g):
+                f.copy_(torch.from_numpy(src))
+            stepper.two_pass_buckets(buckets, *state, max_grad_norm=clip)
+            log.append((g, S, zs.control_read(ctl), [x.clone() for x in state]))
+        return log
+
+    first, second = run(), run()
+    os_ = ols.ScalerState(scale=65536.0, growth_interval=2)
+    st, t = (h["master"], h["m"], h["v"], h["p16"]), w.hyper.step
+    for k, ((g, S, c, got), (_, _, c2, got2)) in enumerate(zip(first, second)):
+        print(f"case: two-pass over buckets clip={clip} step {k}", flush=True)
+        assert S == np.float32(os_.scale)
+        want = ozs.shard_step_clipped(g, *st, w.hyper.replace(step=t), S, clip)
+        skip = ols.update_loss_scale(os_, want.overflow)
+        t += 0 if skip else 1
+        _check_control(c, os_, t, skip, want)
+        # the same bits on both runs (NaN on an overflow step included)
+        assert struct.pack("<d", c.sqnorm) == struct.pack("<d", c2.sqnorm)
+        assert struct.pack("<f", c.clip_coef) == struct.pack("<f", c2.clip_coef)
+        for x, y in zip(got, got2):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+        if skip:
+            # untouched: the device's own state before this step, bit for bit
+            prev = first[k - 1][3] if k else [torch.from_numpy(h[key]) for key in
+                                              ("master", "m", "v", "p16")]
+            for x, y in zip(got, prev):
+                assert torch.equal(x.cpu().view(torch.uint8), y.cpu().view(torch.uint8))
+            continue
+        if clip == 0.0:
+            _assert_state(got, want, f"two-pass buckets step {k}")
+        else:
+            assert_matches_oracle(dict(zip(("master", "m", "v", "p16"), got)), want, max_ulp=None)
+        st = (want.master, want.m, want.v, want.p16)
