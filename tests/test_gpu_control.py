@@ -1,12 +1,14 @@
-"""The device-resident step control against the CPU oracle: whole steps
-enqueued with no read-back (two-pass with and without gradient-norm
-clipping, and single pass with the commit on the device) walk the same
-states as the oracle's step, loss scaler and t over clean and overflowing
-steps (whole shard, a bucket table, buckets streamed as they arrive, and the
-two-pass flow over buckets, with clipping,
-at N = 1 .. 64); a
-stale bias-correction table is refused on the device; and a HIP
-graph of one step replays like the eager calls."""
+"""The device-resident step control against the CPU oracle.
+
+Whole steps are enqueued with no read-back: two-pass (with and without
+gradient-norm clipping) and single pass (commit on the device). They walk
+the same states as the oracle's step, loss scaler and t over clean and
+overflowing steps. This holds over the whole shard, a bucket table, buckets
+streamed as they arrive, and the two-pass flow over buckets, at N = 1..64.
+Also: the two-pass norm and clip factor repeat bit for bit; a stale
+bias-correction table is refused on the device; the prepared step equals
+the unprepared one; and a HIP graph of one step replays like the eager
+calls."""
 import struct
 
 import numpy as np
