@@ -116,8 +116,17 @@ def cpu_baseline(dev_shard, w, slices: int):
         results = list(ex.map(run, range(count)))
     dt = time.perf_counter() - t0
     assert not any(r.overflow for r in results)
+    # the same oracle on one core, over the first few slices only
+    single = min(8, count)
+    t0 = time.perf_counter()
+    for k in range(single):
+        run(k)
+    dt1 = time.perf_counter() - t0
+    n1 = min(single * piece, total)
     return {"value": total / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
             "seconds": dt,
+            "single_core_value": n1 / dt1,
+            "single_core_sample": f"the first {n1} params ({single} slices of 2^22), one thread",
             "sample": (f"{'whole' if total == w.n else 'first ' + str(total) + ' params of the'} "
                        f"{w.name} shard ({total} params, {count} slices of 2^22, "
                        f"N={w.n_replicas} replicas): overflow check and AdamW update")}
