@@ -11,9 +11,10 @@ elsewhere.
   step at the halved scale matches the oracle everywhere.
 * ZeRO-2 bucketed (160 buckets, 973,111,296 params on one rank): every
   bucket flattened for 8 replicas, then all 160 slices stepped by one
-  multi-bucket call; buckets 0, 3, 4 and 159 (both bucket shapes, first and
-  last) checked in full against the oracle's flatten and step, the rest by
-  the fp16 writeback property and against 160 single-slice calls.
+  multi-bucket call; every element against the oracle; buckets 0, 3, 4 and
+  159 (both bucket shapes, first and last) also from the replicas' tensors
+  through the oracle's flatten; and against 160 single-slice calls and the
+  device-controlled table call.
 * 70B-class shard (4,412,500,000 params, N = 16) streamed in 23 buckets
   through two chunk buffers: buckets 0, 11 and 22 checked in full, the rest
   by the fp16 writeback property.
@@ -140,9 +141,11 @@ def test_zero2_bucketed_full():
     """Every bucket is flattened for the 8 replicas and this rank's slice of
     each replica's bucket is kept (what the per-bucket reduce-scatter would
     deliver); then one zero_shard_step_buckets call updates all 160 slices,
-    as a ZeRO-2 rank steps after backward.  Sampled buckets are checked in
-    full against the oracle's flatten and step; 160 per-bucket
-    zero_shard_step_out calls must give the same bits."""
+    as a ZeRO-2 rank steps after backward.  Every element of the step is
+    checked against the oracle; sampled buckets are also checked from the
+    replicas' tensors through the oracle's flatten; 160 per-bucket
+    zero_shard_step_out calls and the device-controlled table call must give
+    the same bits."""
     dev = device()
     w = wl.ZERO2
     N, r, S = w.n_replicas, wl.ZERO2_RANK, w.loss_scale
@@ -203,7 +206,12 @@ def test_zero2_bucketed_full():
                                   ref.view(np.uint32)), (b, name)
         assert np.array_equal(out[3][a:a + n].cpu().numpy().view(np.uint16),
                               want.p16.view(np.uint16))
-    _assert_writeback_property(out[0], out[3], "zero2")
+    # every element of the rank's 973M-param step against the oracle, from
+    # the slices the device flatten produced (checked above for the sampled
+    # buckets against the oracle's flatten of the replicas' tensors)
+    print("case: full zero2 rank, all 160 slices vs oracle", flush=True)
+    overflow, want_sq, _ = compare_with_oracle(owned, cur, out, w.hyper, S, label="zero2 ")
+    assert not overflow and rel_close(float(sq.item()), want_sq)
     # the same update as 160 separate calls, and as the whole step under the
     # device control block (what bench.py --workload zero2_bucketed times)
     ref = tuple(torch.empty_like(t) for t in cur)
