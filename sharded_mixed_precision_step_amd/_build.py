@@ -40,16 +40,44 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
+def code_text(src: str) -> str:
+    """C/C++ source with its comments removed and each run of whitespace
+    collapsed to one space: what the compiler sees, so that editing a comment
+    does not change a digest.  String and character literals are kept as
+    they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_digest() -> str:
-    """SHA-256 over the sources that fix the kernels' code and launch shapes
-    (the device source and the internal header).  Hardware counters taken on
-    one digest do not describe kernels built from another."""
+    """SHA-256 over the code of the sources that fix the kernels' code and
+    launch shapes (the device source and the internal header), comments and
+    layout aside.  Hardware counters taken on one digest do not describe
+    kernels built from another."""
     import hashlib
     h = hashlib.sha256()
     for p in (os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_internal.h")):
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -2,26 +2,36 @@
 //
 //   shard_step_kernel      N fp16 replica chunks -> fp32 sum in replica order
 //                          -> mean -> unscale -> (flag, sum g^2) -> Adam/AdamW
-//                          moments -> fp32 master -> fp16 params, in place.
+//                          moments -> fp32 master -> fp16 params, in place or
+//                          from one copy of the state into another.
+//   bucket_step_kernel     the same over a table of bucket slices (ZeRO-2).
+//   ctl_step_kernel,       the same with S, t, the copy and the clip factor
+//   bucket_ctl_step_kernel read from a device control block.
 //   overflow_check_kernel  the same front half, reductions only.
+//   control_begin_kernel,  start and decide a step on the device (skip, loss
+//   control_decide_kernel  scale, clip factor, t, commit).
 //   reduce_mean_kernel     the replica mean stored as fp16 (page-literal split).
+//   accumulate_kernel      one arriving chunk folded into the fp16 mean.
 //   bucket_flatten_kernel  whole tensors into 256-aligned, zero-padded slots.
 //
 // The update order is that of the ZeRO-1 update step of the ZeRO notes
 // (rkmt.cn/news/44736, section "Deepspeed ZeRO-1", step 更新): fp16 to fp32
 // (not stored), scale, fp32 moments, fp32 master weights, fp16 params.
 //
-// All three are memory-bound streams (well under 1 flop per byte), so the
-// design goal is HBM bandwidth.  Every access is a 16-byte vector (8 fp16
+// The data kernels are memory-bound streams (well under 1 flop per byte), so
+// the design goal is HBM bandwidth.  Every access is a 16-byte vector (8 fp16
 // gradients of one chunk, 4 fp32 of one state array, 8 fp16 params), so each
 // 64-wide wave instruction moves 1 KiB of one array, fully coalesced.  The
-// fused step runs one block per 4096-param tile (a one-shot grid); the check
-// runs a grid-stride loop over a resident grid with streaming loads.  Both
-// launch shapes were chosen by measurement on MI355X: with the N + 7 arrays
-// the step touches, one-shot tiles sustain the most bandwidth, while the
-// read-only check does best as a resident loop.  The overflow flag and the
-// squared norm are reduced per wave with lane shuffles, across the block's
-// four waves in LDS, and published with one atomic each per block.  Every
+// kernels that write run one block per tile (a one-shot grid: 4096 params
+// per block for the step); the check runs a grid-stride loop over a resident
+// grid with streaming loads.  Both launch shapes were chosen by measurement
+// on MI355X: one-shot tiles sustain the most bandwidth for the kernels that
+// write, while the read-only check does best as a resident loop.  The
+// overflow flag and the squared norm are reduced per wave with lane
+// shuffles, across the block's four waves in LDS, and published once per
+// block: the flag by an atomic OR where it is set; the norm by an atomic add
+// into the caller's double or into one of a control block's 16 slots, or, in
+// the control-block check, by a plain add to the block's own partial.  Every
 // fp32 operation is a separate IEEE operation (the file is built without
 // floating-point contraction, division and square root are the correctly
 // rounded forms), so results match the plain per-operation definition bit

@@ -394,3 +394,16 @@ def test_ctypes_structs_and_constants_match_the_header(tmp_path):
             assert getattr(structs[a], b).offset == int(v), (a, b)
         seen += 1
     assert seen == len(consts) + sum(1 + len(py._fields_) for py in structs.values())
+
+
+def test_kernel_digest_follows_code_not_comments():
+    """The digest that ties the committed counter summary to the kernel
+    sources ignores comments and layout, and sees any change of code."""
+    from sharded_mixed_precision_step_amd import _build
+    base = 'int f(int a) {\n  return a + 1;  // one more\n}\nconst char* s = "/* kept */";\n'
+    same = '/* a header */\nint f(int a)\n{\n    return a + 1;\n}\nconst char* s = "/* kept */"; // x\n'
+    other = 'int f(int a) {\n  return a + 2;\n}\nconst char* s = "/* kept */";\n'
+    assert _build.code_text(base) == _build.code_text(same)
+    assert _build.code_text(base) != _build.code_text(other)
+    assert "/* kept */" in _build.code_text(base)
+    assert re.fullmatch(r"[0-9a-f]{64}", _build.kernel_digest())
