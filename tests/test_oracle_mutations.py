@@ -178,7 +178,28 @@ def _clip_variant(kind):
     return coef
 
 
+def _clipped_step_variant(kind):
+    def step(chunks, master, m, v, p16, hyper, loss_scale, max_norm):
+        g = zs.unscaled_grad(chunks, loss_scale)
+        flag = zs.nonfinite(g)
+        sq = zs.grad_sqnorm(g)
+        if flag:
+            return zs.StepResult(True, sq, master.copy(), m.copy(), v.copy(), p16.copy())
+        gc = g * zs.clip_coefficient(sq, max_norm)
+        if kind == "norm_after_clip":
+            sq = zs.grad_sqnorm(gc)
+        elif kind == "update_unclipped":
+            gc = g
+        master1, m1, v1, p161 = zs.adamw_update(gc, master, m, v, hyper)
+        return zs.StepResult(False, sq, master1, m1, v1, p161)
+    return step
+
+
 MUTATIONS.update({
+    "clipped_step_norm_after_clip": (zs, "shard_step_clipped",
+                                     _clipped_step_variant("norm_after_clip")),
+    "clipped_step_updates_unclipped": (zs, "shard_step_clipped",
+                                       _clipped_step_variant("update_unclipped")),
     "clip_not_clamped_to_one": (zs, "clip_coefficient", _clip_variant("no_clamp")),
     "clip_by_squared_norm": (zs, "clip_coefficient", _clip_variant("squared_norm")),
     "clip_inverted": (zs, "clip_coefficient", _clip_variant("inverted")),
