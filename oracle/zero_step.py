@@ -55,6 +55,12 @@ constant-gradient closed form;
 fp16 mean -> exact rational means rounded by hand-coded binary16 rounding on
 exactly summable inputs, and identical replicas (the fp16 mean is then the
 replica itself, and the split equals the fused step bit for bit).
+
+Parity unpinned: the order of ``replica_sum`` where the sum is not exact.
+Its value is pinned wherever every order gives the same bits; the fixed
+order 0..N-1 elsewhere is a reading, since the ring's rotating order would
+round differently and no source decides.  The squared norm is pinned as
+arithmetic only; the pages define no norm.
 """
 from __future__ import annotations
 
