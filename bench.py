@@ -223,6 +223,9 @@ def main():
     two = two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, args.two_pass_steps)
     log(f"bench: two-pass {two['two_pass_ms_per_step']:.3f} ms/step, check "
         f"{two['check_ms']:.3f} ms, in-place step {two['inplace_step_ms']:.3f} ms")
+    dtp = device_two_pass(zs, d, shard, w, scaler, hp, stream, args.two_pass_steps)
+    log(f"bench: device two-pass {dtp['device_two_pass_ms_per_step']:.3f} ms/step, clipped "
+        f"{dtp['device_two_pass_clipped_ms_per_step']:.3f} ms/step")
     lit = page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, args.two_pass_steps)
     log(f"bench: page-literal split {lit['split_ms_per_step']:.3f} ms/step, fp16 mean "
         f"{lit['mean_fp16_ms']:.3f} ms, one-chunk step {lit['split_step_ms']:.3f} ms")
@@ -244,6 +247,7 @@ def main():
     extra["fused_step_pct_twin"] = 100 * k1_gbps / twin["twin_gbps"]
     extra.update(host)
     extra.update(two)
+    extra.update(dtp)
     extra.update(lit)
 
     if not args.no_flatten:
@@ -859,6 +863,34 @@ def two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
             "check_ms": check_ms, "check_gbps": 2 * N * n / (check_ms * 1e-3) / 1e9,
             "inplace_step_ms": step_ms,
             "inplace_step_gbps": w.bytes_per_param_step() * n / (step_ms * 1e-3) / 1e9}
+
+
+def device_two_pass(zs, d, shard, w, scaler, hp, stream, steps: int):
+    """The two-pass step under the device control block, on the current copy
+    in place: begin, the check (its norm partials on a fixed grid), the
+    decision, the in-place update; with no clipping, and with clipping to
+    half the gradient's norm (every step clipped).  No read-back inside the
+    loop."""
+    import torch
+    master, m, v, p16 = shard.current
+    out = {}
+    for label, clip in (("device_two_pass", 0.0), ("device_two_pass_clipped", None)):
+        ctl = zs.control_new(zs.LossScaler.create(scale=scaler.scale), int(hp.step),
+                             master.device)
+        stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper.replace(step=int(hp.step))))
+        if clip is None:
+            stepper.two_pass(d["chunks"], master, m, v, p16)       # measures the norm
+            clip = 0.5 * zs.control_read(ctl).sqnorm ** 0.5
+        ms = _timed(lambda: stepper.two_pass(d["chunks"], master, m, v, p16,
+                                             max_grad_norm=clip, stream=stream), steps)
+        c = zs.control_read(ctl)
+        assert c.error == 0 and c.skipped_steps == 0
+        if label.endswith("clipped"):
+            assert c.clip_coef < 1.0
+        hp.step = int(c.step)
+        out[f"{label}_ms_per_step"] = ms
+        out[f"{label}_params_per_s"] = w.n / (ms * 1e-3)
+    return out
 
 
 def page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
