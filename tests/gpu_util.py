@@ -92,3 +92,29 @@ def assert_matches_oracle(d: dict, want, label: str = "", max_ulp=MAX_ULP) -> di
         ulps[k] = assert_fp32_close(f"{label}{k}", d[k].cpu().numpy(), ref, max_ulp)
     ulps["p16"] = assert_fp16_close(f"{label}p16", d["p16"].cpu().numpy(), want.p16)
     return ulps
+
+
+GUARD = 4096          # bytes of canary on each side of a guarded array
+CANARY = 0xA5
+
+
+def guarded(numel: int, dtype, dev, fill=None):
+    """(buffer, tensor): a tensor of `numel` elements with GUARD bytes of the
+    CANARY byte on either side, inside one 16-byte aligned buffer; the tensor
+    is filled from `fill` if given."""
+    esize = torch.empty(0, dtype=dtype).element_size()
+    g = GUARD // esize
+    buf = torch.empty(numel + 2 * g, dtype=dtype, device=dev)
+    buf.view(torch.uint8).fill_(CANARY)
+    t = buf[g:g + numel]
+    if fill is not None:
+        t.copy_(fill)
+    return buf, t
+
+
+def guards_intact(buf: torch.Tensor, numel: int) -> bool:
+    """Both canary bands of a `guarded` buffer still hold CANARY."""
+    raw = buf.view(torch.uint8)
+    end = GUARD + numel * buf.element_size()
+    return bool((raw[:GUARD] == CANARY).all()) and bool((raw[end:] == CANARY).all())
+

@@ -7,8 +7,9 @@ that state matches the oracle's 2K steps).
 
 Guard bands: every kernel that writes a shard (in-place and out-of-place
 steps, the multi-bucket step, the fp16 mean, the accumulator, the control
-step) leaves the bytes just before and just after its output arrays as they
-were, at sizes with a ragged tail."""
+steps over a shard and over a bucket table, the traffic twin) leaves the
+bytes just before and just after its output arrays as they were, at sizes
+with a ragged tail."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +18,7 @@ import oracle.loss_scale as ols
 import oracle.zero_step as ozs
 import sharded_mixed_precision_step_amd as zs
 import workloads as wl
-from gpu_util import device, flags
+from gpu_util import device, flags, guarded, guards_intact
 
 pytestmark = pytest.mark.gpu
 
@@ -117,28 +118,8 @@ def test_resume_from_checkpoint_is_bit_identical(tmp_path):
         assert np.array_equal(x.cpu().numpy().view(bits), ref.view(bits))
 
 
-GUARD = 4096          # bytes of canary on each side of every output array
-
-
-def _guarded(numel, dtype, dev, fill=None):
-    """A tensor of `numel` elements with GUARD bytes of a canary pattern on
-    either side (the whole buffer 16-byte aligned, the tensor too)."""
-    esize = torch.empty(0, dtype=dtype).element_size()
-    g = GUARD // esize
-    buf = torch.empty(numel + 2 * g, dtype=dtype, device=dev)
-    buf.view(torch.uint8).fill_(0xA5)
-    t = buf[g:g + numel]
-    if fill is not None:
-        t.copy_(fill)
-    return buf, t
-
-
 def _assert_guards(buf, numel, label):
-    esize = buf.element_size()
-    g = GUARD // esize
-    raw = buf.view(torch.uint8)
-    assert bool((raw[:GUARD] == 0xA5).all()), f"{label}: write before the array"
-    assert bool((raw[(g + numel) * esize:] == 0xA5).all()), f"{label}: write past the array"
+    assert guards_intact(buf, numel), f"{label}: a write outside the array"
 
 
 @pytest.mark.parametrize("nn", [1, 7, 4097, 12_345])
@@ -154,7 +135,7 @@ def test_no_writes_outside_the_outputs(nn):
         out = {}
         for k in ("master", "m", "v", "p16"):
             src = torch.from_numpy(h[k]).to(dev)
-            out[k] = _guarded(nn, src.dtype, dev, None if dst_nan else src)
+            out[k] = guarded(nn, src.dtype, dev, None if dst_nan else src)
         return out
 
     # in place
@@ -181,16 +162,26 @@ def test_no_writes_outside_the_outputs(nn):
     zs.DeviceStepper(ctl2, hp).single_pass(
         chunks, (tuple(c0[k][1] for k in ("master", "m", "v", "p16")),
                  tuple(c1[k][1] for k in ("master", "m", "v", "p16"))))
+    # the bucket table under the control block, and the traffic twin
+    ctl3 = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+    t0, t1 = state(), state(dst_nan=True)
+    zs.DeviceStepper(ctl3, hp).single_pass_buckets(
+        zs.BucketSlices([(chunks, 0)]), (tuple(t0[k][1] for k in ("master", "m", "v", "p16")),
+                                         tuple(t1[k][1] for k in ("master", "m", "v", "p16"))))
+    tw_src, tw_dst = state(), state(dst_nan=True)
+    zs.zero_traffic_twin(chunks, *(tw_src[k][1] for k in ("master", "m", "v")),
+                         *(tw_dst[k][1] for k in ("master", "m", "v", "p16")))
     # the fp16 mean and the accumulator
-    mbuf, mean = _guarded(nn, torch.float16, dev)
+    mbuf, mean = guarded(nn, torch.float16, dev)
     zs.zero_reduce_mean_fp16(chunks, mean, w.loss_scale, *flags(dev))
-    abuf, acc = _guarded(nn, torch.float32, dev)
-    a16buf, amean = _guarded(nn, torch.float16, dev)
+    abuf, acc = guarded(nn, torch.float32, dev)
+    a16buf, amean = guarded(nn, torch.float16, dev)
     for i, c in enumerate(chunks):
         zs.zero_accumulate_chunk(c, i, N, acc, amean)
     torch.cuda.synchronize()
     for label, group in (("in place", s), ("out of place", dst), ("bucket table", bdst),
-                         ("control two-pass", cs), ("control single pass", c1)):
+                         ("control two-pass", cs), ("control single pass", c1),
+                         ("control bucket table", t1), ("traffic twin", tw_dst)):
         for k, (buf, _) in group.items():
             _assert_guards(buf, nn, f"{label} {k}")
     _assert_guards(mbuf, nn, "fp16 mean")
@@ -202,6 +193,6 @@ def test_no_writes_outside_the_outputs(nn):
     for k, ref in (("master", want.master), ("m", want.m), ("v", want.v), ("p16", want.p16)):
         bits = np.uint16 if ref.dtype == np.float16 else np.uint32
         for label, group in (("in place", s), ("out of place", dst), ("bucket table", bdst),
-                             ("control single pass", c1)):
+                             ("control single pass", c1), ("control bucket table", t1)):
             got = group[k][1].cpu().numpy().view(bits)
             assert np.array_equal(got, ref.view(bits)), (label, k)

@@ -7,27 +7,9 @@ import pytest
 import torch
 
 import sharded_mixed_precision_step_amd as zs
-from gpu_util import device
+from gpu_util import device, guarded, guards_intact
 
 pytestmark = pytest.mark.gpu
-
-GUARD = 4096
-
-
-def _guarded(numel, dtype, dev):
-    esize = torch.empty(0, dtype=dtype).element_size()
-    g = GUARD // esize
-    buf = torch.empty(numel + 2 * g, dtype=dtype, device=dev)
-    buf.view(torch.uint8).fill_(0x5C)
-    return buf, buf[g:g + numel]
-
-
-def _guards_intact(buf, numel):
-    raw = buf.view(torch.uint8)
-    g = GUARD // buf.element_size()
-    return bool((raw[:GUARD] == 0x5C).all()) and bool((raw[(g + numel) * buf.element_size():]
-                                                        == 0x5C).all())
-
 
 @pytest.mark.parametrize("N", [1, 3, 8, 17])
 @pytest.mark.parametrize("n", [1, 7, 8, 4097, 20_011])
@@ -39,7 +21,7 @@ def test_twin_writes_its_definition(n, N):
     print(f"case: traffic twin n={n} N={N}", flush=True)
     d_ch = [torch.from_numpy(c.view(np.float16)).to(dev) for c in ch]
     d_in = [torch.from_numpy(x.view(np.float32)).to(dev) for x in ins]
-    outs = [_guarded(n, torch.float32, dev) for _ in range(3)] + [_guarded(n, torch.float16, dev)]
+    outs = [guarded(n, torch.float32, dev) for _ in range(3)] + [guarded(n, torch.float16, dev)]
     zs.zero_traffic_twin(d_ch, *d_in, *(t for _, t in outs))
     torch.cuda.synchronize()
     h = np.zeros(n, np.uint16)
@@ -51,4 +33,4 @@ def test_twin_writes_its_definition(n, N):
     for k, ((buf, t), ref) in enumerate(zip(outs, want)):
         got = t.cpu().numpy().view(ref.dtype)
         assert np.array_equal(got, ref), k
-        assert _guards_intact(buf, n), k
+        assert guards_intact(buf, n), k
