@@ -557,6 +557,39 @@ def zero_shard_step_buckets_ctl(slices: BucketSlices, copies, hp: AdamWParams,
                                            _stream(stream)))
 
 
+class _Tiling:
+    """Bucket ranges [offset, offset + length) of an n-element state, added
+    one at a time: each must lie inside the state and overlap none before
+    it, and `complete()` tells whether they now cover it exactly."""
+
+    def __init__(self, n: int):
+        self.n = n
+        self.starts: list = []
+        self.ends: list = []
+        self.covered = 0
+
+    def add(self, offset: int, length: int) -> None:
+        import bisect
+        if offset < 0 or length < 0 or offset + length > self.n:
+            raise ValueError(f"bucket [{offset}, {offset + length}) lies outside the "
+                             f"{self.n}-element state")
+        if length == 0:
+            return
+        k = bisect.bisect_right(self.starts, offset)
+        if k > 0 and self.ends[k - 1] > offset:
+            raise ValueError(f"bucket [{offset}, {offset + length}) overlaps "
+                             f"[{self.starts[k - 1]}, {self.ends[k - 1]})")
+        if k < len(self.starts) and self.starts[k] < offset + length:
+            raise ValueError(f"bucket [{offset}, {offset + length}) overlaps "
+                             f"[{self.starts[k]}, {self.ends[k]})")
+        self.starts.insert(k, offset)
+        self.ends.insert(k, offset + length)
+        self.covered += length
+
+    def complete(self) -> bool:
+        return self.covered == self.n
+
+
 class DeviceStepper:
     """Enqueues whole steps under a control block with no read-back.  The
     update's bias corrections come from a table based at t0 and covering
@@ -594,12 +627,12 @@ class DeviceStepper:
         one decision for the whole shard (skip, loss scale, clip factor from
         the whole shard's norm, t), then one in-place update per bucket."""
         n = master.numel()
-        covered = sum(chunks[0].numel() for chunks, _ in buckets)
-        if covered != n:
-            raise ValueError(f"the buckets cover {covered} elements of a {n}-element state")
+        tiling = _Tiling(n)
         for chunks, off in buckets:
-            if off < 0 or off + chunks[0].numel() > n:
-                raise ValueError(f"bucket at {off} lies outside the {n}-element state")
+            tiling.add(int(off), chunks[0].numel())
+        if not tiling.complete():
+            raise ValueError(f"the buckets cover {tiling.covered} elements of a "
+                             f"{n}-element state")
         self._rebase()
         zero_control_begin(self.ctl, stream=stream)
         for chunks, _ in buckets:
@@ -655,20 +688,22 @@ class DeviceStepper:
         elements [offset, offset + len(chunk)), and the decision and commit
         follow the last.  The generator may refill a chunk buffer once the
         update that read it has been enqueued on the same stream.  The
-        buckets must cover the state arrays exactly once."""
+        buckets must cover the state arrays exactly once: a bucket outside
+        the state or overlapping an earlier one is refused before its update
+        is enqueued, and a shortfall after the last; either way ValueError is
+        raised before the decision, so nothing is committed."""
         self._rebase()
         n = copies[0][0].numel()
-        covered = 0
+        tiling = _Tiling(n)
         zero_control_begin(self.ctl, stream=stream)
         for chunks, off in arrivals:
             nb = chunks[0].numel()
-            if off < 0 or off + nb > n:
-                raise ValueError(f"bucket at {off} of {nb} elements lies outside the {n}-element state")
+            tiling.add(int(off), nb)      # refused before its update is enqueued
             view = tuple(tuple(t[off:off + nb] for t in cp) for cp in copies)
             zero_shard_step_out_ctl(chunks, view, self.hp, self.ctl, stream=stream)
-            covered += nb
-        if covered != n:
-            raise ValueError(f"the buckets cover {covered} elements of a {n}-element state")
+        if not tiling.complete():
+            raise ValueError(f"the buckets cover {tiling.covered} elements of a "
+                             f"{n}-element state")
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
 

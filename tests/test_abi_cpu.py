@@ -407,3 +407,32 @@ def test_kernel_digest_follows_code_not_comments():
     assert _build.code_text(base) != _build.code_text(other)
     assert "/* kept */" in _build.code_text(base)
     assert re.fullmatch(r"[0-9a-f]{64}", _build.kernel_digest())
+
+
+def test_bucket_tiling_refuses_overlaps_gaps_and_strays():
+    """The binding's check that streamed or two-pass buckets cover the state
+    exactly once: a stray or overlapping bucket is refused when it is added,
+    a gap shows as an incomplete cover, in any arrival order."""
+    t = zs._Tiling(100)
+    for off, nb in ((40, 20), (0, 8), (60, 40), (8, 32)):
+        t.add(off, nb)
+    assert t.complete()
+    t = zs._Tiling(100)
+    t.add(0, 50)
+    with pytest.raises(ValueError, match="overlaps"):
+        t.add(40, 20)                  # the left neighbour's tail
+    with pytest.raises(ValueError, match="overlaps"):
+        t.add(49, 1)
+    t.add(50, 25)
+    with pytest.raises(ValueError, match="overlaps"):
+        t.add(70, 10)                  # the right neighbour's head
+    with pytest.raises(ValueError, match="overlaps"):
+        t.add(0, 100)                  # covering several
+    with pytest.raises(ValueError, match="outside"):
+        t.add(90, 20)
+    with pytest.raises(ValueError, match="outside"):
+        t.add(-8, 8)
+    t.add(80, 0)                       # empty buckets are no-ops
+    assert not t.complete() and t.covered == 75      # [75, 100) is a gap
+    t.add(75, 25)
+    assert t.complete()

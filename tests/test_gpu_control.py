@@ -341,8 +341,9 @@ def test_streamed_buckets_single_pass_matches_oracle():
 
 
 def test_streamed_buckets_that_miss_the_state_commit_nothing():
-    """Buckets that do not cover the state raise before the decision: the
-    control block's t and current copy stay where they were."""
+    """Buckets that do not cover the state exactly once (a shortfall, a
+    stray, an overlap) raise before the decision: the control block's t and
+    current copy, and the current state, stay where they were."""
     dev = device()
     w = _workload()
     h = wl.host_shard(w, n=n, offset_seed=908)
@@ -356,6 +357,15 @@ def test_streamed_buckets_that_miss_the_state_commit_nothing():
         stepper.single_pass_streamed(iter([(half, 0)]), (a, b))
     with pytest.raises(ValueError, match="outside"):
         stepper.single_pass_streamed(iter([(chunks, 8)]), (a, b))
+    # two overlapping buckets whose lengths sum to n: refused at the second
+    third = [c[:8 * 1700] for c in chunks]
+    rest = [c[8 * 1700 - 8:] for c in chunks]
+    assert third[0].numel() + rest[0].numel() - 8 == n
+    with pytest.raises(ValueError, match="overlaps"):
+        stepper.single_pass_streamed(iter([(third, 0), (rest, 8 * 1700 - 8),
+                                           ([c[:8] for c in chunks], 0)]), (a, b))
+    with pytest.raises(ValueError, match="overlaps"):
+        stepper.two_pass_buckets([(third, 0), (rest, 8 * 1700 - 8)], *a)
     c = zs.control_read(ctl)
     assert c.cur == 0 and c.step == w.hyper.step and c.error == 0
     for x, k in zip(a, ("master", "m", "v", "p16")):
