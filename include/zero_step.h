@@ -256,7 +256,10 @@ typedef struct zero_bucket_slice {
  * of the *_out arrays, with the flag and squared norm of all slices
  * accumulated into *d_overflow / *d_sqnorm.  The work is enqueued as a few
  * launches (up to 32 slices, and up to 256 chunk pointers, per launch), not
- * one launch per bucket.  State elements outside every slice are not touched.
+ * one launch per bucket.  State elements outside every slice are not touched:
+ * a caller that makes the *_out arrays its current state afterwards (a
+ * double-buffered commit) must pass slices that cover all n_state elements,
+ * as zero_shard_step_buckets_ctl requires.
  *
  *   slices         HOST array of n_slices slices; slices must not share a
  *                  state element; a slice with n == 0 is skipped
