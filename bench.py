@@ -313,7 +313,9 @@ def bench_zero2(args, dev):
     """ZeRO-2 bucketed workload: 160 buckets of 32 decoder layers, N = 8; this
     rank owns slice 3 of every bucket (973,111,296 params).  Times, per step:
     the whole step under the device control block (begin, the update of all
-    160 slices in one zero_shard_step_buckets_ctl call, decide and commit);
+    160 slices in one zero_shard_step_buckets_ctl call, decide and commit),
+    and the same step streamed (one zero_shard_step_out_ctl per bucket, as
+    buckets arrive);
     the update alone as one zero_shard_step_buckets call, as 160
     zero_shard_step_out calls, and as one call over the contiguous shard
     (same bytes, the launch-free ideal); and the rank flattening its own 160
@@ -383,10 +385,17 @@ def bench_zero2(args, dev):
     def device_step():
         stepper.single_pass_buckets(table, copies, stream=stream)
 
+    ctl_s = zs.control_new(zs.LossScaler.create(scale=S), w.hyper.step, dev)
+    stepper_s = zs.DeviceStepper(ctl_s, zs.adamw_params(w.hyper))
+    arrivals = [([o[a:a + n] for o in owned], a) for a, n in offsets]
+
+    def device_streamed():
+        stepper_s.single_pass_streamed(iter(arrivals), copies, stream=stream)
+
     ms = {name: _timed(fn, args.steps) for name, fn in
-          (("device_step", device_step), ("multi_bucket", multi), ("per_bucket", per_bucket),
-           ("whole_shard", whole))}
-    assert zs.control_read(ctl).error == 0
+          (("device_step", device_step), ("device_streamed", device_streamed),
+           ("multi_bucket", multi), ("per_bucket", per_bucket), ("whole_shard", whole))}
+    assert zs.control_read(ctl).error == 0 and zs.control_read(ctl_s).error == 0
     step_bytes = w.bytes_per_param_step() * w.n
     log("bench: " + ", ".join(f"{k} {v:.3f} ms" for k, v in ms.items()) +
         f", flatten {flat_ms:.3f} ms")
