@@ -315,7 +315,8 @@ def bench_zero2(args, dev):
     the whole step under the device control block (begin, the update of all
     160 slices in one zero_shard_step_buckets_ctl call, decide and commit),
     and the same step streamed (one zero_shard_step_out_ctl per bucket, as
-    buckets arrive);
+    buckets arrive), on one stream and alternating over two side streams
+    (chunks already resident, so no per-bucket arrival waits);
     the update alone as one zero_shard_step_buckets call, as 160
     zero_shard_step_out calls, and as one call over the contiguous shard
     (same bytes, the launch-free ideal); and the rank flattening its own 160
@@ -392,10 +393,21 @@ def bench_zero2(args, dev):
     def device_streamed():
         stepper_s.single_pass_streamed(iter(arrivals), copies, stream=stream)
 
+    ctl_2s = zs.control_new(zs.LossScaler.create(scale=S), w.hyper.step, dev)
+    stepper_2s = zs.DeviceStepper(ctl_2s, zs.adamw_params(w.hyper))
+    sides = [torch.cuda.Stream() for _ in range(2)]
+    resident = [(ch, a, None) for ch, a in arrivals]      # chunks already in place
+
+    def device_streamed_2s():
+        stepper_2s.single_pass_streamed(iter(resident), copies, stream=stream,
+                                        side_streams=sides, track_done=False)
+
     ms = {name: _timed(fn, args.steps) for name, fn in
           (("device_step", device_step), ("device_streamed", device_streamed),
+           ("device_streamed_2s", device_streamed_2s),
            ("multi_bucket", multi), ("per_bucket", per_bucket), ("whole_shard", whole))}
-    assert zs.control_read(ctl).error == 0 and zs.control_read(ctl_s).error == 0
+    for c in (ctl, ctl_s, ctl_2s):
+        assert zs.control_read(c).error == 0
     step_bytes = w.bytes_per_param_step() * w.n
     log("bench: " + ", ".join(f"{k} {v:.3f} ms" for k, v in ms.items()) +
         f", flatten {flat_ms:.3f} ms")
@@ -490,10 +502,19 @@ def bench_streamed(args, dev):
     c = zs.control_read(ctl)
     if c.error:
         raise RuntimeError(f"step control reported error {c.error}")
+    # the same steps with the bucket updates alternating over two side streams
+    sides = [torch.cuda.Stream() for _ in range(2)]
+    resident = [(ch, off, None) for ch, off in items]     # chunks already in place
+    ms_2s = _timed(lambda: stepper.single_pass_streamed(iter(resident), (cur, nxt),
+                                                        stream=stream, side_streams=sides,
+                                                        track_done=False),
+                   args.steps, warmup=1)
+    assert zs.control_read(ctl).error == 0
     k1_bytes = w.bytes_per_param_step() * n
     k1_gbps = k1_bytes / (upd_ms * 1e-3) / 1e9
     log(f"bench: streamed device single pass {ms_per_step:.3f} ms/step, {len(w.buckets)} "
-        f"bucket updates {upd_ms:.3f} ms ({k1_gbps:.0f} GB/s), skipped {c.skipped_steps}")
+        f"bucket updates {upd_ms:.3f} ms ({k1_gbps:.0f} GB/s), skipped {c.skipped_steps}; "
+        f"over two side streams {ms_2s:.3f} ms/step")
     out = {
         "metric": METRIC,
         "value": n / (ms_per_step * 1e-3),
@@ -518,6 +539,8 @@ def bench_streamed(args, dev):
             "path": "single pass under the device control block, streamed: "
                     "zero_control_begin, one zero_shard_step_out_ctl per arriving bucket, "
                     "zero_control_decide",
+            "two_side_streams_ms_per_step": ms_2s,
+            "two_side_streams_params_per_s": n / (ms_2s * 1e-3),
             "bucket_updates_ms": upd_ms,
             "bucket_updates_gbps": k1_gbps,
             "bucket_updates_pct_peak": 100 * k1_gbps / HBM_PEAK_GBPS,

@@ -557,6 +557,9 @@ def zero_shard_step_buckets_ctl(slices: BucketSlices, copies, hp: AdamWParams,
                                            _stream(stream)))
 
 
+_ON_STREAM = object()   # a streamed bucket whose chunks arrive on the step's stream
+
+
 class _Tiling:
     """Bucket ranges [offset, offset + length) of an n-element state, added
     one at a time: each must lie inside the state and overlap none before
@@ -602,6 +605,7 @@ class DeviceStepper:
         self.hp = AdamWParams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step,
                               hp.decoupled_wd, hp.bias_correction)
         self.since_base = 0
+        self.bucket_done = None       # see single_pass_streamed
 
     def _rebase(self):
         if self.since_base >= ZERO_CTL_STEPS:
@@ -681,30 +685,102 @@ class DeviceStepper:
         comparable to the kernels.  See PreparedSinglePass."""
         return PreparedSinglePass(self, grad_chunks, copies, stream)
 
-    def single_pass_streamed(self, arrivals, copies, stream=None) -> None:
+    def single_pass_streamed(self, arrivals, copies, stream=None, side_streams=(),
+                             track_done: bool = True) -> None:
         """single_pass over a shard whose gradients arrive bucket by bucket.
         `arrivals` yields (grad_chunks, offset) in arrival order; each bucket
         is updated as it is yielded, from copy cur into the other at state
         elements [offset, offset + len(chunk)), and the decision and commit
-        follow the last.  The generator may refill a chunk buffer once the
-        update that read it has been enqueued on the same stream.  The
-        buckets must cover the state arrays exactly once: a bucket outside
-        the state or overlapping an earlier one is refused before its update
-        is enqueued, and a shortfall after the last; either way ValueError is
-        raised before the decision, so nothing is committed."""
+        follow the last.  The buckets must cover the state arrays exactly
+        once: a bucket outside the state or overlapping an earlier one is
+        refused before its update is enqueued, and a shortfall after the
+        last; either way ValueError is raised before the decision, so nothing
+        is committed.
+
+        Work runs on `stream` (the current stream if None).  With
+        `side_streams`, bucket k's update runs on side_streams[k % len], so
+        consecutive updates overlap each other's start and finish; the
+        decision waits for all of them.  A bucket yielded as (grad_chunks,
+        offset) waits, on its side stream, for everything enqueued on
+        `stream` so far (its arrival); one yielded as (grad_chunks, offset,
+        ready) waits for the event `ready` instead (recorded where its chunks
+        were produced), or for nothing if ready is None (chunks already in
+        place).  With side streams and track_done, after each bucket's update
+        is enqueued `bucket_done` holds an event recorded after it on the
+        stream that runs it, before the generator is asked for the next
+        bucket; a generator that refills a chunk buffer must first make
+        `stream` wait on the bucket_done event of the update that last read
+        that buffer.  Without side streams stream order already implies that
+        wait, and bucket_done stays None.  Side streams pay off when the updates are
+        short (tens of microseconds, as for ZeRO-2 buckets of a few million
+        params), where one update's ramp-up and drain can hide under its
+        neighbour's; for updates of milliseconds they cost a little."""
         self._rebase()
+        main = torch.cuda.current_stream() if stream is None else stream
         n = copies[0][0].numel()
         tiling = _Tiling(n)
-        zero_control_begin(self.ctl, stream=stream)
-        for chunks, off in arrivals:
-            nb = chunks[0].numel()
-            tiling.add(int(off), nb)      # refused before its update is enqueued
-            view = tuple(tuple(t[off:off + nb] for t in cp) for cp in copies)
-            zero_shard_step_out_ctl(chunks, view, self.hp, self.ctl, stream=stream)
+        # the copies are checked once; a bucket's state pointers are then the
+        # base pointers plus its offset (fp32 master, m, v; fp16 params)
+        dts = (torch.float32, torch.float32, torch.float32, torch.float16)
+        bases = []
+        for j in range(4):
+            pair = []
+            for k in range(2):
+                t = copies[k][j]
+                if t.numel() != n:
+                    raise ValueError(f"copy {k} array {j} has {t.numel()} elements, expected {n}")
+                pair.append(_dev(t, dts[j], f"copy {k} array {j}"))
+            bases.append((pair, t.element_size()))
+        ctl_ptr = _ctl(self.ctl)
+        zero_control_begin(self.ctl, stream=main)
+        used = set()
+        self.bucket_done = None
+        # one "arrived" event per side stream, re-recorded for each bucket: a
+        # wait binds to the record that precedes it, so reuse is safe
+        arrived = [torch.cuda.Event() for _ in side_streams]
+        try:
+            for k, item in enumerate(arrivals):
+                chunks, off = item[0], int(item[1])
+                ready = item[2] if len(item) > 2 else _ON_STREAM
+                nb = chunks[0].numel()
+                tiling.add(off, nb)           # refused before its update is enqueued
+                ptrs = []
+                for i, c in enumerate(chunks):
+                    if c.numel() != nb:
+                        raise ValueError(f"grad_chunks[{i}] has {c.numel()} elements, "
+                                         f"expected {nb}")
+                    ptrs.append(_dev(c, torch.float16, f"grad_chunks[{i}]"))
+                tables = [_ptr_array([p + off * es for p in pair]) for pair, es in bases]
+                run_on = main
+                if side_streams:
+                    i = k % len(side_streams)
+                    run_on = side_streams[i]
+                    if i not in used:                # first use this step: after begin
+                        arrived[i].record(main)
+                        run_on.wait_event(arrived[i])
+                    if ready is _ON_STREAM:
+                        arrived[i].record(main)
+                        run_on.wait_event(arrived[i])
+                    elif ready is not None:
+                        run_on.wait_event(ready)
+                    used.add(i)
+                _check(lib.zero_shard_step_out_ctl(_ptr_array(ptrs), len(ptrs), nb, *tables,
+                                                   ctypes.byref(self.hp), ctl_ptr,
+                                                   _stream(run_on)))
+                if side_streams and track_done:
+                    self.bucket_done = torch.cuda.Event()
+                    self.bucket_done.record(run_on)
+        finally:
+            # later work on `stream` (a decision, the next step's begin) comes
+            # after every update, also when a bucket was refused
+            for i in sorted(used):
+                joined = torch.cuda.Event()
+                joined.record(side_streams[i])
+                main.wait_event(joined)
         if not tiling.complete():
             raise ValueError(f"the buckets cover {tiling.covered} elements of a "
                              f"{n}-element state")
-        zero_control_decide(self.ctl, 0.0, True, stream=stream)
+        zero_control_decide(self.ctl, 0.0, True, stream=main)
         self.since_base += 1
 
 

@@ -285,11 +285,16 @@ def test_bucket_table_single_pass_matches_oracle():
         state = (want.master, want.m, want.v, want.p16)
 
 
-def test_streamed_buckets_single_pass_matches_oracle():
+@pytest.mark.parametrize("n_side,ready", [(0, "stream"), (2, "stream"), (2, "event")])
+def test_streamed_buckets_single_pass_matches_oracle(n_side, ready):
     """Buckets arriving one at a time through two reused chunk buffers (the
     last one ragged), each updated as it arrives, one decision per step: the
     same states as the oracle's step of the whole shard, with an overflow in
-    any one bucket skipping the whole step."""
+    any one bucket skipping the whole step.  With side streams the updates
+    alternate between two streams, and a buffer is refilled only after the
+    update that read it (its bucket_done event); each bucket's arrival is
+    either the work on the step's stream or an event the generator records
+    after refilling."""
     dev = device()
     w = _workload()
     sizes = [8 * s for s in (1, 511, 512, 513, 2048, 7)]
@@ -305,6 +310,7 @@ def test_streamed_buckets_single_pass_matches_oracle():
     stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
     bufs = [[torch.empty(max(sizes), dtype=torch.float16, device=dev) for _ in range(N)]
             for _ in range(2)]
+    sides = [torch.cuda.Stream() for _ in range(n_side)]
     state, t, cur = (h["master"], h["m"], h["v"], h["p16"]), w.hyper.step, 0
     for k, plant in enumerate(PLAN):
         S = os_.scale
@@ -314,18 +320,28 @@ def test_streamed_buckets_single_pass_matches_oracle():
             g[k % N][int(offs[3]) + 17] = np.float16(-np.inf)    # in bucket 3 only
 
         def arrivals():
+            done = {}
             for j, (o, s) in enumerate(zip(offs, sizes)):
+                if j >= 2 and done[j - 2] is not None:   # buffer j % 2: read by bucket j - 2
+                    torch.cuda.current_stream().wait_event(done[j - 2])
                 chunks = [buf[:s] for buf in bufs[j % 2]]
                 for c, src in zip(chunks, g):
                     c.copy_(torch.from_numpy(src[o:o + s]))
-                yield chunks, int(o)
+                if ready == "event":
+                    landed = torch.cuda.Event()
+                    landed.record(torch.cuda.current_stream())
+                    yield chunks, int(o), landed
+                else:
+                    yield chunks, int(o)
+                done[j] = stepper.bucket_done
 
-        stepper.single_pass_streamed(arrivals(), copies)
+        stepper.single_pass_streamed(arrivals(), copies, side_streams=sides)
         want = ozs.shard_step(g, *state, w.hyper.replace(step=t), S)
         skip = ols.update_loss_scale(os_, want.overflow)
         t += 0 if skip else 1
         c = zs.control_read(ctl)
-        print(f"case: ctl streamed buckets step {k} plant={plant} S={S}", flush=True)
+        print(f"case: ctl streamed buckets (side streams {n_side}, ready {ready}) step {k} "
+              f"plant={plant} S={S}", flush=True)
         _check_control(c, os_, t, skip, want)
         if skip:
             assert c.cur == cur
