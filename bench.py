@@ -51,9 +51,10 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_8b_shard",
                     choices=("tiny", "llama3_8b_shard", "overflow", "llama70b_shard",
-                             "zero2_bucketed"),
+                             "zero2_bucketed", "replica_sweep"),
                     help="llama3_8b_shard (default), or zero2_bucketed (160 bucket slices "
-                         "in one table), llama70b_shard (23 buckets streamed), tiny, overflow")
+                         "in one table), llama70b_shard (23 buckets streamed), tiny, overflow, "
+                         "replica_sweep (the fused step and its twin at N = 1..32)")
     ap.add_argument("--cpu-sample-slices", type=int, default=0,
                     help="CPU baseline sample: this many slices of 2^22 params "
                          "(0: the whole shard)")
@@ -155,6 +156,8 @@ def main():
         return bench_streamed(args, dev)
     if args.workload == "overflow":
         return bench_overflow(args, dev)
+    if args.workload == "replica_sweep":
+        return bench_replica_sweep(args, dev)
     w = wl.WORKLOADS[args.workload]
     n, N = w.n, w.n_replicas
     log(f"bench: workload={w.name} n={n} N={N} steps={args.steps} warmup={args.warmup}")
@@ -689,6 +692,85 @@ def bench_overflow(args, dev):
             "clean_retry_update_gbps": step_bytes / (clean_upd_ms * 1e-3) / 1e9,
             "final_scale_after_skips": c.scale,
         },
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_replica_sweep(args, dev):
+    """The fused step under the control block, and its traffic twin on the
+    same arrays, at N = 1, 2, 4, 8, 16, 32 replicas over a 250,000,000-param
+    shard (the Llama-3-8B shard's distributions): how the attainable rate
+    moves with the read share, 2N + 12 read against 14 written per param,
+    and how close the step stays to it.  Prints one JSON line."""
+    import torch
+
+    import sharded_mixed_precision_step_amd as zs
+    import workloads as wl
+
+    base = wl.LLAMA3_8B_SHARD
+    n = 250_000_000
+    stream = torch.cuda.current_stream()
+    rows = []
+    for N in (1, 2, 4, 8, 16, 32):
+        w = wl.ShardWorkload(name=f"sweep_n{N}", wid=base.wid, n=n, n_replicas=N,
+                             grad_sigma=base.grad_sigma, loss_scale=base.loss_scale,
+                             hyper=base.hyper, m_sigma=base.m_sigma, v_sigma=base.v_sigma)
+        d = wl.device_shard(w, dev)
+        cur = (d["master"], d["m"], d["v"], d["p16"])
+        nxt = tuple(torch.empty_like(t) for t in cur)
+        ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
+        stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+        ev_step, ev_twin = [], []
+        for k in range(args.warmup + args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            stepper._rebase()
+            zs.zero_control_begin(ctl, stream=stream)
+            e[0].record(stream)
+            zs.zero_shard_step_out_ctl(d["chunks"], (cur, nxt), stepper.hp, ctl, stream=stream)
+            e[1].record(stream)
+            zs.zero_control_decide(ctl, 0.0, False, stream=stream)   # keep reading cur
+            stepper.since_base += 1
+            e[2].record(stream)
+            zs.zero_traffic_twin(d["chunks"], *cur[:3], *nxt, stream=stream)
+            e[3].record(stream)
+            if k >= args.warmup:
+                ev_step.append((e[0], e[1]))
+                ev_twin.append((e[2], e[3]))
+        torch.cuda.synchronize()
+        assert zs.control_read(ctl).error == 0
+        step_ms = sorted(a.elapsed_time(b) for a, b in ev_step)[len(ev_step) // 2]
+        twin_ms = sorted(a.elapsed_time(b) for a, b in ev_twin)[len(ev_twin) // 2]
+        nbytes = w.bytes_per_param_step() * n
+        rows.append({"replicas": N, "bytes_per_param": w.bytes_per_param_step(),
+                     "step_ms": step_ms, "step_gbps": nbytes / (step_ms * 1e-3) / 1e9,
+                     "twin_ms": twin_ms, "twin_gbps": nbytes / (twin_ms * 1e-3) / 1e9,
+                     "step_pct_twin": 100 * twin_ms / step_ms})
+        log(f"bench: N={N:2d} step {step_ms:.3f} ms ({rows[-1]['step_gbps']:.0f} GB/s), "
+            f"twin {twin_ms:.3f} ms ({rows[-1]['twin_gbps']:.0f} GB/s)")
+        del d, cur, nxt
+        torch.cuda.empty_cache()
+    ref = next(r for r in rows if r["replicas"] == 8)
+    out = {
+        "metric": METRIC,
+        "value": n / (ref["step_ms"] * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ref["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded device draws; fp16 grads, fp32 state)",
+        "config": {"workload": "replica_sweep", "shard_params": n,
+                   "replicas": [r["replicas"] for r in rows]},
+        "roofline": {"bound": "hbm", "achieved": ref["step_gbps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": ref["step_gbps"] / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "cpu_baseline": None,
+        "extra": {"sweep": rows,
+                  "note": "value, ms_per_step and roofline are the N = 8 row (fused step only)"},
     }
     print(json.dumps(out), flush=True)
 
