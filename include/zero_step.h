@@ -462,7 +462,9 @@ int zero_shard_step_buckets_ctl(const zero_bucket_slice* slices, int32_t n_slice
  * accesses of zero_shard_step_out with the same arguments (the same vector
  * loads and stores of the same arrays, in the same tiles and launch shape),
  * with integer XORs in place of the step's arithmetic.  Timed beside the step,
- * it gives the bandwidth that access pattern reaches on the device.  Per
+ * it gives the bandwidth that access pattern reaches on the device: a
+ * reference, not a bound (the same accesses issued at other times can run
+ * faster or slower, depending on where the arrays sit in HBM).  Per
  * element j, with h = chunk_0[j] ^ ... ^ chunk_{N-1}[j] (binary16 bit
  * patterns) zero-extended to 32 bits against fp32 bit patterns:
  *   master_out[j] = master_in[j] ^ exp_avg_in[j] ^ exp_avg_sq_in[j] ^ h,

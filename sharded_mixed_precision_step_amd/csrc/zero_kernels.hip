@@ -24,7 +24,7 @@
 // 64-wide wave instruction moves 1 KiB of one array, fully coalesced.  The
 // kernels that write run one block per tile (a one-shot grid: 4096 params
 // per block for the step); the check runs a grid-stride loop over a resident
-// grid with streaming loads.  Both launch shapes were chosen by measurement
+// grid.  Chunk loads are streaming (non-temporal) everywhere.  Both launch shapes were chosen by measurement
 // on MI355X: one-shot tiles sustain the most bandwidth for the kernels that
 // write, while the read-only check does best as a resident loop.  The
 // overflow flag and the squared norm are reduced per wave with lane
@@ -46,8 +46,13 @@ typedef float f8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
+// Every kernel reads a gradient chunk exactly once, so chunk loads are
+// non-temporal (streaming): measured on MI355X against the same arrays, this
+// runs the fused step 2-3 %, the fp16 mean 2.5-5 % and the arrival fold
+// 1.5-2.5 % faster than plain loads.  The state arrays are not read this way:
+// streaming their loads, or any store, measured slower.
 __device__ __forceinline__ f8 load_widen8(const uint16_t* base, int64_t pack) {
-    const h8 h = *reinterpret_cast<const h8*>(base + pack * kPack);
+    const h8 h = __builtin_nontemporal_load(reinterpret_cast<const h8*>(base + pack * kPack));
     return __builtin_convertvector(h, f8);  // binary16 -> binary32 is exact
 }
 
@@ -307,11 +312,6 @@ __global__ __launch_bounds__(kBlock) void bucket_step_kernel(
     if constexpr (REDUCE) publish(bad, sq, d_overflow, d_sqnorm);
 }
 
-__device__ __forceinline__ f8 load_widen8_nt(const uint16_t* base, int64_t pack) {
-    const h8 h = __builtin_nontemporal_load(reinterpret_cast<const h8*>(base + pack * kPack));
-    return __builtin_convertvector(h, f8);
-}
-
 // The check reads only the chunks, once: a grid-stride loop over a grid of
 // kCheckBlocksPerCU blocks per CU, with non-temporal (streaming) loads.
 // The loss-scale scalars of S read from a control block: multiply by 1/S
@@ -348,9 +348,9 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     double sq = 0.0;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < packs;
          i += stride) {
-        f8 s = load_widen8_nt(chunks.p[0], i);
+        f8 s = load_widen8(chunks.p[0], i);
 #pragma unroll
-        for (int c = 1; c < nc; ++c) s += load_widen8_nt(chunks.p[c], i);
+        for (int c = 1; c < nc; ++c) s += load_widen8(chunks.p[c], i);
 #pragma unroll
         for (int e = 0; e < kPack; ++e) {
             const float g = unscaled_mean(s[e], gs);

@@ -2,13 +2,15 @@
 //
 // traffic_twin_kernel makes exactly the memory accesses of the out-of-place
 // fused step (shard_step_kernel) over the same arrays: the same 16-byte
-// vector loads of the N fp16 chunks and of the three fp32 state inputs, the
-// same 16-byte stores of the three fp32 state outputs and the fp16 params,
-// in the same one-shot wave-contiguous tiles and launch shape, and the same
-// scalar tail in the last block.  Its arithmetic is a few integer XORs per
-// element instead of the replica sum, unscale and AdamW update.  Timed beside
-// the step on the same arrays, it gives the bandwidth the step's access
-// pattern can reach on the device at hand, with nothing to hide.
+// vector loads of the N fp16 chunks (non-temporal) and of the three fp32
+// state inputs, the same 16-byte stores of the three fp32 state outputs and
+// the fp16 params, in the same one-shot wave-contiguous tiles and launch
+// shape, and the same scalar tail in the last block.  Its arithmetic is a
+// few integer XORs per element instead of the replica sum, unscale and AdamW
+// update.  Timed beside the step on the same arrays, it gives the bandwidth
+// that access pattern reaches on the device at hand with no arithmetic to
+// hide (a reference, not a bound: the two kernels issue the same accesses
+// at different times, and in some placements the step is the faster).
 //
 // Per element j, with h = chunk_0[j] ^ chunk_1[j] ^ ... ^ chunk_{N-1}[j]
 // (binary16 bit patterns) zero-extended to 32 bits where it meets fp32 bits:
@@ -24,17 +26,22 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
+// One chunk's 16-byte vector, loaded non-temporally like the step's chunk
+// loads.
+__device__ __forceinline__ u16x8 chunk8(const uint16_t* chunk, int64_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(chunk + i * kPack));
+}
+
 // h of pack i: the XOR of the N chunks' 16-byte vectors.
 template <int NC>
 __device__ __forceinline__ u16x8 chunk_xor8(const uint16_t* const* chunks, int n_chunks,
                                             int64_t i) {
-    u16x8 h = *reinterpret_cast<const u16x8*>(chunks[0] + i * kPack);
+    u16x8 h = chunk8(chunks[0], i);
     if constexpr (NC > 0) {
 #pragma unroll
-        for (int c = 1; c < NC; ++c) h ^= *reinterpret_cast<const u16x8*>(chunks[c] + i * kPack);
+        for (int c = 1; c < NC; ++c) h ^= chunk8(chunks[c], i);
     } else {
-        for (int c = 1; c < n_chunks; ++c)
-            h ^= *reinterpret_cast<const u16x8*>(chunks[c] + i * kPack);
+        for (int c = 1; c < n_chunks; ++c) h ^= chunk8(chunks[c], i);
     }
     return h;
 }
