@@ -19,6 +19,12 @@ and so is the step's traffic twin (the same loads and stores with XORs for
 arithmetic), whose rate is the ceiling of the step's access pattern on the
 device at hand.
 
+Before timing, the shard's 16 arrays go through the placement search of
+sharded_mixed_precision_step_amd.placement (each array re-allocated and kept
+where the step runs faster; contents unchanged), as a training run would do
+once at start-up.  `extra.placement` gives the two-direction step time before
+and after; `--no-placement` times the arrays where torch put them.
+
 Prints one JSON line.  `value` is params/s of the whole step.  `roofline`
 rates the fused update kernel, the dominant one, by its algorithmic bytes
 (2N + 24 + 2 per param) over its average duration measured with HIP events
@@ -62,6 +68,9 @@ def parse_args():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 copy kernel (counter calibration)")
     ap.add_argument("--no-flatten", action="store_true")
+    ap.add_argument("--no-placement", action="store_true",
+                    help="time the arrays where torch allocated them, without the "
+                         "placement search")
     ap.add_argument("--two-pass-steps", type=int, default=10,
                     help="steps of the two-pass path (check, then in-place step), "
                          "timed after the main loop for comparison")
@@ -173,7 +182,24 @@ def main():
             f"({cpu['seconds']:.1f} s)")
 
     stream = torch.cuda.current_stream()
-    shard = zs.DoubleBufferedShard(d["master"], d["m"], d["v"], d["p16"])
+    spare = tuple(torch.empty_like(d[k]) for k in ("master", "m", "v", "p16"))
+    placed = None
+    if not args.no_placement:
+        from sharded_mixed_precision_step_amd import placement
+        chunks, copies, rep = placement.place_shard(
+            d["chunks"], ((d["master"], d["m"], d["v"], d["p16"]), spare), w.hyper,
+            w.loss_scale, stream=stream)
+        d["chunks"] = chunks
+        d["master"], d["m"], d["v"], d["p16"] = copies[0]
+        spare = copies[1]
+        del chunks, copies
+        placed = {"initial_ms_two_steps": rep.initial_ms, "final_ms_two_steps": rep.final_ms,
+                  "gain": rep.gain, "trials": rep.trials, "kept_trials": rep.kept,
+                  "seconds": rep.seconds}
+        log(f"bench: placement search {rep.seconds:.1f} s, {rep.trials} trials, kept "
+            f"{rep.kept}: two steps {rep.initial_ms:.3f} -> {rep.final_ms:.3f} ms")
+    shard = zs.DoubleBufferedShard(d["master"], d["m"], d["v"], d["p16"], spare=spare)
+    del spare
     ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
     stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
     fused_events = []
@@ -245,6 +271,7 @@ def main():
         "fused_step_gbps": k1_gbps, "fused_step_pct_peak": 100 * k1_gbps / HBM_PEAK_GBPS,
         "step_gbps": k1_bytes / (ms_per_step * 1e-3) / 1e9,
         "skipped_steps": skipped,
+        "placement": placed if placed is not None else "allocation as made (--no-placement)",
     }
     extra.update(twin)
     extra["fused_step_pct_twin"] = 100 * k1_gbps / twin["twin_gbps"]
