@@ -725,7 +725,7 @@ hipError_t step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const Gr
                      double* d_sqnorm, hipStream_t stream) {
     const int64_t grid = step_grid(n);
     hipLaunchKernelGGL((shard_step_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, as, st, d_overflow,
+                       dim3(kBlock), kStepLdsReserve, stream, chunks, n_chunks, n, gs, as, st, d_overflow,
                        d_sqnorm);
     return hipGetLastError();
 }
@@ -736,7 +736,7 @@ hipError_t bucket_impl(const BucketTable& t, int n_chunks, const GradScalars& gs
                        double* d_sqnorm, hipStream_t stream) {
     const int64_t grid = t.tile_start[t.count];
     hipLaunchKernelGGL((bucket_step_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), 0, stream, t, n_chunks, gs, as, st, d_overflow, d_sqnorm);
+                       dim3(kBlock), kStepLdsReserve, stream, t, n_chunks, gs, as, st, d_overflow, d_sqnorm);
     return hipGetLastError();
 }
 
@@ -757,7 +757,7 @@ hipError_t ctl_step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, cons
                          zero_step_control* ctl, hipStream_t stream) {
     const int64_t grid = step_grid(n);
     hipLaunchKernelGGL((ctl_step_kernel<NC, SINGLE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, as, tab, sc, ctl);
+                       dim3(kBlock), kStepLdsReserve, stream, chunks, n_chunks, n, gs, as, tab, sc, ctl);
     return hipGetLastError();
 }
 
@@ -767,7 +767,7 @@ hipError_t bucket_ctl_impl(const BucketTable& t, int n_chunks, const GradScalars
                            zero_step_control* ctl, hipStream_t stream) {
     const int64_t grid = t.tile_start[t.count];
     hipLaunchKernelGGL(bucket_ctl_step_kernel<NC>, dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), 0, stream, t, n_chunks, gs, as, tab, sc, ctl);
+                       dim3(kBlock), kStepLdsReserve, stream, t, n_chunks, gs, as, tab, sc, ctl);
     return hipGetLastError();
 }
 
