@@ -24,9 +24,11 @@
 // 64-wide wave instruction moves 1 KiB of one array, fully coalesced.  The
 // kernels that write run one block per tile (a one-shot grid: 4096 params
 // per block for the step); the check runs a grid-stride loop over a resident
-// grid.  Chunk loads are streaming (non-temporal) everywhere.  Both launch shapes were chosen by measurement
-// on MI355X: one-shot tiles sustain the most bandwidth for the kernels that
-// write, while the read-only check does best as a resident loop.  The
+// grid.  Chunk loads are streaming (non-temporal) everywhere.  Both launch
+// shapes were chosen by measurement on MI355X: one-shot tiles sustain the
+// most bandwidth for the kernels that write, while the read-only check does
+// best as a resident loop.  Step blocks with a constant replica count also
+// reserve unused LDS so that two share a CU (zero_internal.h).  The
 // overflow flag and the squared norm are reduced per wave with lane
 // shuffles, across the block's four waves in LDS, and published once per
 // block: the flag by an atomic OR where it is set; the norm by an atomic add
@@ -725,8 +727,8 @@ hipError_t step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const Gr
                      double* d_sqnorm, hipStream_t stream) {
     const int64_t grid = step_grid(n);
     hipLaunchKernelGGL((shard_step_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), kStepLdsReserve, stream, chunks, n_chunks, n, gs, as, st, d_overflow,
-                       d_sqnorm);
+                       dim3(kBlock), step_lds_reserve<NC>(), stream, chunks, n_chunks, n, gs, as,
+                       st, d_overflow, d_sqnorm);
     return hipGetLastError();
 }
 
@@ -736,7 +738,8 @@ hipError_t bucket_impl(const BucketTable& t, int n_chunks, const GradScalars& gs
                        double* d_sqnorm, hipStream_t stream) {
     const int64_t grid = t.tile_start[t.count];
     hipLaunchKernelGGL((bucket_step_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), kStepLdsReserve, stream, t, n_chunks, gs, as, st, d_overflow, d_sqnorm);
+                       dim3(kBlock), step_lds_reserve<NC>(), stream, t, n_chunks, gs, as, st,
+                       d_overflow, d_sqnorm);
     return hipGetLastError();
 }
 
@@ -757,7 +760,8 @@ hipError_t ctl_step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, cons
                          zero_step_control* ctl, hipStream_t stream) {
     const int64_t grid = step_grid(n);
     hipLaunchKernelGGL((ctl_step_kernel<NC, SINGLE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), kStepLdsReserve, stream, chunks, n_chunks, n, gs, as, tab, sc, ctl);
+                       dim3(kBlock), step_lds_reserve<NC>(), stream, chunks, n_chunks, n, gs, as,
+                       tab, sc, ctl);
     return hipGetLastError();
 }
 
@@ -767,7 +771,8 @@ hipError_t bucket_ctl_impl(const BucketTable& t, int n_chunks, const GradScalars
                            zero_step_control* ctl, hipStream_t stream) {
     const int64_t grid = t.tile_start[t.count];
     hipLaunchKernelGGL(bucket_ctl_step_kernel<NC>, dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), kStepLdsReserve, stream, t, n_chunks, gs, as, tab, sc, ctl);
+                       dim3(kBlock), step_lds_reserve<NC>(), stream, t, n_chunks, gs, as, tab, sc,
+                       ctl);
     return hipGetLastError();
 }
 

@@ -140,15 +140,15 @@ hipError_t launch_traffic_twin(const ChunkTable& chunks, int n_chunks, int64_t n
     switch (n_chunks) {
 #define ZERO_TWIN_CASE(K)                                                                     \
     case K:                                                                                   \
-        hipLaunchKernelGGL(traffic_twin_kernel<K>, grid, block, kStepLdsReserve, stream,      \
-                           chunks, n_chunks, n, st);                                          \
+        hipLaunchKernelGGL(traffic_twin_kernel<K>, grid, block, step_lds_reserve<K>(),        \
+                           stream, chunks, n_chunks, n, st);                                  \
         break;
         ZERO_TWIN_CASE(1) ZERO_TWIN_CASE(2) ZERO_TWIN_CASE(3) ZERO_TWIN_CASE(4)
         ZERO_TWIN_CASE(8) ZERO_TWIN_CASE(16)
 #undef ZERO_TWIN_CASE
         default:
-            hipLaunchKernelGGL(traffic_twin_kernel<0>, grid, block, kStepLdsReserve, stream,
-                               chunks, n_chunks, n, st);
+            hipLaunchKernelGGL(traffic_twin_kernel<0>, grid, block, step_lds_reserve<0>(),
+                               stream, chunks, n_chunks, n, st);
     }
     return hipGetLastError();
 }
