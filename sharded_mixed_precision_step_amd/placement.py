@@ -37,11 +37,12 @@ import dataclasses
 import random
 import statistics
 import time
-from typing import List, Sequence
+from typing import Callable, List, Optional, Sequence
 
 import torch
 
 from . import zero_shard_step_out, adamw_params, AdamWParams
+
 
 @dataclasses.dataclass
 class PlacementReport:
@@ -77,6 +78,34 @@ def _time_both(chunks, copies, hp, loss_scale, flag, sq, stream, reps) -> float:
     return sum(statistics.median(a.elapsed_time(b) for a, b in t) for t in times)
 
 
+def _search(best_set: list, timed: Callable[[list], float],
+            make_set: Callable[[list], Optional[list]], release: Callable[[], None], *,
+            trials: int, budget_s: float, min_gain: float,
+            clock: Callable[[], float] = time.perf_counter):
+    """The search itself, apart from allocation and timing.  `timed(set)`
+    gives a set's time; `make_set(set)` returns a new set with the same
+    contents, or None when memory runs out; `release()` returns the memory of
+    dropped sets.  Returns (best_set, initial_ms, best_ms, trials_done,
+    kept), `kept` listing the 1-based trials whose set was kept."""
+    t_start = clock()
+    best = timed(best_set)
+    initial = best
+    done, kept = 0, []
+    while done < trials and clock() - t_start < budget_s:
+        new = make_set(best_set)
+        if new is None:
+            release()
+            break
+        t = timed(new)
+        done += 1
+        if t < best * (1.0 - min_gain):
+            best, best_set = t, new
+            kept.append(done)
+        del new
+        release()
+    return best_set, initial, best, done, kept
+
+
 def place_shard(chunks: Sequence[torch.Tensor], copies, hp, loss_scale: float, *,
                 trials: int = 12, budget_s: float = 30.0, min_gain: float = 0.005,
                 max_spacer: int = 4 << 30, reps: int = 2, seed: int = 0, stream=None):
@@ -90,8 +119,9 @@ def place_shard(chunks: Sequence[torch.Tensor], copies, hp, loss_scale: float, *
     the step in both directions.  The set with the lowest time is kept (a
     new set must beat the kept one by more than `min_gain`, relative).  The
     search stops after `trials` trials, after `budget_s` seconds, or at the
-    first allocation that fails; while it runs it needs room for two sets,
-    the spacers and a saved copy of copy 0.
+    first allocation that fails.  While it runs it needs room for three
+    sets (the caller's, the kept one and the trial), the spacers and a
+    saved copy of copy 0.
 
     Returns (chunks, copies, report) with the same contents in possibly new
     tensors.  The caller must use the returned tensors and drop its
@@ -104,8 +134,8 @@ def place_shard(chunks: Sequence[torch.Tensor], copies, hp, loss_scale: float, *
         hp = adamw_params(hp)
     rng = random.Random(seed)
     n_chunks = len(chunks)
-    best_set = list(chunks) + list(copies[0]) + list(copies[1])
-    dev = best_set[0].device
+    first_set = list(chunks) + list(copies[0]) + list(copies[1])
+    dev = first_set[0].device
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     sq = torch.zeros(1, dtype=torch.float64, device=dev)
     t_start = time.perf_counter()
@@ -117,32 +147,26 @@ def place_shard(chunks: Sequence[torch.Tensor], copies, hp, loss_scale: float, *
         c, cp = split(arrs)
         return _time_both(c, cp, hp, loss_scale, flag, sq, stream, reps)
 
+    def make_set(cur):
+        spacers, new = [], []
+        try:
+            for t in cur:
+                spacers.append(torch.empty(1 + rng.randrange(max_spacer), dtype=torch.uint8,
+                                           device=dev))
+                new.append(torch.empty_like(t))
+        except torch.OutOfMemoryError:
+            return None
+        del spacers
+        for dst, src in zip(new, cur):
+            dst.copy_(src)
+        return new
+
     with torch.cuda.stream(stream):
-        saved = [t.clone() for t in best_set[n_chunks:n_chunks + 4]]
-        best = timed(best_set)
-        initial = best
-        done, kept = 0, []
-        while done < trials and time.perf_counter() - t_start < budget_s:
-            spacers, new = [], []
-            try:
-                for t in best_set:
-                    spacers.append(torch.empty(1 + rng.randrange(max_spacer), dtype=torch.uint8,
-                                               device=dev))
-                    new.append(torch.empty_like(t))
-            except torch.OutOfMemoryError:
-                del spacers, new
-                torch.cuda.empty_cache()
-                break
-            del spacers
-            for dst, src in zip(new, best_set):
-                dst.copy_(src)
-            t = timed(new)
-            done += 1
-            if t < best * (1.0 - min_gain):
-                best, best_set = t, new
-                kept.append(done)
-            del new
-            torch.cuda.empty_cache()
+        saved = [t.clone() for t in first_set[n_chunks:n_chunks + 4]]
+        best_set, initial, best, done, kept = _search(
+            first_set, timed, make_set, torch.cuda.empty_cache, trials=trials,
+            budget_s=budget_s, min_gain=min_gain)
+        del first_set
         for dst, src in zip(best_set[n_chunks:n_chunks + 4], saved):
             dst.copy_(src)
         del saved
