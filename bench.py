@@ -71,6 +71,8 @@ def parse_args():
     ap.add_argument("--no-placement", action="store_true",
                     help="time the arrays where torch allocated them, without the "
                          "placement search")
+    ap.add_argument("--placement-trials", type=int, default=12,
+                    help="trial sets of the placement search (default 12)")
     ap.add_argument("--two-pass-steps", type=int, default=10,
                     help="steps of the two-pass path (check, then in-place step), "
                          "timed after the main loop for comparison")
@@ -188,7 +190,8 @@ def main():
         from sharded_mixed_precision_step_amd import placement
         chunks, copies, rep = placement.place_shard(
             d["chunks"], ((d["master"], d["m"], d["v"], d["p16"]), spare), w.hyper,
-            w.loss_scale, stream=stream)
+            w.loss_scale, trials=args.placement_trials,
+            budget_s=max(30.0, 2.5 * args.placement_trials), stream=stream)
         d["chunks"] = chunks
         d["master"], d["m"], d["v"], d["p16"] = copies[0]
         spare = copies[1]
