@@ -394,7 +394,21 @@ def bench_zero2(args, dev):
     owned = wl.device_chunks(w, dev)
     st = wl.device_state(w, dev)
     cur = (st["master"], st["m"], st["v"], st["p16"])
+    del st
     out = tuple(torch.empty_like(t) for t in cur)
+    placed = "allocation as made (--no-placement)"
+    if not args.no_placement:
+        # the slices are views into the N replica buffers and the two state
+        # copies, so the whole-shard search places them all at once
+        from sharded_mixed_precision_step_amd import placement
+        owned, (cur, out), rep = placement.place_shard(
+            owned, (cur, out), w.hyper, S, trials=args.placement_trials,
+            budget_s=max(30.0, 2.5 * args.placement_trials), stream=stream)
+        placed = {"initial_ms_two_steps": rep.initial_ms, "final_ms_two_steps": rep.final_ms,
+                  "gain": rep.gain, "trials": rep.trials, "kept_trials": rep.kept,
+                  "seconds": rep.seconds}
+        log(f"bench: placement search {rep.seconds:.1f} s, {rep.trials} trials, kept "
+            f"{rep.kept}: two steps {rep.initial_ms:.3f} -> {rep.final_ms:.3f} ms")
     table = zs.BucketSlices([([o[a:a + n] for o in owned], a) for a, n in offsets])
     views = [([o[a:a + n] for o in owned], tuple(t[a:a + n] for t in cur[:3]),
               tuple(t[a:a + n] for t in out)) for a, n in offsets]
@@ -465,6 +479,7 @@ def bench_zero2(args, dev):
             **{f"{k}_gbps": step_bytes / (v * 1e-3) / 1e9 for k, v in ms.items()},
             "flatten_own_buckets_ms": flat_ms,
             "flatten_own_buckets_gbps": flat_bytes / (flat_ms * 1e-3) / 1e9,
+            "placement": placed,
         },
     }
     print(json.dumps(out_line), flush=True)
