@@ -14,17 +14,21 @@ constexpr int kPack = 8;           // params per 16-byte fp16 vector ("pack")
 constexpr int kWaveSpan = 2;       // packs per lane in a step tile
 constexpr int kTilePacks = kBlock * kWaveSpan;  // packs per step tile (one block)
 constexpr int kCheckBlocksPerCU = 6;            // resident blocks of the check kernel
-// Dynamic LDS that a block of the fused step (and of its traffic twin)
-// reserves and does not use, when the replica count is a template constant.
-// With 160 KiB of LDS per CU it lets at most two step blocks share a CU (two
-// waves per SIMD) where the registers alone allow four at N = 8.  Those
-// kernels issue all of a lane's loads before any arithmetic, so two waves
-// per SIMD keep enough bytes in flight.  Measured on MI355X, same arrays,
-// alternating launches: at N = 8, 0.9-2.6 % faster than four blocks per CU
-// (0.3-0.6 % with three, slower with one); at N = 16, within 1 %.  The
-// generic kernel (NC = 0, a runtime loop over the chunks) waits on each
-// chunk's load in turn and needs the extra waves to hide it: capped, it ran
-// 35 % slower at N = 32, so it reserves nothing.
+// Dynamic LDS that a block of the one-shot kernels that write (the fused
+// step, its traffic twin, the fp16 mean and the arrival fold) reserves and
+// does not use, when the replica count is a template constant.  With
+// 160 KiB of LDS per CU it lets at most two such blocks share a CU (two
+// waves per SIMD) where the registers alone allow four (the step at N = 8)
+// or eight (the mean, the fold).  These kernels issue all of a lane's loads
+// before any arithmetic, so two waves per SIMD keep enough bytes in flight,
+// and fewer streams compete at once.  Measured on MI355X, same arrays,
+// alternating launches, against the registers' own limit: the step at N = 8
+// 0.9-2.6 % faster (0.3-0.6 % with three per CU, slower with one), at
+// N = 16 within 1 %; the fp16 mean at N = 8 1.8-3.6 % faster; one middle
+// arrival of the fold 6.6-7.0 % faster.  The generic kernels (NC = 0, a
+// runtime loop over the chunks) wait on each chunk's load in turn and need
+// the extra waves to hide it: the step, capped, ran 35 % slower at N = 32,
+// so they reserve nothing.
 constexpr unsigned kStepLdsReserve = 60 * 1024;
 template <int NC>
 constexpr unsigned step_lds_reserve() { return NC > 0 ? kStepLdsReserve : 0u; }

@@ -749,8 +749,8 @@ hipError_t mean_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const Gr
                      hipStream_t stream) {
     const int64_t grid = mean_tiles(n);
     hipLaunchKernelGGL((reduce_mean_kernel<NC, REDUCE>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, mean16, d_overflow,
-                       d_sqnorm);
+                       dim3(kBlock), step_lds_reserve<NC>(), stream, chunks, n_chunks, n, gs,
+                       mean16, d_overflow, d_sqnorm);
     return hipGetLastError();
 }
 
@@ -883,20 +883,20 @@ hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const G
     const dim3 grid(static_cast<unsigned>(step_tiles(n))), block(kBlock);
     switch (mode) {
         case 0:
-            hipLaunchKernelGGL(accumulate_kernel<0>, grid, block, 0, stream, chunk, n, gs, acc,
-                               mean16);
+            hipLaunchKernelGGL(accumulate_kernel<0>, grid, block, kStepLdsReserve, stream, chunk,
+                               n, gs, acc, mean16);
             break;
         case 1:
-            hipLaunchKernelGGL(accumulate_kernel<1>, grid, block, 0, stream, chunk, n, gs, acc,
-                               mean16);
+            hipLaunchKernelGGL(accumulate_kernel<1>, grid, block, kStepLdsReserve, stream, chunk,
+                               n, gs, acc, mean16);
             break;
         case 2:
-            hipLaunchKernelGGL(accumulate_kernel<2>, grid, block, 0, stream, chunk, n, gs, acc,
-                               mean16);
+            hipLaunchKernelGGL(accumulate_kernel<2>, grid, block, kStepLdsReserve, stream, chunk,
+                               n, gs, acc, mean16);
             break;
         default:
-            hipLaunchKernelGGL(accumulate_kernel<3>, grid, block, 0, stream, chunk, n, gs, acc,
-                               mean16);
+            hipLaunchKernelGGL(accumulate_kernel<3>, grid, block, kStepLdsReserve, stream, chunk,
+                               n, gs, acc, mean16);
             break;
     }
     return hipGetLastError();
