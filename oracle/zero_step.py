@@ -57,8 +57,9 @@ exactly summable inputs, and identical replicas (the fp16 mean is then the
 replica itself, and the split equals the fused step bit for bit).
 
 Parity unpinned: the order of ``replica_sum`` where the sum is not exact.
-Its value is pinned wherever every order gives the same bits; the fixed
-order 0..N-1 elsewhere is a reading, since the ring's rotating order would
+Its value is pinned wherever every order gives the same bits, and bounded
+elsewhere (within the recursive-summation error bound of the exact sum);
+the fixed order 0..N-1 is a reading, since the ring's rotating order would
 round differently and no source decides.  The squared norm is pinned as
 arithmetic only; the pages define no norm.
 """

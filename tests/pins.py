@@ -96,6 +96,35 @@ def pin_replica_sum_matches_ring():
                 assert np.array_equal(_bits32(row), _bits32(want)), (n_rep, n)
 
 
+def pin_replica_sum_error_bound():
+    """On inexact inputs (fp16 values of mixed magnitudes whose fp32 partial
+    sums round), the oracle's sum lies within the error bound of recursive
+    summation (Higham, Accuracy and Stability of Numerical Algorithms,
+    section 4.2): |s - S| <= (N - 1) u sum |x_i|, u = 2^-24, where S is the
+    exact sum.  For N <= 16 fp16 terms S is exact in float64 (the terms span
+    at most 2^-24..2^16).  The ring's rotating order, the pages' own, meets
+    the same bound, so the two orders differ by at most twice it; the
+    order itself is a reading, the value is not."""
+    rng = np.random.default_rng(seed_of(97))
+    u = 2.0 ** -24
+    for n_rep in (2, 3, 5, 8, 16):
+        n = 4096
+        chunks = []
+        for _ in range(n_rep):
+            mag = np.exp2(rng.integers(-20, 12, n)).astype(np.float64)
+            x = (rng.standard_normal(n) * mag).astype(np.float16)
+            chunks.append(x)
+        exact = np.sum([c.astype(np.float64) for c in chunks], axis=0)
+        bound = (n_rep - 1) * u * np.sum([np.abs(c.astype(np.float64)) for c in chunks], axis=0)
+        s = zs.replica_sum(chunks).astype(np.float64)
+        assert np.all(np.abs(s - exact) <= bound), n_rep
+        rows, _ = _ring_sum(chunks)
+        for row in rows:
+            assert np.all(np.abs(row.astype(np.float64) - exact) <= bound), n_rep
+        # the inputs are inexact: some partial sums do round
+        assert np.any(s != exact), n_rep
+
+
 def pin_ring_traffic():
     """Each rank sends 2 (N - 1) messages of psi / N elements (about 2 psi)."""
     for n_rep in (2, 3, 4, 8):
