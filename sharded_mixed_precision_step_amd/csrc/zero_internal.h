@@ -14,6 +14,10 @@ constexpr int kPack = 8;           // params per 16-byte fp16 vector ("pack")
 constexpr int kWaveSpan = 2;       // packs per lane in a step tile
 constexpr int kTilePacks = kBlock * kWaveSpan;  // packs per step tile (one block)
 constexpr int kCheckBlocksPerCU = 6;            // resident blocks of the check kernel
+// Packs per thread per trip of the check's grid-stride loop, their loads
+// issued together: 1-2.3 % faster than one at a time on MI355X (same
+// arrays), with the same partial sums bit for bit.
+constexpr int kCheckUnroll = 4;
 // Dynamic LDS that a block of the one-shot kernels that write (the fused
 // step, its traffic twin, the fp16 mean and the arrival fold) reserves and
 // does not use, when the replica count is a template constant.  With

@@ -350,8 +350,30 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     const int nc = NC > 0 ? NC : n_chunks;
     bool bad = false;
     double sq = 0.0;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < packs;
-         i += stride) {
+    // kCheckUnroll of the thread's packs per trip, all their loads issued
+    // before the arithmetic; the packs are then taken in the same order as
+    // one at a time, so every partial sum keeps its bits
+    int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    for (; i + (kCheckUnroll - 1) * stride < packs; i += kCheckUnroll * stride) {
+        f8 s[kCheckUnroll];
+#pragma unroll
+        for (int u = 0; u < kCheckUnroll; ++u) s[u] = load_widen8(chunks.p[0], i + u * stride);
+#pragma unroll
+        for (int c = 1; c < nc; ++c) {
+#pragma unroll
+            for (int u = 0; u < kCheckUnroll; ++u) s[u] += load_widen8(chunks.p[c], i + u * stride);
+        }
+#pragma unroll
+        for (int u = 0; u < kCheckUnroll; ++u) {
+#pragma unroll
+            for (int e = 0; e < kPack; ++e) {
+                const float g = unscaled_mean(s[u][e], gs);
+                bad |= nonfinite(g);
+                sq += static_cast<double>(g) * static_cast<double>(g);
+            }
+        }
+    }
+    for (; i < packs; i += stride) {
         f8 s = load_widen8(chunks.p[0], i);
 #pragma unroll
         for (int c = 1; c < nc; ++c) s += load_widen8(chunks.p[c], i);
