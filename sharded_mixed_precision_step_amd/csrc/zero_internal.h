@@ -19,23 +19,28 @@ constexpr int kCheckBlocksPerCU = 6;            // resident blocks of the check 
 // arrays), with the same partial sums bit for bit.
 constexpr int kCheckUnroll = 4;
 // Dynamic LDS that a block of the one-shot kernels that write (the fused
-// step, its traffic twin, the fp16 mean and the arrival fold) reserves and
-// does not use, when the replica count is a template constant.  With
-// 160 KiB of LDS per CU it lets at most two such blocks share a CU (two
-// waves per SIMD) where the registers alone allow four (the step at N = 8)
-// or eight (the mean, the fold).  These kernels issue all of a lane's loads
-// before any arithmetic, so two waves per SIMD keep enough bytes in flight,
-// and fewer streams compete at once.  Measured on MI355X, same arrays,
-// alternating launches, against the registers' own limit: the step at N = 8
-// 0.9-2.6 % faster (0.3-0.6 % with three per CU, slower with one), at
-// N = 16 within 1 %; the fp16 mean at N = 8 1.8-3.6 % faster; one middle
-// arrival of the fold 6.6-7.0 % faster.  The generic kernels (NC = 0, a
-// runtime loop over the chunks) wait on each chunk's load in turn and need
-// the extra waves to hide it: the step, capped, ran 35 % slower at N = 32,
-// so they reserve nothing.
+// step, its traffic twin, the fp16 mean) reserves and does not use, when
+// the replica count is a template constant.  With 160 KiB of LDS per CU it
+// lets at most two such blocks share a CU (two waves per SIMD) where the
+// registers alone allow four (the step at N = 8) or eight (the mean).  These
+// kernels issue all of a lane's loads before any arithmetic, so two waves
+// per SIMD keep enough bytes in flight, and fewer streams compete at once.
+// Measured on MI355X, same arrays, alternating launches, against the
+// registers' own limit: the step at N = 8 0.9-2.6 % faster (0.3-0.6 % with
+// three per CU, slower with one), at N = 16 within 1 %; the fp16 mean at
+// N = 8 1.8-3.6 % faster (0.7-1.5 % with four per CU).  The generic kernels
+// (NC = 0, a runtime loop over the chunks) wait on each chunk's load in
+// turn and need the extra waves to hide it: the step, capped, ran 35 %
+// slower at N = 32, so they reserve nothing.
 constexpr unsigned kStepLdsReserve = 60 * 1024;
 template <int NC>
 constexpr unsigned step_lds_reserve() { return NC > 0 ? kStepLdsReserve : 0u; }
+// The arrival fold moves fewer bytes per lane (one chunk, at most one
+// accumulator) and does best with four blocks per CU.  Against the
+// registers' eight: the first arrival 4.0-4.5 % faster, the last 4.6-4.9 %,
+// a middle one 6.2-6.6 %.  Two per CU match four on a middle arrival but run
+// the first 20 % and the last 14 % slower than eight.
+constexpr unsigned kFoldLdsReserve = 36 * 1024;
 constexpr int kMeanSpan = 4;       // packs per lane in an fp16-mean tile
 constexpr int kMeanTilePacks = kBlock * kMeanSpan;  // packs per fp16-mean tile (one block)
 constexpr int kFlattenBatch = 32;  // tensors per flatten launch (kernel-argument table)

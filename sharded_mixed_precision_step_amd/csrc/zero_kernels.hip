@@ -27,8 +27,8 @@
 // grid.  Chunk loads are streaming (non-temporal) everywhere.  Both launch
 // shapes were chosen by measurement on MI355X: one-shot tiles sustain the
 // most bandwidth for the kernels that write, while the read-only check does
-// best as a resident loop.  Step blocks with a constant replica count also
-// reserve unused LDS so that two share a CU (zero_internal.h).  The
+// best as a resident loop.  Blocks of the kernels that write also reserve
+// unused LDS so that fewer share a CU (zero_internal.h).  The
 // overflow flag and the squared norm are reduced per wave with lane
 // shuffles, across the block's four waves in LDS, and published once per
 // block: the flag by an atomic OR where it is set; the norm by an atomic add
@@ -912,19 +912,19 @@ hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const G
     const dim3 grid(static_cast<unsigned>(step_tiles(n))), block(kBlock);
     switch (mode) {
         case 0:
-            hipLaunchKernelGGL(accumulate_kernel<0>, grid, block, kStepLdsReserve, stream, chunk,
+            hipLaunchKernelGGL(accumulate_kernel<0>, grid, block, kFoldLdsReserve, stream, chunk,
                                n, gs, acc, mean16);
             break;
         case 1:
-            hipLaunchKernelGGL(accumulate_kernel<1>, grid, block, kStepLdsReserve, stream, chunk,
+            hipLaunchKernelGGL(accumulate_kernel<1>, grid, block, kFoldLdsReserve, stream, chunk,
                                n, gs, acc, mean16);
             break;
         case 2:
-            hipLaunchKernelGGL(accumulate_kernel<2>, grid, block, kStepLdsReserve, stream, chunk,
+            hipLaunchKernelGGL(accumulate_kernel<2>, grid, block, kFoldLdsReserve, stream, chunk,
                                n, gs, acc, mean16);
             break;
         default:
-            hipLaunchKernelGGL(accumulate_kernel<3>, grid, block, kStepLdsReserve, stream, chunk,
+            hipLaunchKernelGGL(accumulate_kernel<3>, grid, block, kFoldLdsReserve, stream, chunk,
                                n, gs, acc, mean16);
             break;
     }
