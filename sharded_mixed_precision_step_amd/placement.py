@@ -29,7 +29,8 @@ copy 0 is saved first and restored at the end; copy 1 is left holding the
 last timing step's output, which the first real step overwrites.
 
 Allocation goes through torch's caching allocator; the search empties its
-cache after each rejected trial so that the next trial gets fresh memory.
+cache after every trial, so that the next trial gets fresh memory and a
+rejected set's memory goes back to the driver.
 """
 from __future__ import annotations
 
