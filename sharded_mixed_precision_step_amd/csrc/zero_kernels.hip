@@ -696,7 +696,8 @@ __global__ __launch_bounds__(kBlock) void bucket_flatten_kernel(FlattenTable tab
             if (i >= packs) continue;
             const int64_t e = i * kPack;
             if (src_vec && e + kPack <= d.numel) {
-                val[u] = *reinterpret_cast<const u16x8*>(d.src + e);
+                // each source gradient is read once: a streaming load
+                val[u] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(d.src + e));
             } else {
 #pragma unroll
                 for (int k = 0; k < kPack; ++k) val[u][k] = (e + k < d.numel) ? d.src[e + k] : 0;
@@ -1012,7 +1013,7 @@ hipError_t launch_bucket_flatten(const FlattenTable& table, int count, int64_t m
     if (count <= 0 || max_slot_len <= 0) return hipSuccess;
     const int64_t gx = (max_slot_len + kFlattenTile - 1) / kFlattenTile;
     hipLaunchKernelGGL(bucket_flatten_kernel, dim3(static_cast<unsigned>(gx), count), dim3(kBlock),
-                       0, stream, table, bucket);
+                       kFlattenLdsReserve, stream, table, bucket);
     return hipGetLastError();
 }
 
