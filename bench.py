@@ -101,6 +101,24 @@ def read_traffic(digest: str, n: int):
     return (vals["fetch_bytes_per_param"] + vals["write_bytes_per_param"]) * n
 
 
+# One GPU's share of a GPU host's cores: the oracle's thread pool never takes
+# more, however many cores the process can see (the host is shared by the
+# jobs of its other GPUs).
+ORACLE_MAX_THREADS = 16
+
+
+def oracle_threads() -> int:
+    return max(1, min(ORACLE_MAX_THREADS, len(os.sched_getaffinity(0))))
+
+
+def host_cpus() -> dict:
+    """The host's cores as this process sees them, beside the pool's size."""
+    return {"host_cpus_visible": len(os.sched_getaffinity(0)),
+            "host_cpu_count": os.cpu_count(),
+            "cores_rule": f"thread pool of min({ORACLE_MAX_THREADS}, visible cores): one "
+                          f"GPU's share of the host"}
+
+
 def cpu_baseline(dev_shard, w, slices: int):
     """The CPU oracle as it stands, on the first `slices` x 2^22 params of the
     shard (host copies of the device inputs), over a thread pool."""
@@ -114,7 +132,7 @@ def cpu_baseline(dev_shard, w, slices: int):
                 master=dev_shard["master"][:total].cpu().numpy(),
                 m=dev_shard["m"][:total].cpu().numpy(), v=dev_shard["v"][:total].cpu().numpy(),
                 p16=dev_shard["p16"][:total].cpu().numpy())
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = oracle_threads()
 
     def run(k):
         sl = slice(k * piece, min((k + 1) * piece, total))
@@ -136,7 +154,7 @@ def cpu_baseline(dev_shard, w, slices: int):
     dt1 = time.perf_counter() - t0
     n1 = min(single * piece, total)
     return {"value": total / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
-            "seconds": dt,
+            **host_cpus(), "seconds": dt,
             "single_core_value": n1 / dt1,
             "single_core_sample": f"the first {n1} params ({single} slices of 2^22), one thread",
             "sample": (f"{'whole' if total == w.n else 'first ' + str(total) + ' params of the'} "
@@ -185,6 +203,9 @@ def main():
 
     stream = torch.cuda.current_stream()
     spare = tuple(torch.empty_like(d[k]) for k in ("master", "m", "v", "p16"))
+    unplaced = fused_step_median(zs, d["chunks"], (d["master"], d["m"], d["v"], d["p16"]),
+                                 spare, w, stream)
+    log(f"bench: fused step where torch allocated the arrays: median {unplaced:.3f} ms")
     placed = None
     if not args.no_placement:
         from sharded_mixed_precision_step_amd import placement
@@ -213,7 +234,7 @@ def main():
         decision, loss-scale move and commit on the device.  Nothing is read
         back, so the host enqueues the next step at once."""
         stepper._rebase()
-        zs.zero_control_begin(ctl, stream=stream)
+        zs.zero_control_begin(ctl, stepper.hp, stream=stream)
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
@@ -275,6 +296,9 @@ def main():
         "step_gbps": k1_bytes / (ms_per_step * 1e-3) / 1e9,
         "skipped_steps": skipped,
         "placement": placed if placed is not None else "allocation as made (--no-placement)",
+        "unplaced_fused_step_median_ms": unplaced,
+        "unplaced_fused_step_pct_peak":
+            100 * w.bytes_per_param_step() * n / (unplaced * 1e-3) / 1e9 / HBM_PEAK_GBPS,
     }
     extra.update(twin)
     extra["fused_step_pct_twin"] = 100 * k1_gbps / twin["twin_gbps"]
@@ -287,6 +311,7 @@ def main():
         extra.update(bench_flatten(zs, wl, dev, stream))
     extra.update(copy_ceiling(dev, stream))
     extra["fused_step_pct_copy_ceiling"] = 100 * k1_gbps / extra["copy_ceiling_gbps"]
+    extra["fused_step_pct_add_ceiling"] = 100 * k1_gbps / extra["add_ceiling_gbps"]
     extra.update(tiny_graph(dev))
     if args.calibrate_copy:
         calibration_copy(dev)
@@ -631,7 +656,7 @@ def bench_overflow(args, dev):
 
     def timed_single(ctl, steps, events):
         for k in range(steps):
-            zs.zero_control_begin(ctl, stream=stream)
+            zs.zero_control_begin(ctl, hp, stream=stream)
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
             zs.zero_shard_step_out_ctl(d["chunks"], (cur, spare), hp, ctl, stream=stream)
@@ -652,7 +677,7 @@ def bench_overflow(args, dev):
 
     def timed_two_pass(ctl, steps, events):
         for k in range(steps):
-            zs.zero_control_begin(ctl, stream=stream)
+            zs.zero_control_begin(ctl, hp, stream=stream)
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
             zs.zero_overflow_check_ctl(d["chunks"], ctl, stream=stream)
@@ -686,7 +711,7 @@ def bench_overflow(args, dev):
     def timed_clean(ctl, steps, events):
         for k in range(steps):
             stepper3._rebase()
-            zs.zero_control_begin(ctl, stream=stream)
+            zs.zero_control_begin(ctl, stepper3.hp, stream=stream)
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
             zs.zero_shard_step_out_ctl(d["chunks"], (cur, spare), stepper3.hp, ctl,
@@ -751,6 +776,7 @@ def bench_replica_sweep(args, dev):
 
     import sharded_mixed_precision_step_amd as zs
     import workloads as wl
+    from sharded_mixed_precision_step_amd import twin as zt
 
     base = wl.LLAMA3_8B_SHARD
     n = 250_000_000
@@ -769,14 +795,14 @@ def bench_replica_sweep(args, dev):
         for k in range(args.warmup + args.steps):
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             stepper._rebase()
-            zs.zero_control_begin(ctl, stream=stream)
+            zs.zero_control_begin(ctl, stepper.hp, stream=stream)
             e[0].record(stream)
             zs.zero_shard_step_out_ctl(d["chunks"], (cur, nxt), stepper.hp, ctl, stream=stream)
             e[1].record(stream)
             zs.zero_control_decide(ctl, 0.0, False, stream=stream)   # keep reading cur
             stepper.since_base += 1
             e[2].record(stream)
-            zs.zero_traffic_twin(d["chunks"], *cur[:3], *nxt, stream=stream)
+            zt.zero_traffic_twin(d["chunks"], *cur[:3], *nxt, stream=stream)
             e[3].record(stream)
             if k >= args.warmup:
                 ev_step.append((e[0], e[1]))
@@ -829,7 +855,7 @@ def cpu_baseline_buckets(w, items, state, sampled):
     import oracle.zero_step as ozs
 
     piece = 1 << 22
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = oracle_threads()
     seconds, params = 0.0, 0
     for b in sampled:
         chunks, off = items[b]
@@ -851,12 +877,36 @@ def cpu_baseline_buckets(w, items, state, sampled):
         del ch, stt, results
     rate = params / seconds
     return {"value": rate, "unit": "params/s", "cores": threads, "kind": "oracle",
-            "seconds": seconds, "params": params,
+            **host_cpus(), "seconds": seconds, "params": params,
             "extrapolated_whole_shard_seconds": w.n / rate,
             "sample": (f"buckets {', '.join(map(str, sampled))} of the {w.name} shard "
                        f"({params} params, N={w.n_replicas} replicas, 2^22-param slices): "
                        f"overflow check and AdamW update; the whole-shard time is "
                        f"extrapolated at this rate")}
+
+
+def fused_step_median(zs, chunks, cur, nxt, w, stream, reps: int = 9) -> float:
+    """Median over `reps` launches (after two untimed) of the fused update
+    under a control block of its own, from `cur` into `nxt`, on the arrays as
+    given: the decision never flips the copy, so `cur` is only read."""
+    import torch
+    ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, cur[0].device)
+    hp = zs.adamw_params(w.hyper)
+    ev = []
+    for k in range(reps + 2):
+        zs.zero_control_begin(ctl, hp, stream=stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        zs.zero_shard_step_out_ctl(chunks, (cur, nxt), hp, ctl, stream=stream)
+        e[1].record(stream)
+        zs.zero_control_decide(ctl, 0.0, False, stream=stream)
+        if k >= 2:
+            ev.append(e)
+    torch.cuda.synchronize()
+    c = zs.control_read(ctl)
+    assert c.error == 0 and c.skip == 0
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2]
 
 
 def traffic_twin(zs, d, shard, w, stream, reps: int = 20):
@@ -865,14 +915,16 @@ def traffic_twin(zs, d, shard, w, stream, reps: int = 20):
     its rate is what the step's access pattern reaches on this device.
     Average and median of HIP-event timings of single launches."""
     import torch
+
+    from sharded_mixed_precision_step_amd import twin as zt
     src, dst = shard.current, shard.other
     for _ in range(3):
-        zs.zero_traffic_twin(d["chunks"], *src[:3], *dst, stream=stream)
+        zt.zero_traffic_twin(d["chunks"], *src[:3], *dst, stream=stream)
     ev = []
     for _ in range(reps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         e[0].record(stream)
-        zs.zero_traffic_twin(d["chunks"], *src[:3], *dst, stream=stream)
+        zt.zero_traffic_twin(d["chunks"], *src[:3], *dst, stream=stream)
         e[1].record(stream)
         ev.append(e)
     torch.cuda.synchronize()
@@ -964,7 +1016,7 @@ def tiny_graph(dev, steps: int = 200):
         if flushed:
             flush.fill_(float(k))
         st._rebase()
-        zs.zero_control_begin(ctl, stream=stream)
+        zs.zero_control_begin(ctl, st.hp, stream=stream)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         e[0].record(stream)
         zs.zero_shard_step_out_ctl(d["chunks"], copies, st.hp, ctl, stream=stream)
@@ -1119,24 +1171,44 @@ def page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
 
 
 def copy_ceiling(dev, stream, reps: int = 5):
-    """A plain 4 GiB elementwise copy (torch's vectorized elementwise kernel,
-    dst = -src): the bandwidth a two-array stream reaches on this device
-    (read + write bytes over time)."""
+    """Plain streams on 4 GiB fp32 arrays, each timed over `reps` launches
+    with HIP events on the launch stream: the bandwidth this device reaches
+    for a given read/write mix, beside which the step's rate is read.
+      read only   zero_stream_read (16-byte non-temporal loads, resident grid)
+      write only  torch's fill
+      copy 1:1    torch's elementwise dst = -src
+      add 2:1     torch's elementwise c = a + b (two arrays read, one written:
+                  the step's mix at N = 8 is 28 bytes read to 14 written)
+    Each figure is bytes moved over time."""
     import torch
-    src = torch.empty(1 << 30, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    src.fill_(1.0)
-    torch.neg(src, out=dst)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(stream)
-    for _ in range(reps):
-        torch.neg(src, out=dst)
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / reps
-    nbytes = 2 * src.numel() * 4
-    del src, dst
-    return {"copy_ceiling_gbps": nbytes / (ms * 1e-3) / 1e9}
+
+    from sharded_mixed_precision_step_amd import twin as zt
+    a = torch.empty(1 << 30, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    c = torch.empty_like(a)
+    a.fill_(1.0)
+    b.fill_(2.0)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    nb = a.numel() * 4
+
+    def timed(fn, nbytes):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return nbytes / (ev[0].elapsed_time(ev[1]) / reps * 1e-3) / 1e9
+
+    out = {
+        "read_ceiling_gbps": timed(lambda: zt.zero_stream_read(a, sink, stream=stream), nb),
+        "write_ceiling_gbps": timed(lambda: c.fill_(3.0), nb),
+        "copy_ceiling_gbps": timed(lambda: torch.neg(a, out=c), 2 * nb),
+        "add_ceiling_gbps": timed(lambda: torch.add(a, b, out=c), 3 * nb),
+    }
+    del a, b, c
+    return out
 
 
 def bench_flatten(zs, wl, dev, stream, reps: int = 10):

@@ -114,11 +114,19 @@ typedef struct zero_step_control {
     float clip_coef;         /* factor on g of this step's update (1: none)      */
     int32_t overflow;        /* non-finite flag of this step                     */
     int32_t skip;            /* the decision: 1 = the update was skipped         */
-    int32_t error;           /* bit 0: step_used was outside the update's table
-                                of bias corrections and nothing was updated;
-                                sticky until the host clears it                 */
+    int32_t error;           /* bit 0: a step's t lay outside the table of bias
+                                corrections its begin was given (see
+                                table_miss); sticky until the host clears it   */
     int32_t check_ran;       /* set by zero_overflow_check_ctl: check_part
                                 holds partials to fold and later to clear     */
+    float bc1_used;          /* 1 - beta1^t and 1 - beta2^t of t = step_used,   */
+    float bc2_used;          /* looked up by zero_control_begin                 */
+    int32_t table_miss;      /* 1: this step's t was outside begin's table; the
+                                step is skipped (skip = 1 from begin on) and
+                                changes nothing: no update, and the decision
+                                leaves t, the scale, good_steps, skipped_steps
+                                and cur as they were                           */
+    int32_t pad_;
     /* this step's partial sums of g^2 from the fused update kernels: block b
        adds its sum into sqnorm_part[ZERO_NORM_STRIDE * (b % ZERO_NORM_SLOTS)];
        the other elements stay 0 */
@@ -363,6 +371,40 @@ int zero_bucket_flatten(const void* const* tensors, const int64_t* numels,
                         void* bucket, int64_t bucket_capacity,
                         int64_t* offsets_out, void* stream);
 
+/* One bucket of zero_bucket_flatten_batch: the arguments zero_bucket_flatten
+ * takes for that bucket.  HOST struct. */
+typedef struct zero_flatten_bucket {
+    const void* const* tensors; /* HOST array of n_tensors DEVICE pointers to fp16
+                                   data, 2-byte aligned; NULL only if numel is 0 */
+    const int64_t* numels;      /* HOST int64[n_tensors], each >= 0              */
+    int64_t* offsets_out;       /* HOST int64[n_tensors + 1]: the slot offsets,
+                                   then the padded length L                     */
+    void* bucket;               /* DEVICE fp16, 16-byte aligned                  */
+    int64_t bucket_capacity;    /* elements                                      */
+    int32_t n_tensors;          /* >= 0                                          */
+    int32_t pad_;
+} zero_flatten_bucket;
+
+/*
+ * zero_bucket_flatten_batch -- zero_bucket_flatten for many buckets in few
+ * launches.
+ *
+ * A ZeRO-2 rank fills a bucket after another as backward proceeds (ZeRO
+ * notes, rkmt.cn/news/44736, section "Deepspeed ZeRO-2", sync step); when
+ * several are ready together, one call flattens them all.  Bucket k gets
+ * exactly what zero_bucket_flatten(buckets[k].tensors, buckets[k].numels,
+ * buckets[k].n_tensors, align, pad_multiple, buckets[k].bucket,
+ * buckets[k].bucket_capacity, buckets[k].offsets_out, stream) gives it; the
+ * tensor slots of all buckets are enqueued together, up to 64 slots per
+ * launch.  Every bucket is validated (and its offsets_out filled) before
+ * anything is enqueued, in bucket order: the first failure is returned and
+ * no bucket is written.  No bucket may share a byte with another bucket or
+ * with any tensor of the batch.  Returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN,
+ * ZERO_ERANGE (a bucket's capacity below its L) or ZERO_EHIP.
+ */
+int zero_bucket_flatten_batch(const zero_flatten_bucket* buckets, int32_t n_buckets,
+                              int64_t align, int64_t pad_multiple, void* stream);
+
 /*
  * zero_update_loss_scale -- host-only, synchronous dynamic loss scaling.
  *
@@ -390,7 +432,18 @@ int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_
  *
  * zero_control_begin: start a step: overflow = 0, sqnorm = 0 and its
  * partial sums cleared, skip = 0, clip_coef = 1, scale_used = scale,
- * step_used = step.
+ * step_used = step, and the step's bias corrections looked up.  hp (HOST,
+ * validated as for zero_shard_step) gives the table: hp->step is its base
+ * t0, and it holds 1 - beta^t (1 - beta^t evaluated in fp64 from the fp32
+ * beta and rounded to fp32, as for the host calls; 1 when
+ * hp->bias_correction is 0) for t = t0 .. t0 + ZERO_CTL_STEPS - 1.  If the
+ * block's t lies outside it (a table miss) the step is void from the start:
+ * table_miss = 1, skip = 1, bit 0 of error set; the check and the update
+ * kernels of the step then return without writing anything, and
+ * zero_control_decide leaves t, the scale, good_steps, skipped_steps and
+ * cur unchanged (only sqnorm, of nothing, is written).  The caller keeps t0
+ * within reach: t grows by at most one per step enqueued since it last
+ * read the block.
  *
  * zero_overflow_check_ctl: zero_overflow_check with S = d_ctl->scale_used,
  * the flag into d_ctl->overflow and the squared norm into d_ctl->check_part:
@@ -411,28 +464,28 @@ int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_
  * zero_shard_step_ctl: the two-pass update, in place: if d_ctl->skip is set
  * nothing is touched; otherwise zero_shard_step with S = scale_used,
  * g multiplied by clip_coef (one fp32 multiply) before the moments, and the
- * bias corrections of t = step_used.
+ * block's bias corrections bc1_used and bc2_used.
  *
  * zero_shard_step_out_ctl: the single-pass update: zero_shard_step_out from
  * copy cur into copy 1 - cur (masters[2], exp_avgs[2], exp_avg_sqs[2],
  * params_fp16[2]: HOST arrays of two DEVICE pointers each), with
- * S = scale_used and the bias corrections of t = step_used, accumulating the
- * flag and the squared-norm slots (sqnorm_part) of d_ctl.  Follow it with zero_control_decide(...,
- * flip_copy = 1): a clean step then makes the written copy current.
+ * S = scale_used and the block's bias corrections, accumulating the flag
+ * and the squared-norm slots (sqnorm_part) of d_ctl; nothing is written if
+ * d_ctl->skip is set (only a table miss sets it before the decision).
+ * Follow it with zero_control_decide(..., flip_copy = 1): a clean step then
+ * makes the written copy current.
  *
- * Bias corrections: hp->step is the base t0 of a table the call computes
- * for t = t0 .. t0 + ZERO_CTL_STEPS - 1 (1 - beta^t in fp64, rounded to fp32,
- * as for the host calls); a step whose step_used falls outside it sets bit 0
- * of d_ctl->error and updates nothing.  The caller keeps t0 within reach:
- * t can only have grown by the number of steps enqueued since it last read
- * the block.  Other arguments are as for the calls without _ctl; d_ctl is
+ * In the update calls hp supplies lr, beta1, beta2, eps, weight_decay and
+ * decoupled_wd (validated as for zero_shard_step); the bias corrections
+ * always come from the block, so their hp->step and hp->bias_correction are
+ * not used.  Other arguments are as for the calls without _ctl; d_ctl is
  * DEVICE, 8-byte aligned.  Each returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN or
  * ZERO_EHIP.
  */
 #define ZERO_CTL_STEPS 64
 
 int zero_control_init(zero_step_control* ctl, const zero_loss_scaler* scaler, int64_t step);
-int zero_control_begin(zero_step_control* d_ctl, void* stream);
+int zero_control_begin(zero_step_control* d_ctl, const zero_adamw_params* hp, void* stream);
 int zero_overflow_check_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
                             zero_step_control* d_ctl, void* stream);
 int zero_control_decide(zero_step_control* d_ctl, float max_grad_norm, int32_t flip_copy,
@@ -456,28 +509,6 @@ int zero_shard_step_buckets_ctl(const zero_bucket_slice* slices, int32_t n_slice
                                 float* const* exp_avgs, float* const* exp_avg_sqs,
                                 void* const* params_fp16, const zero_adamw_params* hp,
                                 zero_step_control* d_ctl, void* stream);
-
-/*
- * zero_traffic_twin -- a measurement aid, not part of the step: the memory
- * accesses of zero_shard_step_out with the same arguments (the same vector
- * loads and stores of the same arrays, in the same tiles and launch shape),
- * with integer XORs in place of the step's arithmetic.  Timed beside the step,
- * it gives the bandwidth that access pattern reaches on the device: a
- * reference, not a bound (the same accesses issued at other times can run
- * faster or slower, depending on where the arrays sit in HBM).  Per
- * element j, with h = chunk_0[j] ^ ... ^ chunk_{N-1}[j] (binary16 bit
- * patterns) zero-extended to 32 bits against fp32 bit patterns:
- *   master_out[j] = master_in[j] ^ exp_avg_in[j] ^ exp_avg_sq_in[j] ^ h,
- *   exp_avg_out[j] = exp_avg_in[j] ^ h, exp_avg_sq_out[j] = exp_avg_sq_in[j] ^ h,
- *   param_fp16_out[j] = h ^ (low 16 bits of master_in[j]).
- * Arguments, alignment and overlap rules are those of zero_shard_step_out
- * (no loss scale, hyperparameters or flags).  Returns ZERO_OK, ZERO_EINVAL,
- * ZERO_EALIGN or ZERO_EHIP.
- */
-int zero_traffic_twin(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
-                      const float* master_in, const float* exp_avg_in,
-                      const float* exp_avg_sq_in, float* master_out, float* exp_avg_out,
-                      float* exp_avg_sq_out, void* param_fp16_out, void* stream);
 
 /* Text of the last error reported by a call on this thread ("" if none). */
 const char* zero_last_error_string(void);

@@ -32,10 +32,11 @@ ZERO_MAX_CHUNKS = 64
 
 EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
             "zero_shard_step_buckets", "zero_reduce_mean_fp16", "zero_accumulate_chunk",
-            "zero_bucket_flatten", "zero_update_loss_scale", "zero_control_init",
+            "zero_bucket_flatten", "zero_bucket_flatten_batch", "zero_update_loss_scale",
+            "zero_control_init",
             "zero_control_begin", "zero_overflow_check_ctl", "zero_control_decide",
             "zero_shard_step_ctl", "zero_shard_step_out_ctl", "zero_shard_step_buckets_ctl",
-            "zero_traffic_twin", "zero_last_error_string")
+            "zero_last_error_string")
 ZERO_CTL_STEPS = 64
 ZERO_NORM_SLOTS = 16
 ZERO_NORM_STRIDE = 8
@@ -79,8 +80,18 @@ class StepControl(ctypes.Structure):
                 ("scale_used", ctypes.c_float), ("clip_coef", ctypes.c_float),
                 ("overflow", ctypes.c_int32), ("skip", ctypes.c_int32),
                 ("error", ctypes.c_int32), ("check_ran", ctypes.c_int32),
+                ("bc1_used", ctypes.c_float), ("bc2_used", ctypes.c_float),
+                ("table_miss", ctypes.c_int32), ("pad_", ctypes.c_int32),
                 ("sqnorm_part", ctypes.c_double * (ZERO_NORM_SLOTS * ZERO_NORM_STRIDE)),
                 ("check_part", ctypes.c_double * ZERO_CHECK_PARTS)]
+
+
+class FlattenBucketC(ctypes.Structure):
+    _fields_ = [("tensors", ctypes.POINTER(ctypes.c_void_p)),
+                ("numels", ctypes.POINTER(ctypes.c_int64)),
+                ("offsets_out", ctypes.POINTER(ctypes.c_int64)), ("bucket", ctypes.c_void_p),
+                ("bucket_capacity", ctypes.c_int64), ("n_tensors", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)]
 
 
 class BucketSliceC(ctypes.Structure):
@@ -115,11 +126,12 @@ def _load() -> ctypes.CDLL:
     lib.zero_accumulate_chunk.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     lib.zero_bucket_flatten.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), i32, i64, i64,
                                         vp, i64, ctypes.POINTER(ctypes.c_int64), vp]
+    lib.zero_bucket_flatten_batch.argtypes = [ctypes.POINTER(FlattenBucketC), i32, i64, i64, vp]
     lib.zero_update_loss_scale.argtypes = [ctypes.POINTER(LossScaler), i32,
                                            ctypes.POINTER(ctypes.c_int32)]
     lib.zero_control_init.argtypes = [ctypes.POINTER(StepControl), ctypes.POINTER(LossScaler),
                                       i64]
-    lib.zero_control_begin.argtypes = [vp, vp]
+    lib.zero_control_begin.argtypes = [vp, ctypes.POINTER(AdamWParams), vp]
     lib.zero_overflow_check_ctl.argtypes = [pp, i32, i64, vp, vp]
     lib.zero_control_decide.argtypes = [vp, ctypes.c_float, i32, vp]
     lib.zero_shard_step_ctl.argtypes = [pp, i32, i64, vp, vp, vp, vp, ctypes.POINTER(AdamWParams),
@@ -128,7 +140,6 @@ def _load() -> ctypes.CDLL:
                                             ctypes.POINTER(AdamWParams), vp, vp]
     lib.zero_shard_step_buckets_ctl.argtypes = [ctypes.POINTER(BucketSliceC), i32, i32, i64, pp,
                                                 pp, pp, pp, ctypes.POINTER(AdamWParams), vp, vp]
-    lib.zero_traffic_twin.argtypes = [pp, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.zero_last_error_string.argtypes = []
     lib.zero_last_error_string.restype = ctypes.c_char_p
     for name in EXPORTED[:-1]:
@@ -337,31 +348,6 @@ def zero_accumulate_chunk(chunk: torch.Tensor, index: int, n_chunks: int,
                                      _stream(stream)))
 
 
-def zero_traffic_twin(grad_chunks: Sequence[torch.Tensor], master_in: torch.Tensor,
-                      exp_avg_in: torch.Tensor, exp_avg_sq_in: torch.Tensor,
-                      master_out: torch.Tensor, exp_avg_out: torch.Tensor,
-                      exp_avg_sq_out: torch.Tensor, param_fp16_out: torch.Tensor,
-                      stream=None) -> None:
-    """The fused step's memory accesses with XORs for arithmetic: a bandwidth
-    reference for the step's access pattern (see zero_step.h)."""
-    ptrs = [_dev(c, torch.float16, f"grad_chunks[{i}]") for i, c in enumerate(grad_chunks)]
-    n = master_in.numel()
-    for name, t in (("exp_avg_in", exp_avg_in), ("exp_avg_sq_in", exp_avg_sq_in),
-                    ("master_out", master_out), ("exp_avg_out", exp_avg_out),
-                    ("exp_avg_sq_out", exp_avg_sq_out), ("param_fp16_out", param_fp16_out),
-                    *((f"grad_chunks[{i}]", c) for i, c in enumerate(grad_chunks))):
-        if t.numel() != n:
-            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
-    _check(lib.zero_traffic_twin(
-        _ptr_array(ptrs), len(ptrs), n, _dev(master_in, torch.float32, "master_in"),
-        _dev(exp_avg_in, torch.float32, "exp_avg_in"),
-        _dev(exp_avg_sq_in, torch.float32, "exp_avg_sq_in"),
-        _dev(master_out, torch.float32, "master_out"),
-        _dev(exp_avg_out, torch.float32, "exp_avg_out"),
-        _dev(exp_avg_sq_out, torch.float32, "exp_avg_sq_out"),
-        _dev(param_fp16_out, torch.float16, "param_fp16_out"), _stream(stream)))
-
-
 def zero_bucket_flatten(tensors: Sequence[torch.Tensor], bucket: torch.Tensor,
                         align: int = 256, pad_multiple: int = 0, stream=None) -> list:
     """Pack fp16 tensors into ``bucket``; returns the offsets and padded length."""
@@ -376,6 +362,53 @@ def zero_bucket_flatten(tensors: Sequence[torch.Tensor], bucket: torch.Tensor,
                                    _dev(bucket, torch.float16, "bucket"), bucket.numel(), offs,
                                    _stream(stream)))
     return list(offs)
+
+
+class FlattenBatch:
+    """Arguments of zero_bucket_flatten_batch marshalled once: ``buckets`` is a
+    sequence of (tensors, bucket), fp16 device tensors.  The tensors are
+    referenced, so their memory stays valid while the object exists; their
+    contents may change between calls.  ``offsets`` holds each bucket's slot
+    offsets and padded length after a call."""
+
+    def __init__(self, buckets, align: int = 256, pad_multiple: int = 0):
+        self.align, self.pad_multiple = int(align), int(pad_multiple)
+        self.count = len(buckets)
+        self.table = (FlattenBucketC * max(self.count, 1))()
+        self._keep = []
+        self._offs = []
+        for k, (tensors, bucket) in enumerate(buckets):
+            ptrs = [_dev(t, torch.float16, f"bucket {k} tensor {i}") if t.numel() else 0
+                    for i, t in enumerate(tensors)]
+            nt = len(ptrs)
+            parr = _ptr_array(ptrs)
+            narr = (ctypes.c_int64 * max(nt, 1))(*[t.numel() for t in tensors])
+            oarr = (ctypes.c_int64 * (nt + 1))()
+            self._keep.append((list(tensors), bucket, parr, narr))
+            self._offs.append(oarr)
+            self.table[k].tensors = ctypes.cast(parr, ctypes.POINTER(ctypes.c_void_p))
+            self.table[k].numels = ctypes.cast(narr, ctypes.POINTER(ctypes.c_int64))
+            self.table[k].offsets_out = ctypes.cast(oarr, ctypes.POINTER(ctypes.c_int64))
+            self.table[k].bucket = _dev(bucket, torch.float16, f"bucket {k}")
+            self.table[k].bucket_capacity = bucket.numel()
+            self.table[k].n_tensors = nt
+
+    @property
+    def offsets(self) -> list:
+        return [list(o) for o in self._offs]
+
+    def __call__(self, stream=None) -> list:
+        _check(lib.zero_bucket_flatten_batch(self.table, self.count, self.align,
+                                             self.pad_multiple, _stream(stream)))
+        return self.offsets
+
+
+def zero_bucket_flatten_batch(buckets, align: int = 256, pad_multiple: int = 0,
+                              stream=None) -> list:
+    """Pack each bucket's fp16 tensors into it, all buckets in few launches;
+    ``buckets``: a sequence of (tensors, bucket).  Returns every bucket's
+    offsets and padded length."""
+    return FlattenBatch(buckets, align, pad_multiple)(stream)
 
 
 def zero_update_loss_scale(scaler: LossScaler, overflow: int) -> bool:
@@ -479,8 +512,12 @@ def _ctl(ctl: torch.Tensor) -> int:
     return _dev(ctl, torch.uint8, "ctl")
 
 
-def zero_control_begin(ctl: torch.Tensor, stream=None) -> None:
-    _check(lib.zero_control_begin(_ctl(ctl), _stream(stream)))
+def zero_control_begin(ctl: torch.Tensor, hp: AdamWParams, stream=None) -> None:
+    """Start a step; hp gives the table of bias corrections (base t0 =
+    hp.step) from which the step's are looked up."""
+    if not isinstance(hp, AdamWParams):
+        hp = adamw_params(hp)
+    _check(lib.zero_control_begin(_ctl(ctl), ctypes.byref(hp), _stream(stream)))
 
 
 def zero_overflow_check_ctl(grad_chunks: Sequence[torch.Tensor], ctl: torch.Tensor,
@@ -594,11 +631,11 @@ class _Tiling:
 
 
 class DeviceStepper:
-    """Enqueues whole steps under a control block with no read-back.  The
-    update's bias corrections come from a table based at t0 and covering
-    ZERO_CTL_STEPS values of t; since t grows by at most one per step, the
-    stepper reads the block back (once per ZERO_CTL_STEPS steps) only to move
-    the base to the current t."""
+    """Enqueues whole steps under a control block with no read-back.  Each
+    step's bias corrections are looked up at its begin in a table based at
+    t0 = hp.step and covering ZERO_CTL_STEPS values of t; since t grows by at
+    most one per step, the stepper reads the block back (once per
+    ZERO_CTL_STEPS steps) only to move the base to the current t."""
 
     def __init__(self, ctl: torch.Tensor, hp: AdamWParams):
         self.ctl = ctl
@@ -609,6 +646,9 @@ class DeviceStepper:
 
     def _rebase(self):
         if self.since_base >= ZERO_CTL_STEPS:
+            # the steps may have run on any stream: wait for the whole device
+            # before reading t back, so the new base is never stale
+            torch.cuda.synchronize(self.ctl.device)
             self.hp.step = control_read(self.ctl).step
             self.since_base = 0
 
@@ -616,7 +656,7 @@ class DeviceStepper:
                  max_grad_norm: float = 0.0, stream=None) -> None:
         """Check, decide (skip, loss scale, clip factor, t), update in place."""
         self._rebase()
-        zero_control_begin(self.ctl, stream=stream)
+        zero_control_begin(self.ctl, self.hp, stream=stream)
         zero_overflow_check_ctl(grad_chunks, self.ctl, stream=stream)
         zero_control_decide(self.ctl, max_grad_norm, False, stream=stream)
         zero_shard_step_ctl(grad_chunks, master, exp_avg, exp_avg_sq, param_fp16, self.hp,
@@ -632,13 +672,40 @@ class DeviceStepper:
         the whole shard's norm, t), then one in-place update per bucket."""
         n = master.numel()
         tiling = _Tiling(n)
-        for chunks, off in buckets:
-            tiling.add(int(off), chunks[0].numel())
+        # Everything the per-bucket updates would refuse is refused here, before
+        # the decision: once decide has run, t and the scale have moved and the
+        # first buckets' updates would be in place.
+        state = [(master, torch.float32, 4), (exp_avg, torch.float32, 4),
+                 (exp_avg_sq, torch.float32, 4), (param_fp16, torch.float16, 2)]
+        spans = []
+        for j, (t, dt, es) in enumerate(state):
+            if t.numel() != n:
+                raise ValueError(f"state array {j} has {t.numel()} elements, expected {n}")
+            base = _dev(t, dt, f"state array {j}")
+            if base % 16:
+                raise ValueError(f"state array {j} is not 16-byte aligned")
+            spans.append((base, n * es))
+        for k, (chunks, off) in enumerate(buckets):
+            off = int(off)
+            nb = chunks[0].numel()
+            if off % 8:
+                raise ValueError(f"bucket {k} offset {off} is not a multiple of 8")
+            tiling.add(off, nb)
+            for i, c in enumerate(chunks):
+                if c.numel() != nb:
+                    raise ValueError(f"bucket {k} chunk {i} has {c.numel()} elements, "
+                                     f"expected {nb}")
+                p = _dev(c, torch.float16, f"bucket {k} chunk {i}")
+                if nb and p % 16:
+                    raise ValueError(f"bucket {k} chunk {i} is not 16-byte aligned")
+                for j, (lo, size) in enumerate(spans):
+                    if nb and p < lo + size and lo < p + 2 * nb:
+                        raise ValueError(f"bucket {k} chunk {i} overlaps state array {j}")
         if not tiling.complete():
             raise ValueError(f"the buckets cover {tiling.covered} elements of a "
                              f"{n}-element state")
         self._rebase()
-        zero_control_begin(self.ctl, stream=stream)
+        zero_control_begin(self.ctl, self.hp, stream=stream)
         for chunks, _ in buckets:
             zero_overflow_check_ctl(chunks, self.ctl, stream=stream)
         zero_control_decide(self.ctl, max_grad_norm, False, stream=stream)
@@ -652,7 +719,7 @@ class DeviceStepper:
     def single_pass(self, grad_chunks, copies, stream=None) -> None:
         """Fused update from copy cur into the other, then decide and commit."""
         self._rebase()
-        zero_control_begin(self.ctl, stream=stream)
+        zero_control_begin(self.ctl, self.hp, stream=stream)
         zero_shard_step_out_ctl(grad_chunks, copies, self.hp, self.ctl, stream=stream)
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
@@ -660,7 +727,7 @@ class DeviceStepper:
     def single_pass_buckets(self, slices: BucketSlices, copies, stream=None) -> None:
         """single_pass over the bucket slices of a ZeRO-2 shard."""
         self._rebase()
-        zero_control_begin(self.ctl, stream=stream)
+        zero_control_begin(self.ctl, self.hp, stream=stream)
         zero_shard_step_buckets_ctl(slices, copies, self.hp, self.ctl, stream=stream)
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
         self.since_base += 1
@@ -673,7 +740,7 @@ class DeviceStepper:
         which unscales by the block's S and fuses the flag and squared norm
         of g = fp32(mean16) / S; then decide and commit."""
         self._rebase()
-        zero_control_begin(self.ctl, stream=stream)
+        zero_control_begin(self.ctl, self.hp, stream=stream)
         zero_reduce_mean_fp16(grad_chunks, mean_fp16, stream=stream)
         zero_shard_step_out_ctl([mean_fp16], copies, self.hp, self.ctl, stream=stream)
         zero_control_decide(self.ctl, 0.0, True, stream=stream)
@@ -732,7 +799,7 @@ class DeviceStepper:
                 pair.append(_dev(t, dts[j], f"copy {k} array {j}"))
             bases.append((pair, t.element_size()))
         ctl_ptr = _ctl(self.ctl)
-        zero_control_begin(self.ctl, stream=main)
+        zero_control_begin(self.ctl, self.hp, stream=main)
         used = set()
         self.bucket_done = None
         # one "arrived" event per side stream, re-recorded for each bucket: a
@@ -815,7 +882,7 @@ class PreparedSinglePass:
     def __call__(self) -> None:
         st = self.stepper
         st._rebase()
-        _check(lib.zero_control_begin(self._ctl, self._stream))
+        _check(lib.zero_control_begin(self._ctl, ctypes.byref(st.hp), self._stream))
         _check(lib.zero_shard_step_out_ctl(*self._args))
         _check(lib.zero_control_decide(self._ctl, 0.0, 1, self._stream))
         st.since_base += 1

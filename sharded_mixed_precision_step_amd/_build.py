@@ -1,4 +1,5 @@
-"""Build of libzerostep.so: the gfx950 kernels and the C-ABI host layer.
+"""Build of libzerostep.so (the gfx950 kernels and the C-ABI host layer) and
+of libzerotwin.so (the benchmark's measurement aids, zero_twin.h).
 
 hipcc cross-compiles for gfx950 on any host, so this runs without a GPU.
 """
@@ -14,8 +15,9 @@ ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libzerostep.so")
-SOURCES = [os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_twin.hip"),
-           os.path.join(CSRC, "zero_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_abi.cpp")]
+TWIN_LIB = os.path.join(HERE, "libzerotwin.so")
+TWIN_SOURCES = [os.path.join(CSRC, "zero_twin.hip")]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -82,27 +84,42 @@ def kernel_digest() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 into libzerostep.so (atomically)."""
-    fd, tmp = tempfile.mkstemp(prefix=".libzerostep.", suffix=".so.tmp", dir=HERE)
-    os.close(fd)
-    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    """Compile both libraries for gfx950 (two hipcc processes side by side),
+    each written atomically."""
+    jobs = []
+    for lib, sources in ((LIB, SOURCES), (TWIN_LIB, TWIN_SOURCES)):
+        name = os.path.basename(lib)
+        fd, tmp = tempfile.mkstemp(prefix=f".{name}.", suffix=".tmp", dir=HERE)
+        os.close(fd)
+        cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, *sources, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        jobs.append((lib, tmp, proc))
+    errors = []
     try:
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
-        if verbose and res.stderr.strip():
-            print(res.stderr, flush=True)
-        os.replace(tmp, LIB)
+        for lib, tmp, proc in jobs:
+            out, err = proc.communicate()
+            if proc.returncode != 0:
+                errors.append(f"hipcc failed ({proc.returncode}) for {os.path.basename(lib)}:"
+                              f"\n{out}\n{err}")
+                continue
+            if verbose and err.strip():
+                print(err, flush=True)
+            os.replace(tmp, lib)
     finally:
-        if os.path.exists(tmp):
-            os.unlink(tmp)
+        for _, tmp, proc in jobs:
+            if proc.poll() is None:
+                proc.kill()
+            if os.path.exists(tmp):
+                os.unlink(tmp)
+    if errors:
+        raise RuntimeError("\n".join(errors))
     return LIB
 
 
 def ensure_built() -> str:
-    """Build only if no library is present."""
-    if not os.path.exists(LIB):
+    """Build only if a library is missing."""
+    if not (os.path.exists(LIB) and os.path.exists(TWIN_LIB)):
         build()
     return LIB

@@ -12,12 +12,6 @@
 #include "zero_internal.h"
 #include "zero_step.h"
 
-namespace zero {
-// zero_twin.hip: the fused step's traffic twin (a measurement aid).
-hipError_t launch_traffic_twin(const ChunkTable& chunks, int n_chunks, int64_t n,
-                               const ShardState& st, hipStream_t stream);
-}  // namespace zero
-
 namespace {
 
 float bias_correction(float beta, int64_t t);
@@ -203,39 +197,17 @@ int check_ctl_ptr(const zero_step_control* d_ctl, const char* who) {
     return ZERO_OK;
 }
 
-// The table of bias corrections for t = hp->step .. + ZERO_CTL_STEPS - 1.
-// Its 2 * ZERO_CTL_STEPS fp64 powers cost more host time than the rest of a
-// small step's call, and a caller stepping under a control block passes the
-// same base t0 for ZERO_CTL_STEPS calls in a row, so each thread keeps the
-// last table it built and reuses it while (beta1, beta2, t0, bias
-// correction) are unchanged (compared bit for bit).
+// The table of bias corrections for t = hp->step .. + ZERO_CTL_STEPS - 1, the
+// same fp64 powers rounded to fp32 as adam_scalars takes for one t.  Built
+// afresh at every step's begin (128 powers, a few microseconds of host time);
+// the library keeps no copy.
 void bias_table(const zero_adamw_params* hp, zero::BiasTable* tab) {
-    struct Memo {
-        bool valid;
-        uint32_t beta1_bits, beta2_bits;
-        int64_t t0;
-        int32_t bias_correction;
-        zero::BiasTable table;
-    };
-    thread_local Memo memo = {};
-    uint32_t b1, b2;
-    memcpy(&b1, &hp->beta1, sizeof b1);
-    memcpy(&b2, &hp->beta2, sizeof b2);
-    const int32_t bc = hp->bias_correction ? 1 : 0;
-    if (!(memo.valid && memo.beta1_bits == b1 && memo.beta2_bits == b2 && memo.t0 == hp->step &&
-          memo.bias_correction == bc)) {
-        memo.table.t0 = hp->step;
-        for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
-            memo.table.bc1[k] = bc ? bias_correction(hp->beta1, hp->step + k) : 1.0f;
-            memo.table.bc2[k] = bc ? bias_correction(hp->beta2, hp->step + k) : 1.0f;
-        }
-        memo.beta1_bits = b1;
-        memo.beta2_bits = b2;
-        memo.t0 = hp->step;
-        memo.bias_correction = bc;
-        memo.valid = true;
+    const bool bc = hp->bias_correction != 0;
+    tab->t0 = hp->step;
+    for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
+        tab->bc1[k] = bc ? bias_correction(hp->beta1, hp->step + k) : 1.0f;
+        tab->bc2[k] = bc ? bias_correction(hp->beta2, hp->step + k) : 1.0f;
     }
-    *tab = memo.table;
 }
 
 // Scalars and slices of a bucket-table call: every slice inside the state,
@@ -401,6 +373,110 @@ int shard_step_common(const void* const* grad_chunks, int32_t n_chunks, int64_t 
     return e == hipSuccess ? ok() : hip_fail(e, who);
 }
 
+// One bucket of a flatten call: validates its arguments, fills offsets_out
+// (off_0 .. off_{n-1}, then the padded length L, also when the capacity is
+// too small) and returns L in *total.  `index` >= 0 names the bucket of a
+// batch in error messages.
+int flatten_layout(const zero_flatten_bucket& bk, int64_t align, int64_t pad_multiple,
+                   const char* who, int32_t index, int64_t* total) {
+    char tag[64] = "";
+    if (index >= 0) snprintf(tag, sizeof tag, " bucket %d", index);
+    const int32_t n_tensors = bk.n_tensors;
+    if (n_tensors < 0) return fail(ZERO_EINVAL, "%s%s: n_tensors < 0", who, tag);
+    if (n_tensors > 0 && (!bk.tensors || !bk.numels))
+        return fail(ZERO_EINVAL, "%s%s: tensors or numels is NULL", who, tag);
+    if (!bk.offsets_out) return fail(ZERO_EINVAL, "%s%s: offsets_out is NULL", who, tag);
+    if (align < 1) return fail(ZERO_EINVAL, "%s: align < 1", who);
+    if (pad_multiple < 0) return fail(ZERO_EINVAL, "%s: pad_multiple < 0", who);
+    if (bk.bucket_capacity < 0) return fail(ZERO_EINVAL, "%s%s: bucket_capacity < 0", who, tag);
+    const int64_t kLimit = INT64_MAX / 4;
+    int64_t end = 0;
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        const int64_t numel = bk.numels[k];
+        if (numel < 0) return fail(ZERO_EINVAL, "%s%s: numels[%d] < 0", who, tag, k);
+        if (numel > 0 && !bk.tensors[k])
+            return fail(ZERO_EINVAL, "%s%s: tensors[%d] is NULL", who, tag, k);
+        if (numel > 0 && !aligned(bk.tensors[k], 2))
+            return fail(ZERO_EALIGN, "%s%s: tensors[%d] is not 2-byte aligned", who, tag, k);
+        const int64_t start = (end + align - 1) / align * align;
+        if (start > kLimit || numel > kLimit - start)
+            return fail(ZERO_EINVAL, "%s%s: bucket length overflows", who, tag);
+        bk.offsets_out[k] = start;
+        end = start + numel;
+    }
+    const int64_t L =
+        pad_multiple > 1 ? (end + pad_multiple - 1) / pad_multiple * pad_multiple : end;
+    bk.offsets_out[n_tensors] = L;
+    *total = L;
+    if (L > 0 && !bk.bucket) return fail(ZERO_EINVAL, "%s%s: bucket is NULL", who, tag);
+    if (L > 0 && !aligned(bk.bucket, 16))
+        return fail(ZERO_EALIGN, "%s%s: bucket is not 16-byte aligned", who, tag);
+    if (L > bk.bucket_capacity)
+        return fail(ZERO_ERANGE, "%s%s: bucket needs %lld elements, capacity is %lld", who, tag,
+                    static_cast<long long>(L), static_cast<long long>(bk.bucket_capacity));
+    for (int32_t k = 0; k < n_tensors; ++k)
+        if (overlap(bk.tensors[k], 2 * bk.numels[k], bk.bucket, 2 * L))
+            return fail(ZERO_EINVAL, "%s%s: tensors[%d] overlaps the bucket", who, tag, k);
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        const int64_t next = k + 1 < n_tensors ? bk.offsets_out[k + 1] : L;
+        if ((next - bk.offsets_out[k] + zero::kFlattenTile - 1) / zero::kFlattenTile >
+            zero::kMaxGridBlocks)
+            return fail(ZERO_EINVAL, "%s%s: tensor %d's slot is longer than one launch covers",
+                        who, tag, k);
+    }
+    return ZERO_OK;
+}
+
+// Flatten slots gathered into launches of up to kFlattenBatch slots (and
+// kMaxGridBlocks blocks), in the order added.  Tensor k of a bucket owns
+// [off_k, off_{k+1}) and the last tensor runs to the padded end; empty slots
+// (a zero-size tensor followed by no gap) are left out.
+struct FlattenBatcher {
+    zero::FlattenTable t;
+    hipStream_t stream;
+    const char* who;
+
+    FlattenBatcher(hipStream_t s, const char* w) : stream(s), who(w) { memset(&t, 0, sizeof t); }
+
+    int flush() {
+        if (t.count > 0) {
+            const hipError_t e = zero::launch_bucket_flatten(t, stream);
+            memset(&t, 0, sizeof t);
+            if (e != hipSuccess) return hip_fail(e, who);
+        }
+        return ok();
+    }
+
+    int add(const uint16_t* src, uint16_t* dst, int64_t numel, int64_t slot_len) {
+        if (slot_len <= 0) return ZERO_OK;
+        const int64_t tiles = (slot_len + zero::kFlattenTile - 1) / zero::kFlattenTile;
+        if (t.count > 0 && (t.count == zero::kFlattenBatch ||
+                            t.tile_start[t.count] + tiles > zero::kMaxGridBlocks)) {
+            int rc = flush();
+            if (rc) return rc;
+        }
+        zero::FlattenSlot& d = t.s[t.count];
+        d.src = numel > 0 ? src : nullptr;
+        d.dst = dst;
+        d.numel = numel;
+        d.slot_len = slot_len;
+        t.tile_start[t.count + 1] = t.tile_start[t.count] + tiles;
+        ++t.count;
+        return ZERO_OK;
+    }
+
+    int add_bucket(const zero_flatten_bucket& bk, int64_t total) {
+        uint16_t* base = static_cast<uint16_t*>(bk.bucket);
+        for (int32_t k = 0; k < bk.n_tensors; ++k) {
+            const int64_t next = k + 1 < bk.n_tensors ? bk.offsets_out[k + 1] : total;
+            int rc = add(static_cast<const uint16_t*>(bk.tensors[k]), base + bk.offsets_out[k],
+                         bk.numels[k], next - bk.offsets_out[k]);
+            if (rc) return rc;
+        }
+        return ZERO_OK;
+    }
+};
+
 }  // namespace
 
 extern "C" {
@@ -493,8 +569,6 @@ int zero_shard_step_buckets_ctl(const zero_bucket_slice* slices, int32_t n_slice
                           masters[1], exp_avgs[1], exp_avg_sqs[1], params_fp16[1]};
     if ((rc = check_copy_pair(arr, n_state, who))) return rc;
     if ((rc = check_slices_clear_of(slices, n_slices, n_chunks, n_state, arr, 8, who))) return rc;
-    zero::BiasTable tab;
-    bias_table(hp, &tab);
     zero::ShardCopies sc;
     for (int k = 0; k < 2; ++k) {
         sc.master[k] = masters[k];
@@ -504,7 +578,7 @@ int zero_shard_step_buckets_ctl(const zero_bucket_slice* slices, int32_t n_slice
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     return launch_bucket_batches(slices, n_slices, n_chunks, who, [&](const zero::BucketTable& t) {
-        return zero::launch_bucket_ctl_step(t, n_chunks, gs, as, tab, sc, d_ctl, hs);
+        return zero::launch_bucket_ctl_step(t, n_chunks, gs, as, sc, d_ctl, hs);
     });
 }
 
@@ -593,10 +667,15 @@ int zero_control_init(zero_step_control* ctl, const zero_loss_scaler* scaler, in
     return ok();
 }
 
-int zero_control_begin(zero_step_control* d_ctl, void* stream) {
+int zero_control_begin(zero_step_control* d_ctl, const zero_adamw_params* hp, void* stream) {
     int rc = check_ctl_ptr(d_ctl, "zero_control_begin");
     if (rc) return rc;
-    const hipError_t e = zero::launch_control_begin(d_ctl, static_cast<hipStream_t>(stream));
+    zero::AdamScalars unused;
+    if ((rc = adam_scalars(hp, &unused))) return rc;  // the table's betas and base t0
+    zero::BiasTable tab;
+    bias_table(hp, &tab);
+    const hipError_t e =
+        zero::launch_control_begin(d_ctl, tab, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "zero_control_begin");
 }
 
@@ -645,8 +724,6 @@ int zero_shard_step_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_
         if ((rc = check_outputs_clear_of(n, master, exp_avg, exp_avg_sq, param_fp16,
                                          grad_chunks[c], 2 * n, who, c)))
             return rc;
-    zero::BiasTable tab;
-    bias_table(hp, &tab);
     zero::ShardCopies sc;
     for (int k = 0; k < 2; ++k) {
         sc.master[k] = master;
@@ -654,7 +731,7 @@ int zero_shard_step_ctl(const void* const* grad_chunks, int32_t n_chunks, int64_
         sc.exp_avg_sq[k] = exp_avg_sq;
         sc.param_fp16[k] = static_cast<uint16_t*>(param_fp16);
     }
-    const hipError_t e = zero::launch_ctl_step(table, n_chunks, n, gs, as, tab, sc, false, d_ctl,
+    const hipError_t e = zero::launch_ctl_step(table, n_chunks, n, gs, as, sc, false, d_ctl,
                                                static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, who);
 }
@@ -686,8 +763,6 @@ int zero_shard_step_out_ctl(const void* const* grad_chunks, int32_t n_chunks, in
         for (int32_t c = 0; c < n_chunks; ++c)
             if (overlap(arr[a], bytes[a], grad_chunks[c], 2 * n))
                 return fail(ZERO_EINVAL, "%s: state array %d overlaps grad_chunks[%d]", who, a, c);
-    zero::BiasTable tab;
-    bias_table(hp, &tab);
     zero::ShardCopies sc;
     for (int k = 0; k < 2; ++k) {
         sc.master[k] = masters[k];
@@ -695,104 +770,58 @@ int zero_shard_step_out_ctl(const void* const* grad_chunks, int32_t n_chunks, in
         sc.exp_avg_sq[k] = exp_avg_sqs[k];
         sc.param_fp16[k] = static_cast<uint16_t*>(params_fp16[k]);
     }
-    const hipError_t e = zero::launch_ctl_step(table, n_chunks, n, gs, as, tab, sc, true, d_ctl,
+    const hipError_t e = zero::launch_ctl_step(table, n_chunks, n, gs, as, sc, true, d_ctl,
                                                static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ok() : hip_fail(e, who);
-}
-
-int zero_traffic_twin(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
-                      const float* master_in, const float* exp_avg_in, const float* exp_avg_sq_in,
-                      float* master_out, float* exp_avg_out, float* exp_avg_sq_out,
-                      void* param_fp16_out, void* stream) {
-    static const char* who = "zero_traffic_twin";
-    zero::ChunkTable table;
-    zero::GradScalars gs;
-    int rc = check_chunks(grad_chunks, n_chunks, n, 1.0f, &table, &gs);
-    if (rc) return rc;
-    if (n == 0) return ok();
-    if ((rc = check_step_length(n, who))) return rc;
-    if ((rc = check_state(n, master_in, exp_avg_in, exp_avg_sq_in, master_out, exp_avg_out,
-                          exp_avg_sq_out, param_fp16_out, who)))
-        return rc;
-    for (int32_t c = 0; c < n_chunks; ++c)
-        if ((rc = check_outputs_clear_of(n, master_out, exp_avg_out, exp_avg_sq_out,
-                                         param_fp16_out, grad_chunks[c], 2 * n, who, c)))
-            return rc;
-    const zero::ShardState st = {master_in,  exp_avg_in,  exp_avg_sq_in,
-                                 master_out, exp_avg_out, exp_avg_sq_out,
-                                 static_cast<uint16_t*>(param_fp16_out)};
-    const hipError_t e =
-        zero::launch_traffic_twin(table, n_chunks, n, st, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, who);
 }
 
 int zero_bucket_flatten(const void* const* tensors, const int64_t* numels, int32_t n_tensors,
                         int64_t align, int64_t pad_multiple, void* bucket, int64_t bucket_capacity,
                         int64_t* offsets_out, void* stream) {
-    if (n_tensors < 0) return fail(ZERO_EINVAL, "n_tensors < 0");
-    if (n_tensors > 0 && (!tensors || !numels))
-        return fail(ZERO_EINVAL, "tensors or numels is NULL");
-    if (!offsets_out) return fail(ZERO_EINVAL, "offsets_out is NULL");
-    if (align < 1) return fail(ZERO_EINVAL, "align < 1");
-    if (pad_multiple < 0) return fail(ZERO_EINVAL, "pad_multiple < 0");
-    if (bucket_capacity < 0) return fail(ZERO_EINVAL, "bucket_capacity < 0");
-    const int64_t kLimit = INT64_MAX / 4;
-    int64_t end = 0;
-    for (int32_t k = 0; k < n_tensors; ++k) {
-        if (numels[k] < 0) return fail(ZERO_EINVAL, "numels[%d] < 0", k);
-        if (numels[k] > 0 && !tensors[k]) return fail(ZERO_EINVAL, "tensors[%d] is NULL", k);
-        if (numels[k] > 0 && !aligned(tensors[k], 2))
-            return fail(ZERO_EALIGN, "tensors[%d] is not 2-byte aligned", k);
-        const int64_t start = (end + align - 1) / align * align;
-        if (start > kLimit || numels[k] > kLimit - start)
-            return fail(ZERO_EINVAL, "bucket length overflows");
-        offsets_out[k] = start;
-        end = start + numels[k];
-    }
-    const int64_t total = pad_multiple > 1 ? (end + pad_multiple - 1) / pad_multiple * pad_multiple : end;
-    offsets_out[n_tensors] = total;
-    if (total > 0 && !bucket) return fail(ZERO_EINVAL, "bucket is NULL");
-    if (total > 0 && !aligned(bucket, 16)) return fail(ZERO_EALIGN, "bucket is not 16-byte aligned");
-    if (total > bucket_capacity)
-        return fail(ZERO_ERANGE, "bucket needs %lld elements, capacity is %lld",
-                    static_cast<long long>(total), static_cast<long long>(bucket_capacity));
-    for (int32_t k = 0; k < n_tensors; ++k)
-        if (overlap(tensors[k], 2 * numels[k], bucket, 2 * total))
-            return fail(ZERO_EINVAL, "tensors[%d] overlaps the bucket", k);
+    static const char* who = "zero_bucket_flatten";
+    zero_flatten_bucket one = {tensors, numels, offsets_out, bucket, bucket_capacity, n_tensors, 0};
+    int64_t total = 0;
+    int rc = flatten_layout(one, align, pad_multiple, who, -1, &total);
+    if (rc) return rc;
     if (total == 0) return ok();
-    for (int32_t k = 0; k < n_tensors; ++k) {
-        const int64_t next = k + 1 < n_tensors ? offsets_out[k + 1] : total;
-        if ((next - offsets_out[k] + zero::kFlattenTile - 1) / zero::kFlattenTile >
-            zero::kMaxGridBlocks)
-            return fail(ZERO_EINVAL, "tensor %d's slot is longer than one launch covers", k);
+    FlattenBatcher fb(static_cast<hipStream_t>(stream), who);
+    if ((rc = fb.add_bucket(one, total))) return rc;
+    return fb.flush();
+}
+
+int zero_bucket_flatten_batch(const zero_flatten_bucket* buckets, int32_t n_buckets,
+                              int64_t align, int64_t pad_multiple, void* stream) {
+    static const char* who = "zero_bucket_flatten_batch";
+    if (n_buckets < 0) return fail(ZERO_EINVAL, "%s: n_buckets < 0", who);
+    if (n_buckets > 0 && !buckets) return fail(ZERO_EINVAL, "%s: buckets is NULL", who);
+    std::vector<int64_t> totals(static_cast<size_t>(n_buckets), 0);
+    for (int32_t k = 0; k < n_buckets; ++k) {
+        int rc = flatten_layout(buckets[k], align, pad_multiple, who, k, &totals[k]);
+        if (rc) return rc;
     }
-    // Slots: tensor k owns [off_k, off_{k+1}); the last slot runs to the padded end.
-    // A bucket with no tensors (all numels 0 and total 0) returned above.
-    zero::FlattenTable table;
-    memset(&table, 0, sizeof table);
-    int count = 0;
-    int64_t max_slot = 0;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    for (int32_t k = 0; k < n_tensors; ++k) {
-        const int64_t next = k + 1 < n_tensors ? offsets_out[k + 1] : total;
-        zero::FlattenDesc& d = table.d[count];
-        d.src = static_cast<const uint16_t*>(tensors[k]);
-        d.numel = numels[k];
-        d.dst_off = offsets_out[k];
-        d.slot_len = next - offsets_out[k];
-        d.vec = (d.dst_off % zero::kPack == 0 && d.slot_len % zero::kPack == 0) ? 1 : 0;
-        if (d.slot_len > max_slot) max_slot = d.slot_len;
-        if (d.slot_len > 0) ++count;
-        if (count == zero::kFlattenBatch || (k + 1 == n_tensors && count > 0)) {
-            const hipError_t e = zero::launch_bucket_flatten(
-                table, count, max_slot, static_cast<uint16_t*>(bucket), st);
-            if (e != hipSuccess) return hip_fail(e, "zero_bucket_flatten launch");
-            memset(&table, 0, sizeof table);
-            count = 0;
-            max_slot = 0;
+    // one launch may hold slots of several buckets, in no order: no bucket may
+    // share a byte with another bucket or with another bucket's sources
+    for (int32_t k = 0; k < n_buckets; ++k) {
+        const zero_flatten_bucket& bk = buckets[k];
+        const int64_t bytes = 2 * totals[k];
+        for (int32_t j = 0; j < n_buckets; ++j) {
+            if (j == k) continue;
+            const zero_flatten_bucket& bj = buckets[j];
+            if (j > k && overlap(bk.bucket, bytes, bj.bucket, 2 * totals[j]))
+                return fail(ZERO_EINVAL, "%s: buckets %d and %d overlap", who, k, j);
+            for (int32_t i = 0; i < bj.n_tensors; ++i)
+                if (overlap(bj.tensors[i], 2 * bj.numels[i], bk.bucket, bytes))
+                    return fail(ZERO_EINVAL, "%s: bucket %d tensor %d overlaps bucket %d", who, j,
+                                i, k);
         }
     }
-    return ok();
+    FlattenBatcher fb(static_cast<hipStream_t>(stream), who);
+    for (int32_t k = 0; k < n_buckets; ++k) {
+        if (totals[k] == 0) continue;
+        int rc = fb.add_bucket(buckets[k], totals[k]);
+        if (rc) return rc;
+    }
+    return fb.flush();
 }
 
 int zero_update_loss_scale(zero_loss_scaler* s, int32_t overflow, int32_t* skip_out) {

@@ -48,7 +48,7 @@ constexpr unsigned kFoldLdsReserve = 36 * 1024;
 constexpr unsigned kFlattenLdsReserve = 36 * 1024;
 constexpr int kMeanSpan = 4;       // packs per lane in an fp16-mean tile
 constexpr int kMeanTilePacks = kBlock * kMeanSpan;  // packs per fp16-mean tile (one block)
-constexpr int kFlattenBatch = 32;  // tensors per flatten launch (kernel-argument table)
+constexpr int kFlattenBatch = 64;  // tensor slots per flatten launch (kernel-argument table)
 constexpr int kFlattenSpan = 4;    // packs per lane in a flatten tile
 constexpr int64_t kFlattenTile = static_cast<int64_t>(kBlock) * kFlattenSpan * kPack;  // elements
 constexpr int64_t kMaxGridBlocks = 0x7fffffff;  // blocks in one launch's x dimension
@@ -112,8 +112,8 @@ struct BucketTable {
 };
 
 // Bias corrections 1 - beta^t for t = t0 .. t0 + ZERO_CTL_STEPS - 1 (fp64,
-// rounded to fp32, as the host computes them), for updates whose t lives in
-// a device control block.
+// rounded to fp32, as the host computes them), from which a control block's
+// begin picks those of the t it holds.
 struct BiasTable {
     int64_t t0;
     float bc1[ZERO_CTL_STEPS];
@@ -128,17 +128,23 @@ struct ShardCopies {
     uint16_t* param_fp16[2];
 };
 
-struct FlattenDesc {
-    const uint16_t* src;  // fp16 bits, 2-byte aligned
+// One tensor's slot in a bucket: the tensor's elements, then zeros up to the
+// next slot (or the padded end).
+struct FlattenSlot {
+    const uint16_t* src;  // fp16 bits, 2-byte aligned; NULL when numel == 0
+    uint16_t* dst;        // the slot's first element in its bucket
     int64_t numel;        // elements of the tensor
-    int64_t dst_off;      // slot start in the bucket (elements)
-    int64_t slot_len;     // slot length: tensor plus the zero gap after it
-    int32_t vec;          // dst_off and slot_len are multiples of 8
-    int32_t pad_;
+    int64_t slot_len;     // slot length: tensor plus the zero gap after it, > 0
 };
 
+// Slots of one flatten launch, from one bucket or several, passed by value in
+// the kernel arguments (about 2.5 KiB).  Slot k owns blocks
+// [tile_start[k], tile_start[k + 1]), one per kFlattenTile elements.
 struct FlattenTable {
-    FlattenDesc d[kFlattenBatch];
+    int64_t tile_start[kFlattenBatch + 1];
+    FlattenSlot s[kFlattenBatch];
+    int32_t count;
+    int32_t pad_;
 };
 
 hipError_t launch_overflow_check(const ChunkTable& chunks, int n_chunks, int64_t n,
@@ -158,17 +164,16 @@ int64_t step_tiles(int64_t n);  // blocks of the fused step over n params
 int64_t mean_tiles(int64_t n);  // blocks of the fp16 mean over n params
 
 hipError_t launch_ctl_step(const ChunkTable& chunks, int n_chunks, int64_t n,
-                           const GradScalars& gs, const AdamScalars& as, const BiasTable& tab,
-                           const ShardCopies& sc, bool single_pass, zero_step_control* ctl,
-                           hipStream_t stream);
+                           const GradScalars& gs, const AdamScalars& as, const ShardCopies& sc,
+                           bool single_pass, zero_step_control* ctl, hipStream_t stream);
 hipError_t launch_bucket_ctl_step(const BucketTable& t, int n_chunks, const GradScalars& gs,
-                                  const AdamScalars& as, const BiasTable& tab,
-                                  const ShardCopies& sc, zero_step_control* ctl,
-                                  hipStream_t stream);
+                                  const AdamScalars& as, const ShardCopies& sc,
+                                  zero_step_control* ctl, hipStream_t stream);
 hipError_t launch_overflow_check_ctl(const ChunkTable& chunks, int n_chunks, int64_t n,
                                      const GradScalars& gs, zero_step_control* ctl,
                                      hipStream_t stream);
-hipError_t launch_control_begin(zero_step_control* ctl, hipStream_t stream);
+hipError_t launch_control_begin(zero_step_control* ctl, const BiasTable& tab,
+                                hipStream_t stream);
 hipError_t launch_control_decide(zero_step_control* ctl, float max_norm, int flip,
                                  hipStream_t stream);
 
@@ -180,8 +185,6 @@ hipError_t launch_reduce_mean(const ChunkTable& chunks, int n_chunks, int64_t n,
 hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const GradScalars& gs,
                              float* acc, uint16_t* mean16, hipStream_t stream);
 
-hipError_t launch_bucket_flatten(const FlattenTable& table, int count,
-                                 int64_t max_slot_len, uint16_t* bucket,
-                                 hipStream_t stream);
+hipError_t launch_bucket_flatten(const FlattenTable& table, hipStream_t stream);
 
 }  // namespace zero

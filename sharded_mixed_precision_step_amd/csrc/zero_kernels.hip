@@ -12,7 +12,8 @@
 //   control_decide_kernel  scale, clip factor, t, commit).
 //   reduce_mean_kernel     the replica mean stored as fp16 (page-literal split).
 //   accumulate_kernel      one arriving chunk folded into the fp16 mean.
-//   bucket_flatten_kernel  whole tensors into 256-aligned, zero-padded slots.
+//   bucket_flatten_kernel  whole tensors into 256-aligned, zero-padded slots, of
+//                          one bucket or of many in one launch.
 //
 // The update order is that of the ZeRO-1 update step of the ZeRO notes
 // (rkmt.cn/news/44736, section "Deepspeed ZeRO-1", step 更新): fp16 to fp32
@@ -340,6 +341,7 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
     ChunkTable chunks, int n_chunks, int64_t n, GradScalars gs,
     int32_t* __restrict__ d_overflow, double* __restrict__ d_sqnorm, zero_step_control* ctl) {
     if constexpr (CTL) {
+        if (ctl->skip) return;  // a bias-table miss: the step will not run
         gs = with_scale(gs, ctl->scale_used);
         d_overflow = &ctl->overflow;
         d_sqnorm = &ctl->check_part[blockIdx.x];
@@ -396,28 +398,23 @@ __global__ __launch_bounds__(kBlock) void overflow_check_kernel(
 }
 
 // The update under a device control block.  SINGLE = false: the two-pass
-// update, in place on copy 0, skipped whole when ctl->skip is set, with g
-// clipped by ctl->clip_coef.  SINGLE = true: the single-pass update from copy
-// cur into copy 1 - cur, with the flag and squared norm into the block.  In
-// both, S = scale_used and the bias corrections are those of t = step_used,
-// looked up in the table the host computed.  Every block reads the same few
+// update, in place on copy 0, with g clipped by ctl->clip_coef.
+// SINGLE = true: the single-pass update from copy cur into copy 1 - cur, with
+// the flag and squared norm into the block.  In both, S = scale_used and the
+// bias corrections are the block's bc1_used and bc2_used (those of
+// t = step_used, set at the step's begin).  The whole update is skipped when
+// ctl->skip is set: in the two-pass flow that is the decision (overflow, or
+// a bias-table miss found at begin); in the single pass, which runs before
+// the decision, only a miss can have set it.  Every block reads the same few
 // words of the block (no block writes them here).
 template <int NC, bool SINGLE>
 __global__ __launch_bounds__(kBlock) void ctl_step_kernel(ChunkTable chunks, int n_chunks,
                                                           int64_t n, GradScalars gs,
-                                                          AdamScalars as, BiasTable tab,
-                                                          ShardCopies sc,
+                                                          AdamScalars as, ShardCopies sc,
                                                           zero_step_control* ctl) {
-    if constexpr (!SINGLE) {
-        if (ctl->skip) return;
-    }
-    const int64_t k = ctl->step_used - tab.t0;
-    if (k < 0 || k >= ZERO_CTL_STEPS) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&ctl->error, 1);
-        return;
-    }
-    as.bc1 = tab.bc1[k];
-    as.bc2 = tab.bc2[k];
+    if (ctl->skip) return;
+    as.bc1 = ctl->bc1_used;
+    as.bc2 = ctl->bc2_used;
     gs = with_scale(gs, ctl->scale_used);
     const int in = SINGLE ? (ctl->cur & 1) : 0;
     const int out = SINGLE ? 1 - in : 0;
@@ -433,19 +430,16 @@ __global__ __launch_bounds__(kBlock) void ctl_step_kernel(ChunkTable chunks, int
 
 // The single-pass update over a bucket table under a control block: slice k
 // of copy cur is read and slice k of copy 1 - cur written, with S, t and
-// the copy from the block and the flag and squared norm into it.
+// the copy from the block and the flag and squared norm into it; skipped
+// whole on a bias-table miss, as ctl_step_kernel.
 template <int NC>
 __global__ __launch_bounds__(kBlock) void bucket_ctl_step_kernel(BucketTable t, int n_chunks,
                                                                  GradScalars gs, AdamScalars as,
-                                                                 BiasTable tab, ShardCopies sc,
+                                                                 ShardCopies sc,
                                                                  zero_step_control* ctl) {
-    const int64_t kt = ctl->step_used - tab.t0;
-    if (kt < 0 || kt >= ZERO_CTL_STEPS) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&ctl->error, 1);
-        return;
-    }
-    as.bc1 = tab.bc1[kt];
-    as.bc2 = tab.bc2[kt];
+    if (ctl->skip) return;
+    as.bc1 = ctl->bc1_used;
+    as.bc2 = ctl->bc2_used;
     gs = with_scale(gs, ctl->scale_used);
     const int in = ctl->cur & 1, out = 1 - in;
     const int64_t b = blockIdx.x;
@@ -465,29 +459,40 @@ __global__ __launch_bounds__(kBlock) void bucket_ctl_step_kernel(BucketTable t, 
 static_assert(ZERO_CHECK_PARTS % kBlock == 0, "check partials fold kBlock-wide");
 static_assert(ZERO_NORM_SLOTS <= kBlock, "norm slots fold kBlock-wide");
 
-// One block: start a step (clear the partial sums, then the fields).  The
+// One block: start a step (clear the partial sums, then the fields), and
+// look up the bias corrections of t = step in the host's table.  A t outside
+// the table is a miss: the step is marked skipped before anything runs, so
+// no update kernel touches the state, and the decision changes nothing.  The
 // check's partials are cleared only if a check wrote them since the last
 // clear, so flows without the check do not pay for them.
-__global__ __launch_bounds__(kBlock) void control_begin_kernel(zero_step_control* c) {
+__global__ __launch_bounds__(kBlock) void control_begin_kernel(zero_step_control* c,
+                                                               BiasTable tab) {
     const bool check_ran = c->check_ran != 0;
     if (check_ran)
         for (int k = threadIdx.x; k < ZERO_CHECK_PARTS; k += kBlock) c->check_part[k] = 0.0;
     if (threadIdx.x < ZERO_NORM_SLOTS) c->sqnorm_part[ZERO_NORM_STRIDE * threadIdx.x] = 0.0;
     __syncthreads();  // every thread has read check_ran before it is cleared
     if (threadIdx.x != 0) return;
+    const int64_t t = c->step;
+    const int64_t k = t - tab.t0;
+    const bool miss = k < 0 || k >= ZERO_CTL_STEPS;
     c->check_ran = 0;
     c->overflow = 0;
     c->sqnorm = 0.0;
-    c->skip = 0;
     c->clip_coef = 1.0f;
     c->scale_used = c->scale;
-    c->step_used = c->step;
+    c->step_used = t;
+    c->table_miss = miss ? 1 : 0;
+    c->skip = miss ? 1 : 0;
+    c->bc1_used = miss ? 1.0f : tab.bc1[k];
+    c->bc2_used = miss ? 1.0f : tab.bc2[k];
+    if (miss) c->error |= 1;
 }
 
 // One block: the step's squared norm folded from its partial sums in a
 // fixed order; then, on one thread, the decision, the loss-scale move (the
 // rules of the host's zero_update_loss_scale, in fp32), the clip factor, t
-// and the copy.
+// and the copy.  After a bias-table miss (begin set skip) nothing moves.
 __global__ __launch_bounds__(kBlock) void control_decide_kernel(zero_step_control* c,
                                                                 float max_norm, int flip) {
     // sqnorm: thread t sums its ZERO_CHECK_PARTS / kBlock consecutive check
@@ -509,6 +514,7 @@ __global__ __launch_bounds__(kBlock) void control_decide_kernel(zero_step_contro
     }
     if (threadIdx.x != 0) return;
     c->sqnorm = part[0];
+    if (c->table_miss) return;  // nothing ran: t, the scale and the copy stay
     const bool skip = c->overflow != 0;
     c->skip = skip ? 1 : 0;
     if (skip) {
@@ -672,18 +678,30 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const uint16_t* __re
     }
 }
 
-// One slot per blockIdx.y: the tensor's elements, then zeros up to the next
-// slot.  Slots are disjoint, so blocks never write the same element.  Block x
-// copies the slot's tile x (kFlattenTile elements; a one-shot grid, as for
-// the step): wave w the kFlattenSpan * 64 packs from w * kFlattenSpan * 64,
-// lane l the packs l, l + 64, ..., all loads before the stores.
-__global__ __launch_bounds__(kBlock) void bucket_flatten_kernel(FlattenTable table,
-                                                                uint16_t* __restrict__ bucket) {
-    const FlattenDesc d = table.d[blockIdx.y];
-    const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kFlattenTile;
-    if (tile0 >= d.slot_len) return;  // a shorter slot than the launch's longest
-    uint16_t* dst = bucket + d.dst_off;
-    if (d.vec) {
+// Tensors into their bucket slots: the tensor's elements, then zeros up to
+// the next slot.  Slots (of one bucket or of several) are disjoint, so blocks
+// never write the same element.  The launch is one-dimensional over the
+// slots' tiles of kFlattenTile elements: a block finds its slot by a binary
+// search of the table's tile starts (block-uniform, from the kernel
+// arguments), so one launch covers many slots of any lengths with no idle
+// blocks.  Within a tile: wave w the kFlattenSpan * 64 packs from
+// w * kFlattenSpan * 64, lane l the packs l, l + 64, ..., all loads before the
+// stores.
+__global__ __launch_bounds__(kBlock) void bucket_flatten_kernel(FlattenTable t) {
+    const int64_t b = blockIdx.x;
+    int lo = 0, hi = t.count - 1;  // the last slot whose first tile is <= b
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t.tile_start[mid] <= b)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const FlattenSlot d = t.s[lo];
+    const int64_t tile0 = (b - t.tile_start[lo]) * kFlattenTile;
+    uint16_t* dst = d.dst;
+    const bool vec = (reinterpret_cast<uintptr_t>(dst) & 15) == 0 && d.slot_len % kPack == 0;
+    if (vec) {
         const bool src_vec = (reinterpret_cast<uintptr_t>(d.src) & 15) == 0;
         const int64_t packs = d.slot_len / kPack;
         const int lane = threadIdx.x & 63;
@@ -719,25 +737,16 @@ __global__ __launch_bounds__(kBlock) void bucket_flatten_kernel(FlattenTable tab
 // Launch sizing.
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxDevices = 64;
-
-int device_cus(int dev) {
-    static int cache[kMaxDevices] = {};
-    if (dev < 0 || dev >= kMaxDevices) return 256;
-    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-    if (v == 0) {
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            v <= 0)
-            v = 256;
-        __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
-    }
-    return v;
-}
-
+// Compute units of the current device, asked of the runtime at each launch
+// that sizes a resident grid (the runtime answers from its own device
+// table; nothing is kept here).
 int current_cus() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    return device_cus(dev);
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+        return 256;
+    return v;
 }
 
 // Step: one block per tile; a grid of one block still runs the tail.
@@ -786,22 +795,22 @@ hipError_t mean_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const Gr
 
 template <int NC, bool SINGLE>
 hipError_t ctl_step_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
-                         const AdamScalars& as, const BiasTable& tab, const ShardCopies& sc,
-                         zero_step_control* ctl, hipStream_t stream) {
+                         const AdamScalars& as, const ShardCopies& sc, zero_step_control* ctl,
+                         hipStream_t stream) {
     const int64_t grid = step_grid(n);
     hipLaunchKernelGGL((ctl_step_kernel<NC, SINGLE>), dim3(static_cast<unsigned>(grid)),
                        dim3(kBlock), step_lds_reserve<NC>(), stream, chunks, n_chunks, n, gs, as,
-                       tab, sc, ctl);
+                       sc, ctl);
     return hipGetLastError();
 }
 
 template <int NC>
 hipError_t bucket_ctl_impl(const BucketTable& t, int n_chunks, const GradScalars& gs,
-                           const AdamScalars& as, const BiasTable& tab, const ShardCopies& sc,
-                           zero_step_control* ctl, hipStream_t stream) {
+                           const AdamScalars& as, const ShardCopies& sc, zero_step_control* ctl,
+                           hipStream_t stream) {
     const int64_t grid = t.tile_start[t.count];
     hipLaunchKernelGGL(bucket_ctl_step_kernel<NC>, dim3(static_cast<unsigned>(grid)),
-                       dim3(kBlock), step_lds_reserve<NC>(), stream, t, n_chunks, gs, as, tab, sc,
+                       dim3(kBlock), step_lds_reserve<NC>(), stream, t, n_chunks, gs, as, sc,
                        ctl);
     return hipGetLastError();
 }
@@ -933,37 +942,34 @@ hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const G
 }
 
 hipError_t launch_ctl_step(const ChunkTable& chunks, int n_chunks, int64_t n,
-                           const GradScalars& gs, const AdamScalars& as, const BiasTable& tab,
-                           const ShardCopies& sc, bool single_pass, zero_step_control* ctl,
-                           hipStream_t stream) {
-#define ZERO_CASE(K)                                                                           \
-    case K:                                                                                    \
-        return single_pass                                                                     \
-                   ? ctl_step_impl<K, true>(chunks, n_chunks, n, gs, as, tab, sc, ctl, stream) \
-                   : ctl_step_impl<K, false>(chunks, n_chunks, n, gs, as, tab, sc, ctl, stream);
+                           const GradScalars& gs, const AdamScalars& as, const ShardCopies& sc,
+                           bool single_pass, zero_step_control* ctl, hipStream_t stream) {
+#define ZERO_CASE(K)                                                                      \
+    case K:                                                                               \
+        return single_pass                                                                \
+                   ? ctl_step_impl<K, true>(chunks, n_chunks, n, gs, as, sc, ctl, stream) \
+                   : ctl_step_impl<K, false>(chunks, n_chunks, n, gs, as, sc, ctl, stream);
     switch (n_chunks) {
         ZERO_FOR_EACH_N(ZERO_CASE)
         default:
             return single_pass
-                       ? ctl_step_impl<0, true>(chunks, n_chunks, n, gs, as, tab, sc, ctl, stream)
-                       : ctl_step_impl<0, false>(chunks, n_chunks, n, gs, as, tab, sc, ctl,
-                                                 stream);
+                       ? ctl_step_impl<0, true>(chunks, n_chunks, n, gs, as, sc, ctl, stream)
+                       : ctl_step_impl<0, false>(chunks, n_chunks, n, gs, as, sc, ctl, stream);
     }
 #undef ZERO_CASE
 }
 
 hipError_t launch_bucket_ctl_step(const BucketTable& t, int n_chunks, const GradScalars& gs,
-                                  const AdamScalars& as, const BiasTable& tab,
-                                  const ShardCopies& sc, zero_step_control* ctl,
-                                  hipStream_t stream) {
+                                  const AdamScalars& as, const ShardCopies& sc,
+                                  zero_step_control* ctl, hipStream_t stream) {
     if (t.count <= 0 || t.tile_start[t.count] <= 0) return hipSuccess;
 #define ZERO_CASE(K) \
     case K:          \
-        return bucket_ctl_impl<K>(t, n_chunks, gs, as, tab, sc, ctl, stream);
+        return bucket_ctl_impl<K>(t, n_chunks, gs, as, sc, ctl, stream);
     switch (n_chunks) {
         ZERO_FOR_EACH_N(ZERO_CASE)
         default:
-            return bucket_ctl_impl<0>(t, n_chunks, gs, as, tab, sc, ctl, stream);
+            return bucket_ctl_impl<0>(t, n_chunks, gs, as, sc, ctl, stream);
     }
 #undef ZERO_CASE
 }
@@ -982,8 +988,9 @@ hipError_t launch_overflow_check_ctl(const ChunkTable& chunks, int n_chunks, int
 #undef ZERO_CASE
 }
 
-hipError_t launch_control_begin(zero_step_control* ctl, hipStream_t stream) {
-    hipLaunchKernelGGL(control_begin_kernel, dim3(1), dim3(kBlock), 0, stream, ctl);
+hipError_t launch_control_begin(zero_step_control* ctl, const BiasTable& tab,
+                                hipStream_t stream) {
+    hipLaunchKernelGGL(control_begin_kernel, dim3(1), dim3(kBlock), 0, stream, ctl, tab);
     return hipGetLastError();
 }
 
@@ -1008,12 +1015,11 @@ hipError_t launch_overflow_check(const ChunkTable& chunks, int n_chunks, int64_t
 #undef ZERO_CASE
 }
 
-hipError_t launch_bucket_flatten(const FlattenTable& table, int count, int64_t max_slot_len,
-                                 uint16_t* bucket, hipStream_t stream) {
-    if (count <= 0 || max_slot_len <= 0) return hipSuccess;
-    const int64_t gx = (max_slot_len + kFlattenTile - 1) / kFlattenTile;
-    hipLaunchKernelGGL(bucket_flatten_kernel, dim3(static_cast<unsigned>(gx), count), dim3(kBlock),
-                       kFlattenLdsReserve, stream, table, bucket);
+hipError_t launch_bucket_flatten(const FlattenTable& table, hipStream_t stream) {
+    if (table.count <= 0 || table.tile_start[table.count] <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bucket_flatten_kernel,
+                       dim3(static_cast<unsigned>(table.tile_start[table.count])), dim3(kBlock),
+                       kFlattenLdsReserve, stream, table);
     return hipGetLastError();
 }
 

@@ -1,4 +1,8 @@
-// The fused step's traffic twin: a measurement aid, not part of the step.
+// Measurement aids, built into their own library (libzerotwin.so, declared
+// in zero_twin.h) and loaded only by the benchmark and its tests; none of
+// this is part of the step library.
+//
+// The fused step's traffic twin.
 //
 // traffic_twin_kernel makes exactly the memory accesses of the out-of-place
 // fused step (shard_step_kernel) over the same arrays: the same 16-byte
@@ -18,7 +22,11 @@
 //   exp_avg_out[j]    = exp_avg_in[j] ^ h
 //   exp_avg_sq_out[j] = exp_avg_sq_in[j] ^ h
 //   param_fp16_out[j] = h ^ (low 16 bits of master_in[j])
+#include <stdarg.h>
+#include <stdio.h>
+
 #include "zero_internal.h"
+#include "zero_twin.h"
 
 namespace zero {
 namespace {
@@ -132,25 +140,148 @@ __global__ __launch_bounds__(kBlock) void traffic_twin_kernel(ChunkTable chunks,
     }
 }
 
-}  // namespace
+// A read-only stream: every 16-byte vector of src read once (non-temporal,
+// as the step reads its chunks) in a grid-stride loop over a resident grid,
+// four vectors per thread per trip with their loads issued together; the
+// XOR of everything read is folded into *sink, so no load is dead.
+__global__ __launch_bounds__(kBlock) void stream_read_kernel(const u32x4* __restrict__ src,
+                                                             int64_t vecs,
+                                                             uint32_t* __restrict__ sink) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + 3 * stride < vecs; i += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u];
+    }
+    for (; i < vecs; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+    uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
+    if ((threadIdx.x & 63) == 0 && x != 0u) atomicXor(sink, x);
+}
 
-hipError_t launch_traffic_twin(const ChunkTable& chunks, int n_chunks, int64_t n,
-                               const ShardState& st, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(step_tiles(n))), block(kBlock);
+thread_local char g_twin_error[256] = "";
+
+int twin_fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_twin_error, sizeof g_twin_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + static_cast<uintptr_t>(nb) &&
+           y < x + static_cast<uintptr_t>(na);
+}
+
+}  // namespace
+}  // namespace zero
+
+extern "C" {
+
+const char* zero_twin_last_error_string(void) { return zero::g_twin_error; }
+
+int zero_traffic_twin(const void* const* grad_chunks, int32_t n_chunks, int64_t n,
+                      const float* master_in, const float* exp_avg_in, const float* exp_avg_sq_in,
+                      float* master_out, float* exp_avg_out, float* exp_avg_sq_out,
+                      void* param_fp16_out, void* stream) {
+    using namespace zero;
+    if (!grad_chunks) return twin_fail(ZERO_EINVAL, "grad_chunks is NULL");
+    if (n_chunks < 1 || n_chunks > ZERO_MAX_CHUNKS)
+        return twin_fail(ZERO_EINVAL, "n_chunks = %d outside [1, %d]", n_chunks, ZERO_MAX_CHUNKS);
+    if (n < 0) return twin_fail(ZERO_EINVAL, "n < 0");
+    g_twin_error[0] = '\0';
+    if (n == 0) return ZERO_OK;
+    const int64_t tiles = (n / kPack + kTilePacks - 1) / kTilePacks;
+    const int64_t grid = tiles < 1 ? 1 : tiles;
+    if (grid > kMaxGridBlocks) return twin_fail(ZERO_EINVAL, "n is longer than one launch covers");
+    const void* in[3] = {master_in, exp_avg_in, exp_avg_sq_in};
+    const void* out[4] = {master_out, exp_avg_out, exp_avg_sq_out, param_fp16_out};
+    const int64_t out_bytes[4] = {4 * n, 4 * n, 4 * n, 2 * n};
+    ChunkTable chunks;
+    for (int c = 0; c < ZERO_MAX_CHUNKS; ++c) chunks.p[c] = nullptr;
+    for (int32_t c = 0; c < n_chunks; ++c) {
+        if (!grad_chunks[c]) return twin_fail(ZERO_EINVAL, "grad_chunks[%d] is NULL", c);
+        if (!aligned16(grad_chunks[c]))
+            return twin_fail(ZERO_EALIGN, "grad_chunks[%d] is not 16-byte aligned", c);
+        chunks.p[c] = static_cast<const uint16_t*>(grad_chunks[c]);
+    }
+    for (int a = 0; a < 3; ++a) {
+        if (!in[a]) return twin_fail(ZERO_EINVAL, "state input %d is NULL", a);
+        if (!aligned16(in[a])) return twin_fail(ZERO_EALIGN, "state input %d is misaligned", a);
+    }
+    for (int a = 0; a < 4; ++a) {
+        if (!out[a]) return twin_fail(ZERO_EINVAL, "output %d is NULL", a);
+        if (!aligned16(out[a])) return twin_fail(ZERO_EALIGN, "output %d is misaligned", a);
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(out[a], out_bytes[a], out[b], out_bytes[b]))
+                return twin_fail(ZERO_EINVAL, "outputs %d and %d overlap", a, b);
+        for (int b = 0; b < 3; ++b)
+            if (!(a == b && out[a] == in[b]) && overlap(out[a], out_bytes[a], in[b], 4 * n))
+                return twin_fail(ZERO_EINVAL, "output %d overlaps input %d", a, b);
+        for (int32_t c = 0; c < n_chunks; ++c)
+            if (overlap(out[a], out_bytes[a], grad_chunks[c], 2 * n))
+                return twin_fail(ZERO_EINVAL, "output %d overlaps grad_chunks[%d]", a, c);
+    }
+    const ShardState st = {master_in,  exp_avg_in,  exp_avg_sq_in,
+                           master_out, exp_avg_out, exp_avg_sq_out,
+                           static_cast<uint16_t*>(param_fp16_out)};
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const dim3 g(static_cast<unsigned>(grid)), block(kBlock);
     switch (n_chunks) {
-#define ZERO_TWIN_CASE(K)                                                                     \
-    case K:                                                                                   \
-        hipLaunchKernelGGL(traffic_twin_kernel<K>, grid, block, step_lds_reserve<K>(),        \
-                           stream, chunks, n_chunks, n, st);                                  \
+#define ZERO_TWIN_CASE(K)                                                                    \
+    case K:                                                                                  \
+        hipLaunchKernelGGL(traffic_twin_kernel<K>, g, block, step_lds_reserve<K>(), hs,      \
+                           chunks, n_chunks, n, st);                                         \
         break;
         ZERO_TWIN_CASE(1) ZERO_TWIN_CASE(2) ZERO_TWIN_CASE(3) ZERO_TWIN_CASE(4)
         ZERO_TWIN_CASE(8) ZERO_TWIN_CASE(16)
 #undef ZERO_TWIN_CASE
         default:
-            hipLaunchKernelGGL(traffic_twin_kernel<0>, grid, block, step_lds_reserve<0>(),
-                               stream, chunks, n_chunks, n, st);
+            hipLaunchKernelGGL(traffic_twin_kernel<0>, g, block, step_lds_reserve<0>(), hs,
+                               chunks, n_chunks, n, st);
     }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? ZERO_OK
+                           : twin_fail(ZERO_EHIP, "zero_traffic_twin launch: %s",
+                                       hipGetErrorString(e));
 }
 
-}  // namespace zero
+int zero_stream_read(const void* src, int64_t bytes, uint32_t* d_sink, void* stream) {
+    using namespace zero;
+    if (bytes < 0 || bytes % 16 != 0)
+        return twin_fail(ZERO_EINVAL, "bytes = %lld is not a non-negative multiple of 16",
+                         static_cast<long long>(bytes));
+    if (bytes > 0 && (!src || !d_sink)) return twin_fail(ZERO_EINVAL, "src or d_sink is NULL");
+    if (bytes > 0 && !aligned16(src)) return twin_fail(ZERO_EALIGN, "src is misaligned");
+    if (bytes > 0 && (reinterpret_cast<uintptr_t>(d_sink) & 3))
+        return twin_fail(ZERO_EALIGN, "d_sink is misaligned");
+    g_twin_error[0] = '\0';
+    if (bytes == 0) return ZERO_OK;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    const int64_t vecs = bytes / 16;
+    const int64_t want = (vecs + kBlock - 1) / kBlock;
+    const int64_t resident = static_cast<int64_t>(kCheckBlocksPerCU) * cus;
+    const int64_t grid = want < resident ? want : resident;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), vecs,
+                       d_sink);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? ZERO_OK
+                           : twin_fail(ZERO_EHIP, "zero_stream_read launch: %s",
+                                       hipGetErrorString(e));
+}
+
+}  // extern "C"

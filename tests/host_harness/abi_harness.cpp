@@ -30,9 +30,8 @@ struct BucketLaunch {
     std::vector<const void*> chunk;
 };
 struct FlattenLaunch {
-    int count;
-    int64_t max_slot;
-    std::vector<zero::FlattenDesc> d;
+    std::vector<int64_t> tile_start;
+    std::vector<zero::FlattenSlot> s;
 };
 
 std::vector<BucketLaunch> g_bucket;
@@ -96,33 +95,37 @@ hipError_t launch_bucket_step(const BucketTable& t, int n_chunks, const GradScal
 }
 
 hipError_t launch_bucket_ctl_step(const BucketTable& t, int n_chunks, const GradScalars& gs,
-                                  const AdamScalars& as, const BiasTable& tab,
-                                  const ShardCopies&, zero_step_control*, hipStream_t s) {
-    g_bias.push_back(tab);
+                                  const AdamScalars& as, const ShardCopies&, zero_step_control*,
+                                  hipStream_t s) {
     return launch_bucket_step(t, n_chunks, gs, as, ShardState{}, nullptr, nullptr, s);
 }
 
-hipError_t launch_bucket_flatten(const FlattenTable& table, int count, int64_t max_slot_len,
-                                 uint16_t*, hipStream_t) {
+hipError_t launch_bucket_flatten(const FlattenTable& table, hipStream_t) {
     FlattenLaunch f;
-    f.count = count;
-    f.max_slot = max_slot_len;
-    for (int k = 0; k < count; ++k) f.d.push_back(table.d[k]);
+    for (int k = 0; k <= table.count; ++k) f.tile_start.push_back(table.tile_start[k]);
+    for (int k = 0; k < table.count; ++k) f.s.push_back(table.s[k]);
     g_flatten.push_back(f);
     return hipSuccess;
 }
 
 hipError_t launch_ctl_step(const ChunkTable&, int, int64_t, const GradScalars&,
-                           const AdamScalars& as, const BiasTable& tab, const ShardCopies&, bool,
-                           zero_step_control*, hipStream_t) {
+                           const AdamScalars&, const ShardCopies&, bool, zero_step_control*,
+                           hipStream_t) {
+    if (!g_threaded.load()) ++g_other_launches;
+    return hipSuccess;
+}
+
+// Thread-local in the threaded scenario: the betas the calling thread passed.
+thread_local float t_beta1 = 0.0f, t_beta2 = 0.0f;
+
+hipError_t launch_control_begin(zero_step_control*, const BiasTable& tab, hipStream_t) {
     if (g_threaded.load()) {
-        // the table belongs to this call's betas and t0: its first entries
-        // are the corrections adam_scalars computed for hp->step itself
-        bool ok = tab.bc1[0] == as.bc1 && tab.bc2[0] == as.bc2;
+        // the table belongs to this call's own betas and t0
+        bool ok = true;
         for (int k = 0; k < ZERO_CTL_STEPS; ++k) {
             const double t = double(tab.t0) + k;
-            ok = ok && tab.bc1[k] == float(1.0 - pow(double(as.beta1), t)) &&
-                 tab.bc2[k] == float(1.0 - pow(double(as.beta2), t));
+            ok = ok && tab.bc1[k] == float(1.0 - pow(double(t_beta1), t)) &&
+                 tab.bc2[k] == float(1.0 - pow(double(t_beta2), t));
         }
         ++g_table_checks;
         if (!ok) ++g_table_bad;
@@ -152,10 +155,7 @@ hipError_t launch_overflow_check_ctl(const ChunkTable&, int, int64_t, const Grad
                                      zero_step_control*, hipStream_t) ZERO_STUB
 hipError_t launch_reduce_mean(const ChunkTable&, int, int64_t, const GradScalars&, uint16_t*,
                               int32_t*, double*, hipStream_t) ZERO_STUB
-hipError_t launch_control_begin(zero_step_control*, hipStream_t) ZERO_STUB
 hipError_t launch_control_decide(zero_step_control*, float, int, hipStream_t) ZERO_STUB
-hipError_t launch_traffic_twin(const ChunkTable&, int, int64_t, const ShardState&,
-                               hipStream_t) ZERO_STUB
 
 }  // namespace zero
 
@@ -250,18 +250,35 @@ static void flatten_tables() {
         end = start + numel[k];
     }
     EXPECT(offs[T] == (end + 2047) / 2048 * 2048);
+    // launches of at most kFlattenBatch slots, each slot's tiles counted in
+    // its table, slots in tensor order with their destinations in the bucket
     int seen = 0;
+    std::vector<const zero::FlattenSlot*> all;
     for (const FlattenLaunch& f : g_flatten) {
-        EXPECT(f.count >= 1 && f.count <= zero::kFlattenBatch);
-        for (const zero::FlattenDesc& d : f.d) {
-            EXPECT(d.slot_len > 0 && d.slot_len <= f.max_slot);
-            EXPECT(d.numel <= d.slot_len);
+        EXPECT(!f.s.empty() && f.s.size() <= size_t(zero::kFlattenBatch));
+        EXPECT(f.tile_start[0] == 0);
+        for (size_t k = 0; k < f.s.size(); ++k) {
+            const zero::FlattenSlot& d = f.s[k];
+            EXPECT(d.slot_len > 0 && d.numel <= d.slot_len);
+            EXPECT(f.tile_start[k + 1] - f.tile_start[k] ==
+                   (d.slot_len + zero::kFlattenTile - 1) / zero::kFlattenTile);
+            all.push_back(&d);
             ++seen;
         }
     }
     int nonempty_slots = 0;
-    for (int k = 0; k < T; ++k) nonempty_slots += ((k + 1 < T ? offs[k + 1] : offs[T]) > offs[k]);
+    for (int k = 0; k < T; ++k) {
+        const int64_t next = k + 1 < T ? offs[k + 1] : offs[T];
+        if (next == offs[k]) continue;
+        const zero::FlattenSlot& d = *all[nonempty_slots];
+        EXPECT(d.dst == static_cast<uint16_t*>(fake(0x200000000000ull)) + offs[k]);
+        EXPECT(d.slot_len == next - offs[k] && d.numel == numel[k]);
+        EXPECT(d.src == (numel[k] ? src[k] : nullptr));
+        ++nonempty_slots;
+    }
     EXPECT(seen == nonempty_slots);
+    EXPECT(g_flatten.size() == size_t((nonempty_slots + zero::kFlattenBatch - 1) /
+                                      zero::kFlattenBatch));
     // capacity too small: ZERO_ERANGE with the offsets still filled
     EXPECT(zero_bucket_flatten(src.data(), numel.data(), T, 256, 2048, fake(0x200000000000ull),
                                offs[T] - 1, offs.data(), nullptr) == ZERO_ERANGE);
@@ -272,32 +289,94 @@ static void flatten_tables() {
                                offs.data(), nullptr) == ZERO_EINVAL);
 }
 
-// Bias tables of the control-block steps: 64 values of t from hp->step.
+// Many buckets in one batch: slots of consecutive buckets share launches,
+// each bucket's offsets are its own layout, and a batch with any bad bucket
+// (too small, overlapping another bucket or another bucket's source) is
+// refused whole, before any launch.
+static void flatten_batch() {
+    reset();
+    const int B = 40;
+    std::vector<std::vector<const void*>> src(B);
+    std::vector<std::vector<int64_t>> numel(B), offs(B);
+    std::vector<zero_flatten_bucket> bk(B);
+    int slots = 0;
+    for (int b = 0; b < B; ++b) {
+        const int nt = 1 + b % 3;
+        for (int k = 0; k < nt; ++k) {
+            numel[b].push_back(1 + (b * 7919 + k * 104729) % 70000);
+            src[b].push_back(fake(kBase + (uint64_t(b) << 24) + (uint64_t(k) << 20)));
+        }
+        offs[b].assign(nt + 1, -1);
+        bk[b] = {src[b].data(), numel[b].data(), offs[b].data(),
+                 fake(0x200000000000ull + (uint64_t(b) << 24)), int64_t(1) << 22, nt, 0};
+        slots += nt;
+    }
+    EXPECT(zero_bucket_flatten_batch(bk.data(), B, 256, 2048, nullptr) == ZERO_OK);
+    EXPECT(g_flatten.size() == size_t((slots + zero::kFlattenBatch - 1) / zero::kFlattenBatch));
+    size_t li = 0, si = 0;
+    for (int b = 0; b < B; ++b) {
+        int64_t end = 0;
+        for (size_t k = 0; k < numel[b].size(); ++k) {
+            const int64_t start = (end + 255) / 256 * 256;
+            EXPECT(offs[b][k] == start);
+            end = start + numel[b][k];
+            const zero::FlattenSlot& d = g_flatten[li].s[si];
+            EXPECT(d.src == src[b][k] && d.numel == numel[b][k]);
+            EXPECT(d.dst == static_cast<uint16_t*>(bk[b].bucket) + start);
+            if (++si == g_flatten[li].s.size()) ++li, si = 0;
+        }
+        EXPECT(offs[b].back() == (end + 2047) / 2048 * 2048);
+    }
+    // refused whole: a bucket too small, two buckets overlapping, a source on
+    // another bucket
+    reset();
+    std::vector<zero_flatten_bucket> bad(bk);
+    bad[7].bucket_capacity = 16;
+    EXPECT(zero_bucket_flatten_batch(bad.data(), B, 256, 2048, nullptr) == ZERO_ERANGE);
+    EXPECT(strstr(zero_last_error_string(), "bucket 7") != nullptr);
+    bad = bk;
+    bad[9].bucket = bk[8].bucket;
+    EXPECT(zero_bucket_flatten_batch(bad.data(), B, 256, 2048, nullptr) == ZERO_EINVAL);
+    bad = bk;
+    std::vector<const void*> moved(src[3]);
+    moved[0] = bk[5].bucket;
+    bad[3].tensors = moved.data();
+    EXPECT(zero_bucket_flatten_batch(bad.data(), B, 256, 2048, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_bucket_flatten_batch(nullptr, 1, 256, 2048, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_bucket_flatten_batch(bk.data(), -1, 256, 2048, nullptr) == ZERO_EINVAL);
+    EXPECT(g_flatten.empty());
+    EXPECT(zero_bucket_flatten_batch(nullptr, 0, 256, 2048, nullptr) == ZERO_OK);
+}
+
+// Bias tables of the control-block steps: zero_control_begin builds one per
+// call, 64 values of t from hp->step; the update calls build none.
 static void bias_tables() {
     reset();
     const void* ch[2] = {fake(kBase), fake(kBase + (1 << 20))};
     float* st[4] = {(float*)fake(0x300000000000ull), (float*)fake(0x310000000000ull),
                     (float*)fake(0x320000000000ull), (float*)fake(0x330000000000ull)};
+    zero_step_control* ctl = (zero_step_control*)fake(0x340000000000ull);
     zero_adamw_params p = hp(1000);
-    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
-                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p, ctl, nullptr) ==
+           ZERO_OK);
+    EXPECT(g_bias.empty() && g_other_launches == 1);
+    EXPECT(zero_control_begin(ctl, &p, nullptr) == ZERO_OK);
     p.bias_correction = 0;
-    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
-                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
-    // the per-thread table cache: back to the first key, then a new t0, then
-    // a new beta1 and a new beta2, each must give that key's own table
+    EXPECT(zero_control_begin(ctl, &p, nullptr) == ZERO_OK);
+    // each call builds its own key's table: the first key again, then a new
+    // t0, then a new beta1 and a new beta2
     p.bias_correction = 1;
-    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
-                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    EXPECT(zero_control_begin(ctl, &p, nullptr) == ZERO_OK);
     p.step = 1001;
-    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
-                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    EXPECT(zero_control_begin(ctl, &p, nullptr) == ZERO_OK);
     p.beta1 = 0.8f;
-    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
-                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    EXPECT(zero_control_begin(ctl, &p, nullptr) == ZERO_OK);
     p.beta2 = 0.99f;
-    EXPECT(zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p,
-                               (zero_step_control*)fake(0x340000000000ull), nullptr) == ZERO_OK);
+    EXPECT(zero_control_begin(ctl, &p, nullptr) == ZERO_OK);
+    // an invalid table is refused before any launch
+    p.beta2 = 1.0f;
+    EXPECT(zero_control_begin(ctl, &p, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_control_begin(ctl, nullptr, nullptr) == ZERO_EINVAL);
     EXPECT(g_bias.size() == 6);
     EXPECT(g_bias[0].t0 == 1000 && g_bias[1].t0 == 1000 && g_bias[2].t0 == 1000);
     EXPECT(g_bias[3].t0 == 1001 && g_bias[4].t0 == 1001 && g_bias[5].t0 == 1001);
@@ -393,8 +472,6 @@ static void launch_length_limits() {
                         nullptr, nullptr, nullptr);     // refused later, for overlapping arrays
     EXPECT(strstr(zero_last_error_string(), "longer than one launch") == nullptr);
     EXPECT(zero_accumulate_chunk(ch[0], too_long, 0, 2, st[0], nullptr, nullptr) == ZERO_EINVAL);
-    EXPECT(zero_traffic_twin(ch, 1, too_long, st[0], st[1], st[2], st[3], st[4], st[5], st[6],
-                             nullptr) == ZERO_EINVAL);
     const int64_t mean_too_long = (zero::kMaxGridBlocks + 1) * zero::kMeanTilePacks * zero::kPack;
     EXPECT(zero_reduce_mean_fp16(ch, 1, mean_too_long, 1.0f, st[0], nullptr, nullptr, nullptr) ==
            ZERO_EINVAL);
@@ -410,8 +487,8 @@ static void launch_length_limits() {
            g_other_launches == 0);
 }
 
-// The bucket table under a control block: the same batching, one bias table
-// per launch, and slices that must tile the state exactly.
+// The bucket table under a control block: the same batching, and slices
+// that must tile the state exactly.
 static void bucket_tables_ctl() {
     reset();
     const int S = 40, N = 8;
@@ -434,7 +511,7 @@ static void bucket_tables_ctl() {
     zero_adamw_params p = hp(7);
     EXPECT(zero_shard_step_buckets_ctl(sl.data(), S, N, off, m, a, v, p16, &p, ctl, nullptr) ==
            ZERO_OK);
-    EXPECT(g_bucket.size() == 2 && g_bias.size() == 2 && g_bias[0].t0 == 7);
+    EXPECT(g_bucket.size() == 2 && g_bias.empty());
     EXPECT(g_bucket[0].n.size() == 32 && g_bucket[1].n.size() == 8);
     // a gap, a missing end, the same copy twice
     EXPECT(zero_shard_step_buckets_ctl(sl.data(), S, N, off + 8, m, a, v, p16, &p, ctl, nullptr) ==
@@ -448,10 +525,10 @@ static void bucket_tables_ctl() {
            ZERO_EINVAL);
 }
 
-// Calls from several threads at once: each thread steps with its own betas
-// and a t0 that keeps changing (so the per-thread bias-table cache both hits
-// and rebuilds), and provokes its own validation errors, whose text must be
-// its own (the error buffer is per thread).
+// Calls from several threads at once: each thread begins steps with its own
+// betas and a t0 that keeps changing, updates, and provokes its own
+// validation errors, whose text must be its own (the error buffer is per
+// thread); every table a begin builds must be its own call's.
 static void threaded_calls(int n_threads, int iters) {
     g_threaded = 1;
     g_table_checks = 0;
@@ -468,8 +545,11 @@ static void threaded_calls(int n_threads, int iters) {
             p.beta1 = 0.9f - 0.01f * th;
             p.beta2 = 0.999f - 0.0001f * th;
             zero_step_control* ctl = (zero_step_control*)fake(0x500000000000ull + 4096 * th);
+            zero::t_beta1 = p.beta1;
+            zero::t_beta2 = p.beta2;
             for (int i = 0; i < iters; ++i) {
                 p.step = 100 + (i / 3 % 5) * 7;
+                if (zero_control_begin(ctl, &p, nullptr) != ZERO_OK) ++wrong_error;
                 if (zero_shard_step_ctl(ch, 2, 4096, st[0], st[1], st[2], st[3], &p, ctl,
                                         nullptr) != ZERO_OK)
                     ++wrong_error;
@@ -501,6 +581,7 @@ int main(int argc, char** argv) {
     bucket_tables_ctl();
     bucket_tables();
     flatten_tables();
+    flatten_batch();
     bias_tables();
     accumulate_modes();
     scaler_and_control();

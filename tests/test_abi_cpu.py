@@ -14,14 +14,15 @@ import sharded_mixed_precision_step_amd as zs
 
 pytestmark = pytest.mark.cpu
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                      "include", "zero_step.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "zero_step.h")
+TWIN_HEADER = os.path.join(INCLUDE, "zero_twin.h")
 
 A = 0x7f0000001000          # a 16-byte aligned fake device address (never dereferenced)
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(zero_[a-z_0-9]+)\s*\(", text)))
 
@@ -32,6 +33,21 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(zs.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
+
+
+def test_measurement_aids_live_in_their_own_library():
+    """The step library exports the step calls only; the benchmark's twin and
+    read stream are in libzerotwin.so, which exports what zero_twin.h
+    declares."""
+    from sharded_mixed_precision_step_amd import twin as zt
+    names = declared_functions(TWIN_HEADER)
+    assert set(names) == set(zt.EXPORTED)
+    lib = ctypes.CDLL(zt.LIB_PATH)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    step_lib = ctypes.CDLL(zs.LIB_PATH)
+    for nm in ("zero_traffic_twin", "zero_stream_read"):
+        assert not hasattr(step_lib, nm), nm
 
 
 def test_single_hip_runtime_in_process():
@@ -163,7 +179,8 @@ def test_traffic_twin_rejects_what_the_step_rejects():
     ins = (B, B + 4 * n, B + 8 * n)
     C = B + (1 << 20)
     outs = (C, C + 4 * n, C + 8 * n, C + 12 * n)
-    twin = lambda ch, nc, nn, i, o: zs.lib.zero_traffic_twin(ch, nc, nn, *i, *o, None)
+    from sharded_mixed_precision_step_amd import twin as zt
+    twin = lambda ch, nc, nn, i, o: zt.lib.zero_traffic_twin(ch, nc, nn, *i, *o, None)
     assert twin(_ptrs(A), 0, n, ins, outs) == zs.ZERO_EINVAL
     assert twin(_ptrs(A + 2), 1, n, ins, outs) == zs.ZERO_EALIGN
     assert twin(_ptrs(A), 1, -1, ins, outs) == zs.ZERO_EINVAL
@@ -171,8 +188,14 @@ def test_traffic_twin_rejects_what_the_step_rejects():
     assert twin(_ptrs(A), 1, n, ins, (outs[0] + 8,) + outs[1:]) == zs.ZERO_EALIGN
     assert twin(_ptrs(A), 1, n, ins, (ins[1],) + outs[1:]) == zs.ZERO_EINVAL
     assert twin(_ptrs(C + 64), 1, n, ins, outs) == zs.ZERO_EINVAL          # chunk on an output
-    assert "zero_traffic_twin" in _last()
+    assert "grad_chunks[0]" in zt.lib.zero_twin_last_error_string().decode()
     assert twin(_ptrs(0), 1, 0, (None,) * 3, (None,) * 4) == zs.ZERO_OK    # n == 0: no-op
+    read = lambda src, nbytes, sink: zt.lib.zero_stream_read(src, nbytes, sink, None)
+    assert read(A, 24, A) == zs.ZERO_EINVAL                                 # not 16-byte units
+    assert read(A + 8, 32, A) == zs.ZERO_EALIGN
+    assert read(A, 32, A + 2) == zs.ZERO_EALIGN
+    assert read(None, 32, A) == zs.ZERO_EINVAL
+    assert read(None, 0, None) == zs.ZERO_OK                                # nothing to read
 
 
 def _buckets(specs, n_chunks, n_state, ins, outs, hp, flag=None):
@@ -269,8 +292,14 @@ def test_control_init_and_ctl_calls_reject_bad_arguments():
     assert zs.lib.zero_control_init(ctypes.byref(ctl), ctypes.byref(bad), 1) == zs.ZERO_EINVAL
     assert zs.lib.zero_control_init(None, ctypes.byref(good), 1) == zs.ZERO_EINVAL
     # device-side calls: bad pointers are refused before any launch
-    assert zs.lib.zero_control_begin(None, None) == zs.ZERO_EINVAL
-    assert zs.lib.zero_control_begin(A + 4, None) == zs.ZERO_EALIGN
+    hp = _hp()
+    assert zs.lib.zero_control_begin(None, ctypes.byref(hp), None) == zs.ZERO_EINVAL
+    assert zs.lib.zero_control_begin(A + 4, ctypes.byref(hp), None) == zs.ZERO_EALIGN
+    assert zs.lib.zero_control_begin(A, None, None) == zs.ZERO_EINVAL       # no table
+    bad_hp = _hp(step=0)
+    assert zs.lib.zero_control_begin(A, ctypes.byref(bad_hp), None) == zs.ZERO_EINVAL
+    bad_hp = _hp(beta2=1.0)
+    assert zs.lib.zero_control_begin(A, ctypes.byref(bad_hp), None) == zs.ZERO_EINVAL
     assert zs.lib.zero_control_decide(A, float("nan"), 0, None) == zs.ZERO_EINVAL
     assert zs.lib.zero_control_decide(None, 1.0, 0, None) == zs.ZERO_EINVAL
     assert zs.lib.zero_overflow_check_ctl(_ptrs(A), 1, 10, None, None) == zs.ZERO_EINVAL
@@ -328,6 +357,48 @@ def test_flatten_validation_and_layout():
     assert _flatten([0], [5], 256, 512, B, 4096)[0] == zs.ZERO_EINVAL
     assert _flatten([A], [5], 0, 512, B, 4096)[0] == zs.ZERO_EINVAL
     assert _flatten([B + 64], [5], 256, 512, B, 4096)[0] == zs.ZERO_EINVAL   # source inside bucket
+
+
+def _flatten_batch(specs, align, pad):
+    """specs: (tensor pointers, numels, bucket, capacity) per bucket."""
+    table = (zs.FlattenBucketC * max(len(specs), 1))()
+    keep, offs = [], []
+    for k, (ptrs, numels, bucket, cap) in enumerate(specs):
+        nt = len(numels)
+        parr = _ptrs(*ptrs) if ptrs else _ptrs(0)
+        narr = (ctypes.c_int64 * max(nt, 1))(*numels)
+        oarr = (ctypes.c_int64 * (nt + 1))()
+        keep.append((parr, narr))
+        offs.append(oarr)
+        table[k].tensors = ctypes.cast(parr, ctypes.POINTER(ctypes.c_void_p))
+        table[k].numels = ctypes.cast(narr, ctypes.POINTER(ctypes.c_int64))
+        table[k].offsets_out = ctypes.cast(oarr, ctypes.POINTER(ctypes.c_int64))
+        table[k].bucket, table[k].bucket_capacity, table[k].n_tensors = bucket, cap, nt
+    rc = zs.lib.zero_bucket_flatten_batch(table, len(specs), align, pad, None)
+    return rc, [list(o) for o in offs]
+
+
+def test_flatten_batch_validates_every_bucket_first():
+    """The batch refuses a bad bucket anywhere in it, names it, and fills the
+    offsets of the buckets before it; empty batches and empty buckets are
+    no-ops."""
+    B = A + (1 << 24)
+    C = B + (1 << 24)
+    assert _flatten_batch([], 256, 512) == (zs.ZERO_OK, [])
+    assert _flatten_batch([([], [], B, 0), ([A], [0], C, 0)], 256, 512) == \
+        (zs.ZERO_OK, [[0], [0, 0]])
+    rc, offs = _flatten_batch([([A], [5], B, 4096), ([A + 4096, A + 8192], [300, 1], C, 700)],
+                              256, 512)
+    assert rc == zs.ZERO_ERANGE and offs == [[0, 512], [0, 512, 1024]]
+    assert "bucket 1" in _last()
+    assert _flatten_batch([([A], [5], B, 4096), ([A], [5], B + 512, 4096)],
+                          256, 512)[0] == zs.ZERO_EINVAL                    # buckets overlap
+    assert _flatten_batch([([A], [5], B, 4096), ([B + 64], [5], C, 4096)],
+                          256, 512)[0] == zs.ZERO_EINVAL                    # source on bucket 0
+    assert _flatten_batch([([A], [5], B, 4096), ([A + 1], [5], C, 4096)],
+                          256, 512)[0] == zs.ZERO_EALIGN
+    assert zs.lib.zero_bucket_flatten_batch(None, 1, 256, 512, None) == zs.ZERO_EINVAL
+    assert zs.lib.zero_bucket_flatten_batch(None, -1, 256, 512, None) == zs.ZERO_EINVAL
 
 
 def test_scaler_matches_oracle_on_forced_sequences():

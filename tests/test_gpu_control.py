@@ -5,8 +5,9 @@ gradient-norm clipping) and single pass (commit on the device). They walk
 the same states as the oracle's step, loss scaler and t over clean and
 overflowing steps. This holds over the whole shard, a bucket table, buckets
 streamed as they arrive, and the two-pass flow over buckets, at N = 1..64.
-Also: the two-pass norm and clip factor repeat bit for bit; a stale
-bias-correction table is refused on the device; the prepared step equals
+Also: the two-pass norm and clip factor repeat bit for bit; a step whose t
+lies outside its bias-correction table changes nothing in any flow; a
+misaligned bucket is refused before the decision; the prepared step equals
 the unprepared one; and a HIP graph of one step replays like the eager
 calls."""
 import struct
@@ -165,23 +166,155 @@ def test_two_pass_without_clip_equals_host_driven_step():
         assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), k
 
 
-def test_stale_bias_table_is_refused_on_the_device():
-    """t = 100 against a table based at t0 = 1 (covering t = 1..64): bit 0 of
-    the error word is set and the state is left alone."""
+_KEPT = ("scale", "growth_factor", "backoff_factor", "min_scale", "max_scale",
+         "growth_interval", "good_steps", "cur", "skipped_steps", "step")
+
+
+def _bits(tensors):
+    return [x.clone().view(torch.uint8) for x in tensors]
+
+
+@pytest.mark.parametrize("flow", ["single_pass", "bucket_table", "streamed", "two_pass",
+                                  "two_pass_buckets"])
+@pytest.mark.parametrize("t_block,t0", [(100, 1), (65, 1), (5, 6)])
+def test_bias_table_miss_changes_nothing(flow, t_block, t0):
+    """A step whose t lies outside the table zero_control_begin was given
+    (t = 100 or 65 against t0 = 1, which covers 1..64; t = 5 below t0 = 6)
+    is void in every flow: error bit 0, table_miss and skip are set, and t,
+    the loss scale, good_steps, skipped_steps and the current copy stay as
+    they were, as do both copies of the state, bit for bit.  The two-pass
+    flows decide before they update, so the miss has to be known from begin
+    on; the single-pass flows must not commit the copy no kernel wrote.  With
+    the table moved to cover t, the next step runs and matches the oracle."""
     dev = device()
     w = _workload()
     h = wl.host_shard(w, n=n, offset_seed=904)
-    d = {k: torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16")}
-    snap = {k: x.clone() for k, x in d.items()}
     chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
-    scaler, _ = _scaler()
-    ctl = zs.control_new(scaler, 100, dev)
-    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper.replace(step=1)))
-    stepper.two_pass(chunks, d["master"], d["m"], d["v"], d["p16"])
+    a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+    b = tuple(torch.full_like(x, float("nan")) for x in a)
+    copies = (a, b)
+    scaler = zs.LossScaler.create(scale=65536.0, growth_interval=2)
+    scaler.good_steps = 1                       # a clean step would grow the scale
+    ctl = zs.control_new(scaler, t_block, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper.replace(step=t0)))
+    before = zs.control_read(ctl)
+    snap = _bits(a) + _bits(b)
+    sizes = [8 * 1000, 8 * 1001, n - 8 * 2001]
+    offs = [0, 8 * 1000, 8 * 2001]
+    buckets = [([c[o:o + s] for c in chunks], o) for o, s in zip(offs, sizes)]
+
+    def run():
+        if flow == "single_pass":
+            stepper.single_pass(chunks, copies)
+        elif flow == "bucket_table":
+            stepper.single_pass_buckets(zs.BucketSlices(buckets), copies)
+        elif flow == "streamed":
+            stepper.single_pass_streamed(iter(buckets), copies)
+        elif flow == "two_pass":
+            stepper.two_pass(chunks, *a, max_grad_norm=1.0)
+        else:
+            stepper.two_pass_buckets(buckets, *a, max_grad_norm=1.0)
+
+    print(f"case: bias-table miss flow={flow} t={t_block} t0={t0}", flush=True)
+    run()
     c = zs.control_read(ctl)
-    assert c.error & 1 and c.skip == 0
-    for k in d:
-        assert torch.equal(d[k].view(torch.uint8), snap[k].view(torch.uint8)), k
+    assert c.error & 1 and c.table_miss == 1 and c.skip == 1, (c.error, c.table_miss, c.skip)
+    for name in _KEPT:
+        assert getattr(c, name) == getattr(before, name), name
+    for x, y in zip(snap, _bits(a) + _bits(b)):
+        assert torch.equal(x, y)
+    # the caller clears the error and moves the table base to t: the step runs
+    host = zs.control_read(ctl)
+    host.error = 0
+    ctl.copy_(torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8))
+    stepper.hp.step = t_block
+    run()
+    c = zs.control_read(ctl)
+    want = ozs.shard_step_clipped(h["chunks"], h["master"], h["m"], h["v"], h["p16"],
+                                  w.hyper.replace(step=t_block), 65536.0,
+                                  1.0 if flow.startswith("two_pass") else 0.0)
+    assert c.error == 0 and c.table_miss == 0 and c.skip == 0 and c.step == t_block + 1
+    assert c.scale == 131072.0 and c.good_steps == 0       # grew on this clean step
+    got = a if flow.startswith("two_pass") else copies[c.cur]
+    assert_matches_oracle(dict(zip(("master", "m", "v", "p16"), got)), want, max_ulp=None)
+
+
+def test_last_entry_of_the_bias_table_is_used():
+    """t = t0 + ZERO_CTL_STEPS - 1, the table's last entry, is a hit: the
+    single pass runs and matches the oracle at that t."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=916)
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    copies = _state(h, dev)
+    t = 1 + zs.ZERO_CTL_STEPS - 1
+    ctl = zs.control_new(zs.LossScaler.create(scale=65536.0), t, dev)
+    print(f"case: bias table last entry t={t} t0=1", flush=True)
+    zs.DeviceStepper(ctl, zs.adamw_params(w.hyper.replace(step=1))).single_pass(chunks, copies)
+    c = zs.control_read(ctl)
+    assert c.error == 0 and c.table_miss == 0 and c.skip == 0 and c.step == t + 1
+    want = ozs.shard_step(h["chunks"], h["master"], h["m"], h["v"], h["p16"],
+                          w.hyper.replace(step=t), 65536.0)
+    _assert_state(copies[1], want, "last table entry")
+
+
+def test_two_pass_buckets_refuse_a_misaligned_bucket_before_deciding():
+    """A bucket whose offset is not a multiple of 8, or whose chunks are not
+    16-byte aligned, would be refused by its in-place update only after the
+    decision had moved t and the scale and earlier buckets had been updated.
+    two_pass_buckets refuses it first: the block and the state are left
+    bit-identical."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=914)
+    state = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    ctl = zs.control_new(_scaler()[0], w.hyper.step, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+    before = zs.control_read(ctl)
+    snap = _bits(state)
+    cut = 8 * 1000 + 4                               # offset of the second bucket: 4 mod 8
+    bad_offset = [([c[:cut] for c in chunks], 0), ([c[cut:] for c in chunks], cut)]
+    with pytest.raises(ValueError, match="multiple of 8"):
+        stepper.two_pass_buckets(bad_offset, *state)
+    spare = [torch.empty(n + 8, dtype=torch.float16, device=dev) for _ in range(N)]
+    for sp, c in zip(spare, chunks):
+        sp[1:n + 1].copy_(c)
+    bad_chunk = [([c[:8 * 1000] for c in chunks], 0),
+                 ([sp[1 + 8 * 1000:n + 1] for sp in spare], 8 * 1000)]   # 2 bytes off
+    with pytest.raises(ValueError, match="16-byte aligned"):
+        stepper.two_pass_buckets(bad_chunk, *state)
+    print("case: two-pass buckets refuse a misaligned bucket", flush=True)
+    c = zs.control_read(ctl)
+    for name in _KEPT + ("error", "step_used"):
+        assert getattr(c, name) == getattr(before, name), name
+    for x, y in zip(snap, _bits(state)):
+        assert torch.equal(x, y)
+
+
+def test_stepping_on_a_side_stream_past_the_table_rebases_correctly():
+    """Steps enqueued on a stream that is not torch's current one, past
+    ZERO_CTL_STEPS of them with no synchronisation from the caller: the
+    stepper's rebase waits for the device before reading t back, so no step
+    misses the table and t counts every clean step."""
+    dev = device()
+    w = _workload()
+    nn = 4_099
+    h = wl.host_shard(w, n=nn, offset_seed=915)
+    chunks = [torch.from_numpy(c[:nn]).to(dev) for c in h["chunks"]]
+    a = tuple(torch.from_numpy(h[k][:nn]).to(dev) for k in ("master", "m", "v", "p16"))
+    copies = (a, tuple(torch.empty_like(x) for x in a))
+    ctl = zs.control_new(zs.LossScaler.create(scale=65536.0), w.hyper.step, dev)
+    stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+    side = torch.cuda.Stream()
+    steps = 2 * zs.ZERO_CTL_STEPS + 5
+    print(f"case: {steps} single-pass steps on a side stream", flush=True)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        stepper.single_pass(chunks, copies, stream=side)
+    side.synchronize()
+    c = zs.control_read(ctl)
+    assert c.error == 0 and c.table_miss == 0 and c.step == w.hyper.step + steps
 
 
 def test_graph_of_one_step_replays_like_eager_calls():
@@ -548,7 +681,7 @@ def test_check_partials_accumulate_over_buckets():
     got = []
     for rep in range(2):
         ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
-        zs.zero_control_begin(ctl)
+        zs.zero_control_begin(ctl, zs.adamw_params(w.hyper))
         zs.zero_overflow_check_ctl([c[:half] for c in chunks], ctl)
         zs.zero_overflow_check_ctl([c[half:] for c in chunks], ctl)
         zs.zero_control_decide(ctl, 0.0, False)

@@ -16,8 +16,9 @@ elsewhere.
   through the oracle's flatten; and against 160 single-slice calls and the
   device-controlled table call.
 * 70B-class shard (4,412,500,000 params, N = 16) streamed in 23 buckets
-  through two chunk buffers: buckets 0, 11 and 22 checked in full, the rest
-  by the fp16 writeback property.
+  through two chunk buffers: every bucket against the oracle element by
+  element as it completes, the squared norm against the oracle's sum over
+  the buckets, and the fp16 writeback property over the whole shard.
 """
 import gc
 from concurrent.futures import ThreadPoolExecutor
@@ -231,13 +232,42 @@ def test_zero2_bucketed_full():
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
-LLAMA70B_SAMPLED = (0, 11, 22)
+def test_zero2_rank_flatten_batch_full():
+    """The rank's own 160 gradient buckets (bench.py's flatten leg) flattened
+    by one zero_bucket_flatten_batch call: every bucket equals the one
+    zero_bucket_flatten call per bucket gives, bit for bit, and the sampled
+    buckets equal the oracle's flatten of the tensors."""
+    dev = device()
+    w = wl.ZERO2
+    r = wl.ZERO2_RANK
+    align, pad = wl.ZERO2_ALIGN, wl.ZERO2_ALIGN * w.n_replicas
+    sizes = [int(np.prod(s)) for _, s in wl.zero2_tensors()]
+    plan = wl.zero2_bucket_plan()
+    layouts = [ofl.bucket_layout([sizes[k] for k in idx], align, pad) for idx in plan]
+    print(f"case: full zero2 rank flatten batch, {len(plan)} buckets", flush=True)
+    grads = [[wl.zero2_device_tensor(r, k, dev) for k in idx] for idx in plan]
+    batch = [torch.empty(lay[-1], dtype=torch.float16, device=dev) for lay in layouts]
+    single = [torch.empty(lay[-1], dtype=torch.float16, device=dev) for lay in layouts]
+    offs = zs.zero_bucket_flatten_batch(list(zip(grads, batch)), align=align, pad_multiple=pad)
+    assert offs == layouts
+    for ts, bk in zip(grads, single):
+        zs.zero_bucket_flatten(ts, bk, align=align, pad_multiple=pad)
+    torch.cuda.synchronize()
+    for b, (x, y) in enumerate(zip(batch, single)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), b
+    for b in ZERO2_SAMPLED:
+        want = ofl.flatten([t.cpu().numpy() for t in grads[b]], align, pad)[0]
+        assert np.array_equal(batch[b].cpu().numpy().view(np.uint16), want.view(np.uint16)), b
 
 
 def test_llama70b_shard_streamed():
     """The launch sequence bench.py times for this shard: one step under the
     device control block, each bucket updated as it arrives in one of two
-    chunk buffers (the other refilled meanwhile), one decision at the end."""
+    chunk buffers (the other refilled meanwhile), one decision at the end.
+    Every one of the 23 buckets is compared with the oracle element by
+    element as soon as its update is done (before its buffer is refilled),
+    and the oracle's squared norms, summed over the buckets, must match the
+    block's."""
     dev = device()
     w = wl.LLAMA70B_SHARD
     N, S = w.n_replicas, w.loss_scale
@@ -251,6 +281,7 @@ def test_llama70b_shard_streamed():
             for _ in range(2)]
     ctl = zs.control_new(zs.LossScaler.create(scale=S), w.hyper.step, dev)
     checked = []
+    want_sq_total = [0.0]
 
     def arrivals():
         off = 0
@@ -258,25 +289,23 @@ def test_llama70b_shard_streamed():
             chunks = [c[:nb] for c in bufs[b % 2]]
             wl.device_chunks(w, dev, n=nb, offset_seed=100 + b, out=chunks)
             yield chunks, off
-            # bucket b's update is enqueued; check the sampled ones now,
-            # before their buffer is refilled
-            if b in LLAMA70B_SAMPLED:
-                torch.cuda.synchronize()
-                print(f"case: llama70b bucket {b} (n={nb}) step vs oracle", flush=True)
-                s_in = tuple(t[off:off + nb] for t in cur)
-                s_out = tuple(t[off:off + nb] for t in out)
-                overflow, want_sq, _ = compare_with_oracle(chunks, s_in, s_out, w.hyper, S,
-                                                           label=f"bucket {b} ")
-                fb, sb = flags(dev)
-                zs.zero_overflow_check(chunks, S, fb, sb)
-                assert not overflow and int(fb.item()) == 0
-                assert rel_close(float(sb.item()), want_sq)
-                checked.append(b)
+            # bucket b's update is enqueued; check it now, before its buffer
+            # is refilled
+            torch.cuda.synchronize()
+            print(f"case: llama70b bucket {b} (n={nb}) step vs oracle", flush=True)
+            s_in = tuple(t[off:off + nb] for t in cur)
+            s_out = tuple(t[off:off + nb] for t in out)
+            overflow, want_sq, _ = compare_with_oracle(chunks, s_in, s_out, w.hyper, S,
+                                                       label=f"bucket {b} ")
+            assert not overflow
+            want_sq_total[0] += want_sq
+            checked.append(b)
             off += nb
 
     zs.DeviceStepper(ctl, zs.adamw_params(w.hyper)).single_pass_streamed(arrivals(), (cur, out))
     c = zs.control_read(ctl)
-    assert checked == list(LLAMA70B_SAMPLED)
+    assert checked == list(range(len(w.buckets)))
     assert c.error == 0 and c.overflow == 0 and c.skip == 0 and c.cur == 1
-    assert c.step == w.hyper.step + 1 and c.scale == S and c.sqnorm > 0.0
+    assert c.step == w.hyper.step + 1 and c.scale == S
+    assert rel_close(c.sqnorm, want_sq_total[0]), (c.sqnorm, want_sq_total[0])
     _assert_writeback_property(out[0], out[3], "llama70b")

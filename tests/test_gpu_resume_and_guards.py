@@ -19,6 +19,7 @@ import oracle.zero_step as ozs
 import sharded_mixed_precision_step_amd as zs
 import workloads as wl
 from gpu_util import device, flags, guarded, guards_intact
+from sharded_mixed_precision_step_amd import twin as zt
 
 pytestmark = pytest.mark.gpu
 
@@ -169,7 +170,7 @@ def test_no_writes_outside_the_outputs(nn):
         zs.BucketSlices([(chunks, 0)]), (tuple(t0[k][1] for k in ("master", "m", "v", "p16")),
                                          tuple(t1[k][1] for k in ("master", "m", "v", "p16"))))
     tw_src, tw_dst = state(), state(dst_nan=True)
-    zs.zero_traffic_twin(chunks, *(tw_src[k][1] for k in ("master", "m", "v")),
+    zt.zero_traffic_twin(chunks, *(tw_src[k][1] for k in ("master", "m", "v")),
                          *(tw_dst[k][1] for k in ("master", "m", "v", "p16")))
     # the fp16 mean and the accumulator
     mbuf, mean = guarded(nn, torch.float16, dev)
