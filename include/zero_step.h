@@ -342,6 +342,31 @@ int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n
                           float* acc, void* mean_fp16, void* stream);
 
 /*
+ * zero_accumulate_chunk_noalloc -- zero_accumulate_chunk with the library's
+ * own accumulator, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Each call does exactly what zero_accumulate_chunk(chunk, n, index,
+ * n_chunks, acc, mean_fp16, stream) does, with acc the library's
+ * accumulator: a file-scope device array of ZERO_FOLD_SCRATCH_ELEMS fp32
+ * values (32 MiB) that each GPU the library runs on holds until the process
+ * ends.  The call allocates and frees nothing; the first call on a device
+ * looks up that device's copy of the array.  Every call on one GPU shares
+ * that GPU's array and it keeps the last call's contents, so the N calls of
+ * one fold (index 0 .. N-1) must run in order and no other fold may run on
+ * that GPU between them: folds that overlap in time on one GPU race.  Nothing
+ * needs clearing: index 0 writes the accumulator before anything reads it.
+ *
+ *   chunk, index, n_chunks, mean_fp16, stream   as for zero_accumulate_chunk
+ *   n   elements, 0 .. ZERO_FOLD_SCRATCH_ELEMS
+ * Returns ZERO_OK, ZERO_EINVAL, ZERO_EALIGN, ZERO_ERANGE (n above
+ * ZERO_FOLD_SCRATCH_ELEMS; nothing is enqueued) or ZERO_EHIP.
+ */
+#define ZERO_FOLD_SCRATCH_ELEMS 8388608
+int zero_accumulate_chunk_noalloc(const void* chunk, int64_t n, int32_t index, int32_t n_chunks,
+                                  void* mean_fp16, void* stream);
+
+/*
  * zero_bucket_flatten -- pack whole fp16 gradient tensors into one bucket.
  *
  * Several parameters' gradients are grouped into a bucket and reduced as one

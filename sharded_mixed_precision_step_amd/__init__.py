@@ -32,7 +32,8 @@ ZERO_MAX_CHUNKS = 64
 
 EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
             "zero_shard_step_buckets", "zero_reduce_mean_fp16", "zero_accumulate_chunk",
-            "zero_bucket_flatten", "zero_bucket_flatten_batch", "zero_update_loss_scale",
+            "zero_accumulate_chunk_noalloc", "zero_bucket_flatten", "zero_bucket_flatten_batch",
+            "zero_update_loss_scale",
             "zero_control_init",
             "zero_control_begin", "zero_overflow_check_ctl", "zero_control_decide",
             "zero_shard_step_ctl", "zero_shard_step_out_ctl", "zero_shard_step_buckets_ctl",
@@ -41,6 +42,7 @@ ZERO_CTL_STEPS = 64
 ZERO_NORM_SLOTS = 16
 ZERO_NORM_STRIDE = 8
 ZERO_CHECK_PARTS = 1536
+ZERO_FOLD_SCRATCH_ELEMS = 8388608
 
 
 class ZeroStepError(RuntimeError):
@@ -124,6 +126,7 @@ def _load() -> ctypes.CDLL:
                                              ctypes.POINTER(AdamWParams), vp, vp, vp]
     lib.zero_reduce_mean_fp16.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp, vp]
     lib.zero_accumulate_chunk.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.zero_accumulate_chunk_noalloc.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.zero_bucket_flatten.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), i32, i64, i64,
                                         vp, i64, ctypes.POINTER(ctypes.c_int64), vp]
     lib.zero_bucket_flatten_batch.argtypes = [ctypes.POINTER(FlattenBucketC), i32, i64, i64, vp]
@@ -346,6 +349,19 @@ def zero_accumulate_chunk(chunk: torch.Tensor, index: int, n_chunks: int,
                                      int(n_chunks), _opt(acc, torch.float32, "acc"),
                                      _opt(mean_fp16, torch.float16, "mean_fp16"),
                                      _stream(stream)))
+
+
+def zero_accumulate_chunk_noalloc(chunk: torch.Tensor, index: int, n_chunks: int,
+                                  mean_fp16: Optional[torch.Tensor], stream=None) -> None:
+    """zero_accumulate_chunk with the library's own accumulator (no device
+    memory allocated; see zero_step.h for the sharing rules)."""
+    n = chunk.numel()
+    if mean_fp16 is not None and mean_fp16.numel() != n:
+        raise ValueError(f"mean_fp16 has {mean_fp16.numel()} elements, expected {n}")
+    _check(lib.zero_accumulate_chunk_noalloc(_dev(chunk, torch.float16, "chunk"), n, int(index),
+                                             int(n_chunks),
+                                             _opt(mean_fp16, torch.float16, "mean_fp16"),
+                                             _stream(stream)))
 
 
 def zero_bucket_flatten(tensors: Sequence[torch.Tensor], bucket: torch.Tensor,

@@ -646,6 +646,49 @@ int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n
     return e == hipSuccess ? ok() : hip_fail(e, who);
 }
 
+int zero_accumulate_chunk_noalloc(const void* chunk, int64_t n, int32_t index, int32_t n_chunks,
+                                  void* mean_fp16, void* stream) {
+    static const char* who = "zero_accumulate_chunk_noalloc";
+    if (n_chunks < 1 || n_chunks > ZERO_MAX_CHUNKS)
+        return fail(ZERO_EINVAL, "%s: n_chunks = %d outside [1, %d]", who, n_chunks,
+                    ZERO_MAX_CHUNKS);
+    if (index < 0 || index >= n_chunks)
+        return fail(ZERO_EINVAL, "%s: index = %d outside [0, %d)", who, index, n_chunks);
+    if (n < 0) return fail(ZERO_EINVAL, "%s: n < 0", who);
+    if (n > ZERO_FOLD_SCRATCH_ELEMS)
+        return fail(ZERO_ERANGE,
+                    "%s: n = %lld exceeds the %lld-element accumulator of the allocation-free "
+                    "fold (use zero_accumulate_chunk with an accumulator of your own)",
+                    who, static_cast<long long>(n),
+                    static_cast<long long>(ZERO_FOLD_SCRATCH_ELEMS));
+    const int mode = n_chunks == 1 ? 3 : index == 0 ? 0 : index == n_chunks - 1 ? 2 : 1;
+    const bool uses_acc = mode != 3, writes_mean = mode >= 2;
+    if (n == 0) return ok();
+    if (!chunk) return fail(ZERO_EINVAL, "%s: chunk is NULL", who);
+    if (!aligned(chunk, 16)) return fail(ZERO_EALIGN, "%s: chunk is not 16-byte aligned", who);
+    if (writes_mean) {
+        if (!mean_fp16) return fail(ZERO_EINVAL, "%s: mean_fp16 is NULL", who);
+        if (!aligned(mean_fp16, 16))
+            return fail(ZERO_EALIGN, "%s: mean_fp16 is not 16-byte aligned", who);
+        if (overlap(mean_fp16, 2 * n, chunk, 2 * n))
+            return fail(ZERO_EINVAL, "%s: mean_fp16 overlaps chunk", who);
+    }
+    float* acc = nullptr;
+    if (uses_acc) {
+        const hipError_t e = zero::fold_scratch(&acc);
+        if (e != hipSuccess) return hip_fail(e, "zero_accumulate_chunk_noalloc: scratch address");
+    }
+    zero::ChunkTable unused;
+    zero::GradScalars gs;
+    const void* none[1] = {nullptr};
+    int rc = check_chunks(none, n_chunks, 0, 1.0f, &unused, &gs);  // the 1/N scalars
+    if (rc) return rc;
+    const hipError_t e = zero::launch_accumulate(static_cast<const uint16_t*>(chunk), n, mode, gs,
+                                                 acc, static_cast<uint16_t*>(mean_fp16),
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
 int zero_control_init(zero_step_control* ctl, const zero_loss_scaler* scaler, int64_t step) {
     if (!ctl || !scaler) return fail(ZERO_EINVAL, "zero_control_init: ctl or scaler is NULL");
     int rc = check_scaler(scaler);

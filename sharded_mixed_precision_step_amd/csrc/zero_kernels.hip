@@ -39,7 +39,18 @@
 // floating-point contraction, division and square root are the correctly
 // rounded forms), so results match the plain per-operation definition bit
 // for bit.
+#include <atomic>
+#include <mutex>
+
 #include "zero_internal.h"
+
+// The accumulator of the allocation-free arrival fold
+// (zero_accumulate_chunk_noalloc): ZERO_FOLD_SCRATCH_ELEMS fp32 values
+// (32 MiB), one copy in each device's memory for as long as the process
+// lives.  In host code this name stands for a host-side shadow, not a device
+// address: host code never passes it to a kernel or a copy, only to
+// hipGetSymbolAddress (fold_scratch below), and uses the address that gives.
+static __device__ __align__(256) float scratch[ZERO_FOLD_SCRATCH_ELEMS];
 
 namespace zero {
 namespace {
@@ -737,6 +748,12 @@ __global__ __launch_bounds__(kBlock) void bucket_flatten_kernel(FlattenTable t) 
 // Launch sizing.
 // ---------------------------------------------------------------------------
 
+// Device addresses of `scratch`, one per device, each looked up once with
+// that device current (every device holds its own copy of the array).
+constexpr int kMaxScratchDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+
 // Compute units of the current device, asked of the runtime at each launch
 // that sizes a resident grid (the runtime answers from its own device
 // table; nothing is kept here).
@@ -915,6 +932,28 @@ hipError_t launch_reduce_mean(const ChunkTable& chunks, int n_chunks, int64_t n,
                                                 d_sqnorm, stream);
     }
 #undef ZERO_CASE
+}
+
+hipError_t fold_scratch(float** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void* addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (addr == nullptr) return hipErrorInvalidSymbol;
+            p = static_cast<float*>(addr);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const GradScalars& gs,

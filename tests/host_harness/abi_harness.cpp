@@ -135,9 +135,20 @@ hipError_t launch_control_begin(zero_step_control*, const BiasTable& tab, hipStr
     return hipSuccess;
 }
 
-hipError_t launch_accumulate(const uint16_t*, int64_t, int mode, const GradScalars&, float*,
+std::vector<const float*> g_accumulate_acc;
+int g_scratch_lookups = 0;
+
+hipError_t launch_accumulate(const uint16_t*, int64_t, int mode, const GradScalars&, float* acc,
                              uint16_t*, hipStream_t) {
     g_accumulate_mode.push_back(mode);
+    g_accumulate_acc.push_back(acc);
+    return hipSuccess;
+}
+
+// the library's own accumulator, at a fake device address
+hipError_t fold_scratch(float** ptr) {
+    ++g_scratch_lookups;
+    *ptr = static_cast<float*>(fake(0x600000000000ull));
     return hipSuccess;
 }
 
@@ -395,6 +406,37 @@ static void bias_tables() {
     }
 }
 
+// The allocation-free fold: the same modes, the library's accumulator in
+// place of the caller's, and n above ZERO_FOLD_SCRATCH_ELEMS refused before
+// any device call.
+static void accumulate_noalloc() {
+    reset();
+    zero::g_accumulate_acc.clear();
+    zero::g_scratch_lookups = 0;
+    const void* ch = fake(kBase);
+    void* mean = fake(0x400000000000ull);
+    EXPECT(zero_accumulate_chunk_noalloc(ch, ZERO_FOLD_SCRATCH_ELEMS + 1, 0, 4, mean, nullptr) ==
+           ZERO_ERANGE);
+    EXPECT(strstr(zero_last_error_string(), "allocation-free") != nullptr);
+    EXPECT(zero_accumulate_chunk_noalloc(ch, 100, 4, 4, mean, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_accumulate_chunk_noalloc(ch, 100, 0, 0, mean, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_accumulate_chunk_noalloc(fake(kBase + 8), 100, 0, 4, mean, nullptr) ==
+           ZERO_EALIGN);
+    EXPECT(zero_accumulate_chunk_noalloc(ch, 100, 3, 4, nullptr, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_accumulate_chunk_noalloc(ch, 100, 3, 4, fake(kBase + 64), nullptr) ==
+           ZERO_EINVAL);                                       // mean over the chunk
+    EXPECT(g_accumulate_mode.empty() && zero::g_scratch_lookups == 0);
+    for (int i = 0; i < 4; ++i)
+        EXPECT(zero_accumulate_chunk_noalloc(ch, ZERO_FOLD_SCRATCH_ELEMS, i, 4,
+                                             i == 3 ? mean : nullptr, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunk_noalloc(ch, 100, 0, 1, mean, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunk_noalloc(ch, 0, 0, 4, nullptr, nullptr) == ZERO_OK);  // no-op
+    EXPECT((g_accumulate_mode == std::vector<int>{0, 1, 1, 2, 3}));
+    for (int i = 0; i < 4; ++i)
+        EXPECT(zero::g_accumulate_acc[i] == static_cast<float*>(fake(0x600000000000ull)));
+    EXPECT(zero::g_accumulate_acc[4] == nullptr && zero::g_scratch_lookups == 4);
+}
+
 // Which accumulate mode each (index, N) selects, and what it may leave NULL.
 static void accumulate_modes() {
     reset();
@@ -584,6 +626,7 @@ int main(int argc, char** argv) {
     flatten_batch();
     bias_tables();
     accumulate_modes();
+    accumulate_noalloc();
     scaler_and_control();
     empty_and_errors();
     threaded_calls(4, 100);

@@ -280,6 +280,24 @@ def test_reduce_mean_and_accumulate_reject_bad_arguments():
     assert acc(None, 0, 0, 1, None, None) == zs.ZERO_OK                 # n == 0: no-op
 
 
+def test_allocation_free_fold_refuses_what_it_cannot_hold():
+    """n above the library accumulator's ZERO_FOLD_SCRATCH_ELEMS is refused
+    with ZERO_ERANGE before anything reaches the device; bad arguments are
+    refused as zero_accumulate_chunk refuses them."""
+    B = A + (1 << 24)
+    fold = lambda ch, nn, idx, nc, mean: zs.lib.zero_accumulate_chunk_noalloc(ch, nn, idx, nc,
+                                                                               mean, None)
+    assert fold(A, zs.ZERO_FOLD_SCRATCH_ELEMS + 1, 0, 8, B) == zs.ZERO_ERANGE
+    assert "allocation-free" in _last()
+    assert fold(A, 100, 8, 8, B) == zs.ZERO_EINVAL
+    assert fold(A, 100, 0, 65, B) == zs.ZERO_EINVAL
+    assert fold(A, -1, 0, 8, B) == zs.ZERO_EINVAL
+    assert fold(A + 8, 100, 0, 8, B) == zs.ZERO_EALIGN
+    assert fold(A, 100, 7, 8, None) == zs.ZERO_EINVAL                  # the last needs the mean
+    assert fold(A, 100, 7, 8, B + 8) == zs.ZERO_EALIGN
+    assert fold(None, 0, 0, 8, None) == zs.ZERO_OK                       # n == 0: no-op
+
+
 def test_control_init_and_ctl_calls_reject_bad_arguments():
     ctl = zs.StepControl()
     good = zs.LossScaler.create(scale=65536.0, growth_interval=3)
