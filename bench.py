@@ -378,7 +378,8 @@ def bench_zero2(args, dev):
     the update alone as one zero_shard_step_buckets call, as 160
     zero_shard_step_out calls, and as one call over the contiguous shard
     (same bytes, the launch-free ideal); and the rank flattening its own 160
-    gradient buckets.  Prints one JSON line."""
+    gradient buckets, in one zero_bucket_flatten_batch call and in one
+    zero_bucket_flatten call per bucket.  Prints one JSON line."""
     import torch
 
     import sharded_mixed_precision_step_amd as zs
@@ -402,10 +403,16 @@ def bench_zero2(args, dev):
         lmax = max(lmax, offs[-1])
     buckets = [torch.empty(L, dtype=torch.float16, device=dev) for L in lengths]
 
-    def flatten_all():
+    def flatten_each():
         for ts, bk in zip(grads, buckets):
             zs.zero_bucket_flatten(ts, bk, align, pad, stream=stream)
 
+    batch = zs.FlattenBatch(list(zip(grads, buckets)), align, pad)
+
+    def flatten_all():
+        batch(stream=stream)
+
+    flat_each_ms = _timed(flatten_each, args.steps)
     flat_ms = _timed(flatten_all, args.steps)
     flat_bytes = sum(2 * sum(t.numel() for t in ts) + 2 * L for ts, L in zip(grads, lengths))
     del grads, buckets, scratch
@@ -482,7 +489,7 @@ def bench_zero2(args, dev):
         assert zs.control_read(c).error == 0
     step_bytes = w.bytes_per_param_step() * w.n
     log("bench: " + ", ".join(f"{k} {v:.3f} ms" for k, v in ms.items()) +
-        f", flatten {flat_ms:.3f} ms")
+        f", flatten {flat_ms:.3f} ms (one batch call), {flat_each_ms:.3f} ms (a call per bucket)")
     out_line = {
         "metric": METRIC,
         "value": w.n / (ms["device_step"] * 1e-3),
@@ -504,6 +511,8 @@ def bench_zero2(args, dev):
             **{f"{k}_gbps": step_bytes / (v * 1e-3) / 1e9 for k, v in ms.items()},
             "flatten_own_buckets_ms": flat_ms,
             "flatten_own_buckets_gbps": flat_bytes / (flat_ms * 1e-3) / 1e9,
+            "flatten_own_buckets_per_call_ms": flat_each_ms,
+            "flatten_own_buckets_per_call_gbps": flat_bytes / (flat_each_ms * 1e-3) / 1e9,
             "placement": placed,
         },
     }
@@ -519,7 +528,9 @@ def bench_streamed(args, dev):
     arrives (from the current copy into the other), then decide and commit.
     The CPU oracle runs buckets 0, 11 and 22 in full; its rate is quoted as
     such, and the whole-shard time it implies is labelled extrapolated.
-    Prints one JSON line."""
+    Before timing, the lean placement search (place_streamed) re-places the
+    arrays, one group per trial; `--no-placement` skips it.  Prints one
+    JSON line."""
     import torch
 
     import sharded_mixed_precision_step_amd as zs
@@ -533,6 +544,7 @@ def bench_streamed(args, dev):
     t0 = time.perf_counter()
     st = wl.device_state(w, dev)
     cur = (st["master"], st["m"], st["v"], st["p16"])
+    del st
     nxt = tuple(torch.empty_like(t) for t in cur)
     bmax = max(w.buckets)
     bufs = [wl.device_chunks(w, dev, n=bmax, offset_seed=100 + j) for j in range(2)]
@@ -550,6 +562,19 @@ def bench_streamed(args, dev):
         log(f"bench: cpu oracle {cpu['value']:.3e} params/s on {cpu['cores']} threads "
             f"({cpu['seconds']:.1f} s for {cpu['params']} params)")
 
+    placed = "allocation as made (--no-placement)"
+    if not args.no_placement:
+        n_buf = len(bufs[0])
+        arrays = list(cur) + list(nxt) + list(bufs[0]) + list(bufs[1])
+        del cur, nxt, bufs, items       # the search takes the only references
+        arrays, placed = place_streamed(zs, w, arrays, n_buf, stream, args)
+        cur, nxt = tuple(arrays[0:4]), tuple(arrays[4:8])
+        bufs = [arrays[8:8 + n_buf], arrays[8 + n_buf:8 + 2 * n_buf]]
+        del arrays
+        items, off = [], 0
+        for b, nb in enumerate(w.buckets):
+            items.append(([c[:nb] for c in bufs[b % 2]], off))
+            off += nb
     ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step, dev)
     stepper = zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
     events = []
@@ -609,6 +634,7 @@ def bench_streamed(args, dev):
                      "unit": "GB/s", "frac": k1_gbps / HBM_PEAK_GBPS, "traffic": None},
         "cpu_baseline": cpu,
         "extra": {
+            "placement": placed,
             "path": "single pass under the device control block, streamed: "
                     "zero_control_begin, one zero_shard_step_out_ctl per arriving bucket, "
                     "zero_control_decide",
@@ -624,6 +650,58 @@ def bench_streamed(args, dev):
     if args.calibrate_copy:
         calibration_copy(dev)
     print(json.dumps(out), flush=True)
+
+
+def place_streamed(zs, w, arrays, n_buf, stream, args):
+    """The lean placement search for a shard whose two state copies leave no
+    room for a second set: trials alternate between re-placing the copy the
+    first timing step writes together with the two chunk buffers, and the
+    copy it reads (contents copied over).  Each trial is timed as one
+    streamed step in each direction between the copies; the state's copy 0
+    is saved to host memory before the search and written back after."""
+    import torch
+
+    from sharded_mixed_precision_step_amd import placement
+
+    hp = zs.adamw_params(w.hyper)
+
+    def timed(arrs):
+        c0, c1 = tuple(arrs[0:4]), tuple(arrs[4:8])
+        b = (arrs[8:8 + n_buf], arrs[8 + n_buf:8 + 2 * n_buf])
+        its, off = [], 0
+        for k, nb in enumerate(w.buckets):
+            its.append(([c[:nb] for c in b[k % 2]], off))
+            off += nb
+        ctl = zs.control_new(zs.LossScaler.create(scale=w.loss_scale), w.hyper.step,
+                             c0[0].device)
+        st = zs.DeviceStepper(ctl, hp)
+        times = ([], [])
+        for r in range(3):                    # the first round is a warm-up
+            for d in (0, 1):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record(stream)
+                st.single_pass_streamed(iter(its), (c0, c1), stream=stream)
+                e[1].record(stream)
+                if r:
+                    times[d].append(e)
+        torch.cuda.synchronize()
+        assert zs.control_read(ctl).error == 0
+        return sum(sorted(a.elapsed_time(b) for a, b in t)[len(t) // 2] for t in times)
+
+    groups = [(list(range(4, 8 + 2 * n_buf)), False), (list(range(0, 4)), True)]
+    # spacers of up to 1 GiB: a trial of the first group allocates 36 arrays
+    # (and a spacer before each) beside the 137 GB already resident
+    arrays, rep = placement.place_groups(
+        arrays, groups, timed, restore=range(0, 4), trials=args.placement_trials,
+        budget_s=max(60.0, 5.0 * args.placement_trials), max_spacer=1 << 30, stream=stream)
+    log(f"bench: lean placement search {rep.seconds:.1f} s, {rep.trials} trials, kept "
+        f"{rep.kept}: two steps {rep.initial_ms:.3f} -> {rep.final_ms:.3f} ms")
+    placed = {"search": "lean (one group per trial: the written copy with the chunk buffers, "
+                        "then the read copy)",
+              "initial_ms_two_steps": rep.initial_ms, "final_ms_two_steps": rep.final_ms,
+              "gain": rep.gain, "trials": rep.trials, "kept_trials": rep.kept,
+              "seconds": rep.seconds}
+    return arrays, placed
 
 
 def bench_overflow(args, dev):
@@ -1003,6 +1081,7 @@ def tiny_graph(dev, steps: int = 200):
     torch.cuda.synchronize()
     graph_us = (time.perf_counter() - t0) * 1e6 / reps
     assert zs.control_read(ctl).error == 0
+    raw = hip_graph_replays(zs, d, copies, w, fresh)
     # The fused update alone, timed with HIP events: warm (its 32 MB of
     # inputs are in the 256 MB MALL from the step before) and flushed (a
     # 1 GiB fill between steps, outside the events, evicts them).  Warm and
@@ -1031,11 +1110,71 @@ def tiny_graph(dev, steps: int = 200):
            for f, ev in times.items()}
     step_bytes = w.bytes_per_param_step() * w.n
     return {"tiny_eager_us_per_step": eager_us, "tiny_eager_unprepared_us_per_step": unprepared_us,
-            "tiny_graph_us_per_step": graph_us,
+            "tiny_graph_us_per_step": graph_us, **raw,
             "tiny_graph_params_per_s": w.n / (graph_us * 1e-6),
             "tiny_update_warm_us": med[False], "tiny_update_flushed_us": med[True],
             "tiny_update_warm_gbps": step_bytes / (med[False] * 1e-6) / 1e9,
             "tiny_update_flushed_gbps": step_bytes / (med[True] * 1e-6) / 1e9}
+
+
+def hip_graph_replays(zs, d, copies, w, fresh, per_graph=(1, 8)) -> dict:
+    """The tiny workload's device-controlled single pass captured straight
+    through the HIP runtime (hipStreamBeginCapture on a stream of its own,
+    hipGraphInstantiate once, hipGraphLaunch per replay), with K = 1 and 8
+    steps per graph: per-step wall time over back-to-back replays, and the
+    device time of one replay by HIP events on the replay stream.  K steps
+    share one launch, so the per-launch cost of a graph shows as the
+    difference between K = 1 and K = 8."""
+    import ctypes
+
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so.7")    # the runtime torch already holds
+    vp = ctypes.c_void_p
+    for name, args in (("hipStreamBeginCapture", [vp, ctypes.c_int]),
+                       ("hipStreamEndCapture", [vp, ctypes.POINTER(vp)]),
+                       ("hipGraphInstantiate", [ctypes.POINTER(vp), vp, vp, vp, ctypes.c_size_t]),
+                       ("hipGraphLaunch", [vp, vp]), ("hipGraphExecDestroy", [vp]),
+                       ("hipGraphDestroy", [vp])):
+        getattr(hip, name).argtypes = args
+        getattr(hip, name).restype = ctypes.c_int
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} returned HIP error {rc}")
+
+    out = {}
+    stream = torch.cuda.Stream()
+    sp = vp(stream.cuda_stream)
+    for k in per_graph:
+        ctl, st = fresh()
+        torch.cuda.synchronize()
+        ok(hip.hipStreamBeginCapture(sp, 0), "hipStreamBeginCapture")   # global mode
+        for _ in range(k):
+            st.single_pass(d["chunks"], copies, stream=stream)
+        graph, exe = vp(), vp()
+        ok(hip.hipStreamEndCapture(sp, ctypes.byref(graph)), "hipStreamEndCapture")
+        ok(hip.hipGraphInstantiate(ctypes.byref(exe), graph, None, None, 0), "hipGraphInstantiate")
+        reps = (zs.ZERO_CTL_STEPS - 8) // k       # every step's t inside the captured table
+        ok(hip.hipGraphLaunch(exe, sp), "hipGraphLaunch")
+        stream.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        ok(hip.hipGraphLaunch(exe, sp), "hipGraphLaunch")
+        ev[1].record(stream)
+        stream.synchronize()
+        one_ms = ev[0].elapsed_time(ev[1])
+        t0 = time.perf_counter()
+        for _ in range(reps - 2):
+            ok(hip.hipGraphLaunch(exe, sp), "hipGraphLaunch")
+        stream.synchronize()
+        wall_us = (time.perf_counter() - t0) * 1e6 / ((reps - 2) * k)
+        c = zs.control_read(ctl)
+        assert c.error == 0 and c.step == w.hyper.step + reps * k, (c.error, c.step)
+        ok(hip.hipGraphExecDestroy(exe), "hipGraphExecDestroy")
+        ok(hip.hipGraphDestroy(graph), "hipGraphDestroy")
+        out[f"tiny_hip_graph_{k}_steps_us_per_step"] = wall_us
+        out[f"tiny_hip_graph_{k}_steps_replay_device_us"] = one_ms * 1e3
+    return out
 
 
 def two_pass(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
@@ -1108,7 +1247,8 @@ def page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
     """The page-literal split on the same state, for comparison: the owner's
     gradient mean stored as fp16, then the single-pass update from it as a
     one-chunk step (flag, read-back, loss scale, commit).  Also the fp16 mean
-    built arrival by arrival (one zero_accumulate_chunk per replica chunk)."""
+    built arrival by arrival (one zero_accumulate_chunk per replica chunk),
+    and in groups of 2 and 4 arrivals (one zero_accumulate_chunks each)."""
     import torch
     n, N = w.n, w.n_replicas
     mean16 = torch.empty(n, dtype=torch.float16, device=d["master"].device)
@@ -1158,6 +1298,28 @@ def page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
     mid_ms = (sum(e[1].elapsed_time(e[N - 1]) for e in ev_acc) / len(ev_acc) / (N - 2)
               if N > 2 else None)
     acc_bytes = (6 + 10 * (N - 2) + 8) * n if N > 1 else 4 * n
+    # the same fold with the chunks arriving in groups (one
+    # zero_accumulate_chunks call per group): pairs and quads
+    groups = {}
+    for g in (2, 4):
+        if N % g or N == g:
+            continue
+        ev_g = []
+        for k in range(steps + 1):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            for first in range(0, N, g):
+                zs.zero_accumulate_chunks(d["chunks"][first:first + g], first, N, acc,
+                                          mean16 if first + g == N else None, stream=stream)
+            e[1].record(stream)
+            if k >= 1:
+                ev_g.append(e)
+        torch.cuda.synchronize()
+        g_ms = sum(a.elapsed_time(b) for a, b in ev_g) / len(ev_g)
+        calls = N // g
+        g_bytes = (2 * N + 4 * (calls - 1) + 4 * (calls - 1) + 2) * n
+        groups[f"accumulate_groups_of_{g}_ms"] = g_ms
+        groups[f"accumulate_groups_of_{g}_gbps"] = g_bytes / (g_ms * 1e-3) / 1e9
     del mean16, acc
     out = {"split_ms_per_step": ms, "split_params_per_s": n / (ms * 1e-3),
            "mean_fp16_ms": mean_ms, "mean_fp16_gbps": (2 * N + 2) * n / (mean_ms * 1e-3) / 1e9,
@@ -1167,6 +1329,7 @@ def page_literal(zs, d, shard, w, scaler, hp, flag, sq, stream, steps: int):
     if mid_ms is not None:
         out["accumulate_middle_ms"] = mid_ms
         out["accumulate_middle_gbps"] = 10 * n / (mid_ms * 1e-3) / 1e9
+    out.update(groups)
     return out
 
 

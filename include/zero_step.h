@@ -342,6 +342,37 @@ int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n
                           float* acc, void* mean_fp16, void* stream);
 
 /*
+ * zero_accumulate_chunks -- fold several replicas' chunks that arrive
+ * together into their owner's accumulator, in one pass.
+ *
+ * When the chunks of replicas first .. first + k - 1 (of n_chunks = N) reach
+ * the owner at once (ZeRO notes, section "Deepspeed ZeRO-2", step 同步: each
+ * bucket goes to its owner as soon as it is complete), one call folds them
+ * all, with the result zero_accumulate_chunk gives when called for each of
+ * them in replica order, bit for bit.  Elementwise over j < n, with x_c the
+ * c-th of the k chunks:
+ *   s = x_0 (first == 0), or acc[j] + x_0 (first > 0); then s = s + x_c for
+ *   c = 1 .. k - 1, every addition one fp32 operation in that order;
+ *   first + k < N:    acc[j] = s
+ *   first + k == N:   mean_fp16[j] = fp16(s / N), rounded to nearest even
+ * Calls covering replicas 0 .. N-1 in order, in groups of any sizes, yield
+ * the mean_fp16 of zero_reduce_mean_fp16 over the same chunks.
+ *
+ *   chunks      HOST array of k DEVICE pointers, each to n fp16 values,
+ *               16-byte aligned
+ *   k           1 .. n_chunks - first
+ *   first       0 .. n_chunks - 1: the replica index of chunks[0]
+ *   acc         DEVICE fp32[n], 16-byte aligned; read if first > 0, written
+ *               if first + k < N, otherwise unused (may be NULL)
+ *   mean_fp16   DEVICE fp16[n], 16-byte aligned; written if first + k == N,
+ *               otherwise unused (may be NULL)
+ * Written arrays must not overlap a chunk or each other.  Returns ZERO_OK,
+ * ZERO_EINVAL, ZERO_EALIGN or ZERO_EHIP.
+ */
+int zero_accumulate_chunks(const void* const* chunks, int32_t k, int64_t n, int32_t first,
+                           int32_t n_chunks, float* acc, void* mean_fp16, void* stream);
+
+/*
  * zero_accumulate_chunk_noalloc -- zero_accumulate_chunk with the library's
  * own accumulator, for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation.

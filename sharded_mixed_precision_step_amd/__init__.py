@@ -32,7 +32,8 @@ ZERO_MAX_CHUNKS = 64
 
 EXPORTED = ("zero_overflow_check", "zero_shard_step", "zero_shard_step_out",
             "zero_shard_step_buckets", "zero_reduce_mean_fp16", "zero_accumulate_chunk",
-            "zero_accumulate_chunk_noalloc", "zero_bucket_flatten", "zero_bucket_flatten_batch",
+            "zero_accumulate_chunks", "zero_accumulate_chunk_noalloc", "zero_bucket_flatten",
+            "zero_bucket_flatten_batch",
             "zero_update_loss_scale",
             "zero_control_init",
             "zero_control_begin", "zero_overflow_check_ctl", "zero_control_decide",
@@ -127,6 +128,7 @@ def _load() -> ctypes.CDLL:
     lib.zero_reduce_mean_fp16.argtypes = [pp, i32, i64, ctypes.c_float, vp, vp, vp, vp]
     lib.zero_accumulate_chunk.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     lib.zero_accumulate_chunk_noalloc.argtypes = [vp, i64, i32, i32, vp, vp]
+    lib.zero_accumulate_chunks.argtypes = [pp, i32, i64, i32, i32, vp, vp, vp]
     lib.zero_bucket_flatten.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), i32, i64, i64,
                                         vp, i64, ctypes.POINTER(ctypes.c_int64), vp]
     lib.zero_bucket_flatten_batch.argtypes = [ctypes.POINTER(FlattenBucketC), i32, i64, i64, vp]
@@ -349,6 +351,27 @@ def zero_accumulate_chunk(chunk: torch.Tensor, index: int, n_chunks: int,
                                      int(n_chunks), _opt(acc, torch.float32, "acc"),
                                      _opt(mean_fp16, torch.float16, "mean_fp16"),
                                      _stream(stream)))
+
+
+def zero_accumulate_chunks(chunks: Sequence[torch.Tensor], first: int, n_chunks: int,
+                           acc: Optional[torch.Tensor], mean_fp16: Optional[torch.Tensor],
+                           stream=None) -> None:
+    """Fold replicas first .. first + len(chunks) - 1 of n_chunks into the
+    fp32 accumulator in one pass; the group holding the last replica writes
+    the fp16 mean (see zero_step.h)."""
+    n = chunks[0].numel() if chunks else 0
+    ptrs = []
+    for i, c in enumerate(chunks):
+        if c.numel() != n:
+            raise ValueError(f"chunks[{i}] has {c.numel()} elements, expected {n}")
+        ptrs.append(_dev(c, torch.float16, f"chunks[{i}]"))
+    for name, t in (("acc", acc), ("mean_fp16", mean_fp16)):
+        if t is not None and t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    _check(lib.zero_accumulate_chunks(_ptr_array(ptrs), len(ptrs), n, int(first), int(n_chunks),
+                                      _opt(acc, torch.float32, "acc"),
+                                      _opt(mean_fp16, torch.float16, "mean_fp16"),
+                                      _stream(stream)))
 
 
 def zero_accumulate_chunk_noalloc(chunk: torch.Tensor, index: int, n_chunks: int,

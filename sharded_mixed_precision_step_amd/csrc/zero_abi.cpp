@@ -646,6 +646,59 @@ int zero_accumulate_chunk(const void* chunk, int64_t n, int32_t index, int32_t n
     return e == hipSuccess ? ok() : hip_fail(e, who);
 }
 
+int zero_accumulate_chunks(const void* const* chunks, int32_t k, int64_t n, int32_t first,
+                           int32_t n_chunks, float* acc, void* mean_fp16, void* stream) {
+    static const char* who = "zero_accumulate_chunks";
+    if (n_chunks < 1 || n_chunks > ZERO_MAX_CHUNKS)
+        return fail(ZERO_EINVAL, "%s: n_chunks = %d outside [1, %d]", who, n_chunks,
+                    ZERO_MAX_CHUNKS);
+    if (first < 0 || first >= n_chunks)
+        return fail(ZERO_EINVAL, "%s: first = %d outside [0, %d)", who, first, n_chunks);
+    if (k < 1 || k > n_chunks - first)
+        return fail(ZERO_EINVAL, "%s: k = %d outside [1, %d]", who, k, n_chunks - first);
+    if (n < 0) return fail(ZERO_EINVAL, "%s: n < 0", who);
+    const bool read_acc = first > 0, last = first + k == n_chunks;
+    const bool uses_acc = read_acc || !last;
+    if (n == 0) return ok();
+    int rc = check_step_length(n, who);
+    if (rc) return rc;
+    if (!chunks) return fail(ZERO_EINVAL, "%s: chunks is NULL", who);
+    zero::ChunkTable table;
+    memset(&table, 0, sizeof table);
+    for (int32_t c = 0; c < k; ++c) {
+        if (!chunks[c]) return fail(ZERO_EINVAL, "%s: chunks[%d] is NULL", who, c);
+        if (!aligned(chunks[c], 16))
+            return fail(ZERO_EALIGN, "%s: chunks[%d] is not 16-byte aligned", who, c);
+        table.p[c] = static_cast<const uint16_t*>(chunks[c]);
+    }
+    if (uses_acc) {
+        if (!acc) return fail(ZERO_EINVAL, "%s: acc is NULL", who);
+        if (!aligned(acc, 16)) return fail(ZERO_EALIGN, "%s: acc is not 16-byte aligned", who);
+        for (int32_t c = 0; c < k; ++c)
+            if (overlap(acc, 4 * n, chunks[c], 2 * n))
+                return fail(ZERO_EINVAL, "%s: acc overlaps chunks[%d]", who, c);
+    }
+    if (last) {
+        if (!mean_fp16) return fail(ZERO_EINVAL, "%s: mean_fp16 is NULL", who);
+        if (!aligned(mean_fp16, 16))
+            return fail(ZERO_EALIGN, "%s: mean_fp16 is not 16-byte aligned", who);
+        for (int32_t c = 0; c < k; ++c)
+            if (overlap(mean_fp16, 2 * n, chunks[c], 2 * n))
+                return fail(ZERO_EINVAL, "%s: mean_fp16 overlaps chunks[%d]", who, c);
+        if (uses_acc && overlap(mean_fp16, 2 * n, acc, 4 * n))
+            return fail(ZERO_EINVAL, "%s: mean_fp16 overlaps acc", who);
+    }
+    zero::ChunkTable unused;
+    zero::GradScalars gs;
+    const void* none[1] = {nullptr};
+    if ((rc = check_chunks(none, n_chunks, 0, 1.0f, &unused, &gs))) return rc;  // the 1/N scalars
+    const hipError_t e = zero::launch_fold_group(table, k, n, read_acc, last, gs,
+                                                 uses_acc ? acc : nullptr,
+                                                 static_cast<uint16_t*>(mean_fp16),
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+
 int zero_accumulate_chunk_noalloc(const void* chunk, int64_t n, int32_t index, int32_t n_chunks,
                                   void* mean_fp16, void* stream) {
     static const char* who = "zero_accumulate_chunk_noalloc";

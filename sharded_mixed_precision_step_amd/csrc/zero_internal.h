@@ -190,6 +190,13 @@ hipError_t fold_scratch(float** ptr);
 hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const GradScalars& gs,
                              float* acc, uint16_t* mean16, hipStream_t stream);
 
+// k chunks (replicas first .. first + k - 1 of N) folded in one pass: from
+// acc when read_acc, else from the first chunk; into acc, or into the fp16
+// mean when last.
+hipError_t launch_fold_group(const ChunkTable& chunks, int k, int64_t n, bool read_acc,
+                             bool last, const GradScalars& gs, float* acc, uint16_t* mean16,
+                             hipStream_t stream);
+
 hipError_t launch_bucket_flatten(const FlattenTable& table, hipStream_t stream);
 
 }  // namespace zero

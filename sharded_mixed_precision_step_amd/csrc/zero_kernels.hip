@@ -12,6 +12,7 @@
 //   control_decide_kernel  scale, clip factor, t, commit).
 //   reduce_mean_kernel     the replica mean stored as fp16 (page-literal split).
 //   accumulate_kernel      one arriving chunk folded into the fp16 mean.
+//   fold_group_kernel      several chunks arriving together, folded in one pass.
 //   bucket_flatten_kernel  whole tensors into 256-aligned, zero-padded slots, of
 //                          one bucket or of many in one launch.
 //
@@ -689,6 +690,74 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const uint16_t* __re
     }
 }
 
+// Several replicas' chunks arriving together, folded in one pass:
+// s = x_0 (or acc + x_0 when earlier arrivals are in the accumulator), then
+// s = s + x_c for c = 1 .. k - 1, each one fp32 addition in arrival order, so
+// the bits are those of k single-arrival folds; then acc = s, or, for the
+// group holding the last replica, mean16 = fp16(s / N).  One-shot tiles as
+// the single-arrival fold, every load of a lane issued before its adds.
+template <int NC, bool READ_ACC, bool LAST>
+__global__ __launch_bounds__(kBlock) void fold_group_kernel(ChunkTable chunks, int k, int64_t n,
+                                                            GradScalars gs, float* acc,
+                                                            uint16_t* __restrict__ mean16) {
+    const int nc = NC > 0 ? NC : k;
+    const int64_t packs = n / kPack;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kTilePacks +
+                          wave * (kWaveSpan * 64) + lane;
+    f8 s[kWaveSpan];
+#pragma unroll
+    for (int u = 0; u < kWaveSpan; ++u) {
+        const int64_t i = first + u * 64;
+        if (i >= packs) continue;
+        if constexpr (READ_ACC) {
+            const f4 a0 = reinterpret_cast<const f4*>(acc)[2 * i];
+            const f4 a1 = reinterpret_cast<const f4*>(acc)[2 * i + 1];
+            s[u] = f8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            if constexpr (NC > 0) {
+#pragma unroll
+                for (int c = 0; c < NC; ++c) s[u] += load_widen8(chunks.p[c], i);
+            } else {
+                for (int c = 0; c < nc; ++c) s[u] += load_widen8(chunks.p[c], i);
+            }
+        } else {
+            s[u] = replica_sum8<NC>(chunks.p, nc, i);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kWaveSpan; ++u) {
+        const int64_t i = first + u * 64;
+        if (i >= packs) continue;
+        if constexpr (LAST) {
+            u16x8 out;
+#pragma unroll
+            for (int e = 0; e < kPack; ++e)
+                out[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(mean_of(s[u][e], gs)));
+            __builtin_nontemporal_store(out, reinterpret_cast<u16x8*>(mean16 + i * kPack));
+        } else {
+            reinterpret_cast<f4*>(acc)[2 * i] = f4{s[u][0], s[u][1], s[u][2], s[u][3]};
+            reinterpret_cast<f4*>(acc)[2 * i + 1] = f4{s[u][4], s[u][5], s[u][6], s[u][7]};
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        const int64_t j = packs * kPack + threadIdx.x;
+        if (j < n) {
+            float sj;
+            if constexpr (READ_ACC) {
+                sj = acc[j];
+                for (int c = 0; c < nc; ++c) sj += load_widen1(chunks.p[c], j);
+            } else {
+                sj = replica_sum1<NC>(chunks.p, nc, j);
+            }
+            if constexpr (LAST)
+                mean16[j] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(mean_of(sj, gs)));
+            else
+                acc[j] = sj;
+        }
+    }
+}
+
 // Tensors into their bucket slots: the tensor's elements, then zeros up to
 // the next slot.  Slots (of one bucket or of several) are disjoint, so blocks
 // never write the same element.  The launch is one-dimensional over the
@@ -978,6 +1047,44 @@ hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const G
             break;
     }
     return hipGetLastError();
+}
+
+namespace {
+template <int NC>
+hipError_t fold_group_impl(const ChunkTable& chunks, int k, int64_t n, bool read_acc, bool last,
+                           const GradScalars& gs, float* acc, uint16_t* mean16,
+                           hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(step_tiles(n))), block(kBlock);
+    const unsigned lds = NC > 0 ? kFoldLdsReserve : 0u;
+    if (read_acc && last)
+        hipLaunchKernelGGL((fold_group_kernel<NC, true, true>), grid, block, lds, stream, chunks,
+                           k, n, gs, acc, mean16);
+    else if (read_acc)
+        hipLaunchKernelGGL((fold_group_kernel<NC, true, false>), grid, block, lds, stream,
+                           chunks, k, n, gs, acc, mean16);
+    else if (last)
+        hipLaunchKernelGGL((fold_group_kernel<NC, false, true>), grid, block, lds, stream,
+                           chunks, k, n, gs, acc, mean16);
+    else
+        hipLaunchKernelGGL((fold_group_kernel<NC, false, false>), grid, block, lds, stream,
+                           chunks, k, n, gs, acc, mean16);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fold_group(const ChunkTable& chunks, int k, int64_t n, bool read_acc,
+                             bool last, const GradScalars& gs, float* acc, uint16_t* mean16,
+                             hipStream_t stream) {
+#define ZERO_CASE(K) \
+    case K:          \
+        return fold_group_impl<K>(chunks, k, n, read_acc, last, gs, acc, mean16, stream);
+    switch (k) {
+        ZERO_CASE(1) ZERO_CASE(2) ZERO_CASE(3) ZERO_CASE(4) ZERO_CASE(5) ZERO_CASE(6)
+        ZERO_CASE(7) ZERO_CASE(8)
+        default:
+            return fold_group_impl<0>(chunks, k, n, read_acc, last, gs, acc, mean16, stream);
+    }
+#undef ZERO_CASE
 }
 
 hipError_t launch_ctl_step(const ChunkTable& chunks, int n_chunks, int64_t n,

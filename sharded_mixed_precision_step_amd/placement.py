@@ -31,6 +31,12 @@ last timing step's output, which the first real step overwrites.
 Allocation goes through torch's caching allocator; the search empties its
 cache after every trial, so that the next trial gets fresh memory and a
 rejected set's memory goes back to the driver.
+
+A whole new set needs room for two more sets beside the caller's.  Where
+that does not fit (the 70B-class shard's two state copies alone take 124 GB),
+`place_groups` re-places one group of arrays per trial instead (for example
+the copy a step writes together with the gradient buffers, then the copy it
+reads), keeping the others where they are.
 """
 from __future__ import annotations
 
@@ -105,6 +111,68 @@ def _search(best_set: list, timed: Callable[[list], float],
         del new
         release()
     return best_set, initial, best, done, kept
+
+
+def place_groups(arrays: Sequence[torch.Tensor], groups, timed: Callable[[list], float], *,
+                 restore: Sequence[int] = (), trials: int = 12, budget_s: float = 30.0,
+                 min_gain: float = 0.005, max_spacer: int = 4 << 30, seed: int = 0,
+                 stream=None):
+    """A leaner search: each trial re-places one group of the arrays, not the
+    whole set, so it needs room for one group more rather than two sets more.
+
+    arrays: a list of the long-lived device arrays, which the search takes
+    over: it empties the list, so that the caller holds no reference that
+    would keep a replaced array's memory alive; groups: a sequence of (indices,
+    keep_contents), trial k re-placing group k mod len(groups) (each new
+    array behind a spacer allocation of random size, its contents copied over
+    when keep_contents is true); timed(arrays): the time to minimise, in ms,
+    for the arrays as given.  The timing may overwrite arrays: those listed
+    in `restore` are saved to host memory first and written back into the
+    arrays kept at the end, so they come back bit for bit.  A trial is kept
+    when it beats the best time by more than `min_gain` (relative).  Returns
+    (arrays, report); the caller must use the returned arrays and drop its
+    references to the ones it passed in."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rng = random.Random(seed)
+    work = list(arrays)
+    arrays.clear()
+    dev = work[0].device
+    t_start = time.perf_counter()
+    turn = [0]
+
+    def make_set(cur):
+        idx, keep = groups[turn[0] % len(groups)]
+        turn[0] += 1
+        new = list(cur)
+        spacers = []
+        try:
+            for i in idx:
+                spacers.append(torch.empty(1 + rng.randrange(max_spacer), dtype=torch.uint8,
+                                           device=dev))
+                new[i] = torch.empty_like(cur[i])
+        except torch.OutOfMemoryError:
+            return None
+        del spacers
+        if keep:
+            for i in idx:
+                new[i].copy_(cur[i])
+        return new
+
+    with torch.cuda.stream(stream):
+        saved = {i: work[i].cpu() for i in restore}
+        best_set, initial, best, done, kept = _search(
+            work, timed, make_set, torch.cuda.empty_cache, trials=trials,
+            budget_s=budget_s, min_gain=min_gain)
+        del work
+        for i, host in saved.items():
+            best_set[i].copy_(host)
+        del saved
+        stream.synchronize()
+        torch.cuda.empty_cache()
+    report = PlacementReport(initial_ms=initial, final_ms=best, trials=done, kept=kept,
+                             seconds=time.perf_counter() - t_start)
+    return best_set, report
 
 
 def place_shard(chunks: Sequence[torch.Tensor], copies, hp, loss_scale: float, *,

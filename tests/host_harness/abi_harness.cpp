@@ -145,6 +145,20 @@ hipError_t launch_accumulate(const uint16_t*, int64_t, int mode, const GradScala
     return hipSuccess;
 }
 
+struct FoldGroupLaunch {
+    int k;
+    bool read_acc, last;
+    float* acc;
+    uint16_t* mean;
+};
+std::vector<FoldGroupLaunch> g_fold_group;
+
+hipError_t launch_fold_group(const ChunkTable&, int k, int64_t, bool read_acc, bool last,
+                             const GradScalars&, float* acc, uint16_t* mean16, hipStream_t) {
+    g_fold_group.push_back({k, read_acc, last, acc, mean16});
+    return hipSuccess;
+}
+
 // the library's own accumulator, at a fake device address
 hipError_t fold_scratch(float** ptr) {
     ++g_scratch_lookups;
@@ -437,6 +451,41 @@ static void accumulate_noalloc() {
     EXPECT(zero::g_accumulate_acc[4] == nullptr && zero::g_scratch_lookups == 4);
 }
 
+// Groups of arrivals: which of acc and the mean each group reads and writes,
+// and what it may leave NULL.
+static void accumulate_groups() {
+    zero::g_fold_group.clear();
+    const void* ch[4] = {fake(kBase), fake(kBase + (1 << 20)), fake(kBase + (2 << 20)),
+                         fake(kBase + (3 << 20))};
+    float* acc = (float*)fake(0x400000000000ull);
+    void* mean = fake(0x410000000000ull);
+    // N = 7 in groups of 3, 1, 3: first writes acc, middle reads and writes,
+    // last reads acc and writes the mean
+    EXPECT(zero_accumulate_chunks(ch, 3, 1000, 0, 7, acc, nullptr, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunks(ch, 1, 1000, 3, 7, acc, nullptr, nullptr) == ZERO_OK);
+    EXPECT(zero_accumulate_chunks(ch, 3, 1000, 4, 7, acc, mean, nullptr) == ZERO_OK);
+    // all four at once: no accumulator at all
+    EXPECT(zero_accumulate_chunks(ch, 4, 1000, 0, 4, nullptr, mean, nullptr) == ZERO_OK);
+    EXPECT(zero::g_fold_group.size() == 4);
+    const zero::FoldGroupLaunch* f = zero::g_fold_group.data();
+    EXPECT(f[0].k == 3 && !f[0].read_acc && !f[0].last && f[0].acc == acc);
+    EXPECT(f[1].k == 1 && f[1].read_acc && !f[1].last);
+    EXPECT(f[2].k == 3 && f[2].read_acc && f[2].last && f[2].mean == mean);
+    EXPECT(f[3].k == 4 && !f[3].read_acc && f[3].last && f[3].acc == nullptr);
+    // refused before any launch
+    EXPECT(zero_accumulate_chunks(ch, 4, 1000, 4, 7, acc, mean, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_accumulate_chunks(ch, 0, 1000, 0, 7, acc, mean, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_accumulate_chunks(ch, 1, 1000, 7, 7, acc, mean, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_accumulate_chunks(ch, 3, 1000, 0, 7, nullptr, nullptr, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_accumulate_chunks(ch, 3, 1000, 4, 7, acc, nullptr, nullptr) == ZERO_EINVAL);
+    EXPECT(zero_accumulate_chunks(ch, 3, 1000, 0, 7, (float*)fake(kBase + 64), nullptr,
+                                  nullptr) == ZERO_EINVAL);            // acc over a chunk
+    const void* bad[2] = {fake(kBase), fake(kBase + 8)};
+    EXPECT(zero_accumulate_chunks(bad, 2, 1000, 0, 7, acc, nullptr, nullptr) == ZERO_EALIGN);
+    EXPECT(zero_accumulate_chunks(nullptr, 2, 0, 0, 7, nullptr, nullptr, nullptr) == ZERO_OK);
+    EXPECT(zero::g_fold_group.size() == 4);
+}
+
 // Which accumulate mode each (index, N) selects, and what it may leave NULL.
 static void accumulate_modes() {
     reset();
@@ -626,6 +675,7 @@ int main(int argc, char** argv) {
     flatten_batch();
     bias_tables();
     accumulate_modes();
+    accumulate_groups();
     accumulate_noalloc();
     scaler_and_control();
     empty_and_errors();

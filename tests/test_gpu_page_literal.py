@@ -1,5 +1,6 @@
 """The page-literal split against the CPU oracle: the owner's gradient mean
-stored as fp16 (all chunks at once, or one arriving chunk at a time), then
+stored as fp16 (all chunks at once, one arriving chunk at a time, or groups
+of chunks arriving together), then
 the update from it as a one-chunk step, element by element and bit for bit;
 also the whole split enqueued under the device control block."""
 import numpy as np
@@ -84,6 +85,40 @@ def test_accumulate_chunks_in_arrival_order(n, N):
     want = ozs.accumulate_chunks(ch)
     assert np.array_equal(mean.cpu().numpy().view(np.uint16), want.view(np.uint16))
     assert torch.equal(mean.view(torch.int16), once.view(torch.int16))
+
+
+@pytest.mark.parametrize("N,groups", [(1, [1]), (2, [2]), (8, [2, 2, 2, 2]), (8, [3, 1, 4]),
+                                      (8, [8]), (8, [7, 1]), (17, [5, 9, 3]),
+                                      (64, [16, 16, 16, 16]), (64, [1, 62, 1])])
+@pytest.mark.parametrize("n", [7, 4096, 20_011])
+def test_fold_groups_equal_single_arrivals(n, N, groups):
+    """Chunks folded in groups (zero_accumulate_chunks, one call per group of
+    arrivals) leave the same accumulator after every group, bit for bit, as
+    one zero_accumulate_chunk call per arrival, and the same fp16 mean, the
+    oracle's."""
+    dev = device()
+    assert sum(groups) == N
+    ch = _chunks(n, N, seed=3 * n + N + len(groups))
+    d = _dev(ch, dev)
+    print(f"case: fold groups n={n} N={N} groups={groups}", flush=True)
+    acc_g = torch.full((n,), float("nan"), dtype=torch.float32, device=dev)
+    acc_s = torch.full((n,), float("nan"), dtype=torch.float32, device=dev)
+    mean_g = torch.empty(n, dtype=torch.float16, device=dev)
+    mean_s = torch.empty(n, dtype=torch.float16, device=dev)
+    first = 0
+    for k in groups:
+        last = first + k == N
+        zs.zero_accumulate_chunks(d[first:first + k], first, N, acc_g, mean_g if last else None)
+        for i in range(first, first + k):
+            zs.zero_accumulate_chunk(d[i], i, N, acc_s, mean_s if i == N - 1 else None)
+        first += k
+        if not last:
+            torch.cuda.synchronize()
+            assert torch.equal(acc_g.view(torch.int32), acc_s.view(torch.int32)), first
+    torch.cuda.synchronize()
+    want = ozs.accumulate_chunks(ch)
+    assert np.array_equal(mean_g.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    assert torch.equal(mean_g.view(torch.int16), mean_s.view(torch.int16))
 
 
 @pytest.mark.parametrize("N,S", [(8, 65536.0), (3, 1024.0), (5, 1000.0)])

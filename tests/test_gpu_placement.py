@@ -77,3 +77,35 @@ def test_contents_survive_and_step_matches(n, N, trials):
                           w.loss_scale)
     assert_matches_oracle(dict(zip(KEYS, copies[1])), want)
     assert abs(float(sq.item()) - want.sqnorm) <= 1e-6 * max(want.sqnorm, 1e-300)
+
+
+def test_lean_search_by_groups_keeps_and_restores_contents():
+    """place_groups re-places one group per trial: a group whose contents are
+    kept comes back bit for bit, arrays listed for restoring come back as
+    they were even though the timing overwrites them, the input list is taken
+    over (emptied), and the kept trials follow the times the stand-in timing
+    reports (its own count of calls, so the fastest trial is known)."""
+    dev = device()
+    print("case: lean placement by groups", flush=True)
+    src = [torch.randn(10_001, device=dev) for _ in range(6)]
+    want = [_bits(t) for t in src]
+    arrays = [t.clone() for t in src]
+    calls = [0]
+    times = [10.0, 9.0, 9.5, 7.0, 8.0, 6.0, 6.5]     # initial, then trials 1..6
+
+    def timed(arrs):
+        arrs[0].add_(1.0)                              # the timing overwrites array 0
+        t = times[calls[0]]
+        calls[0] += 1
+        return t
+
+    groups = [([0, 1], True), ([2, 3, 4], True), ([5], False)]
+    got, rep = placement.place_groups(arrays, groups, timed, restore=[0], trials=6,
+                                      max_spacer=1 << 20, budget_s=60.0)
+    torch.cuda.synchronize()
+    assert arrays == [] and len(got) == 6
+    assert rep.trials == 6 and rep.kept == [1, 3, 5]
+    assert rep.initial_ms == 10.0 and rep.final_ms == 6.0
+    for i in range(5):                                 # kept contents, and array 0 restored
+        assert torch.equal(_bits(got[i]), want[i]), i
+    assert got[5].shape == src[5].shape and got[5].dtype == src[5].dtype
