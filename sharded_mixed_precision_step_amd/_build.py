@@ -1,5 +1,6 @@
-"""Build of libzerostep.so (the gfx950 kernels and the C-ABI host layer) and
-of libzerotwin.so (the benchmark's measurement aids, zero_twin.h).
+"""Build of libzerostep.so (the gfx950 kernels and the C-ABI host layer), of
+libzerotwin.so (the benchmark's measurement aids, zero_twin.h) and of
+workloads/libzerogen.so (the device side of the seeded input generators).
 
 hipcc cross-compiles for gfx950 on any host, so this runs without a GPU.
 """
@@ -18,6 +19,11 @@ LIB = os.path.join(HERE, "libzerostep.so")
 SOURCES = [os.path.join(CSRC, "zero_kernels.hip"), os.path.join(CSRC, "zero_abi.cpp")]
 TWIN_LIB = os.path.join(HERE, "libzerotwin.so")
 TWIN_SOURCES = [os.path.join(CSRC, "zero_twin.hip")]
+# the device side of the seeded input generators (workloads/), test and
+# benchmark infrastructure
+GEN_DIR = os.path.join(ROOT, "workloads", "csrc")
+GEN_LIB = os.path.join(ROOT, "workloads", "libzerogen.so")
+GEN_SOURCES = [os.path.join(GEN_DIR, "zero_gen.hip")]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -84,14 +90,14 @@ def kernel_digest() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile both libraries for gfx950 (two hipcc processes side by side),
+    """Compile the three libraries for gfx950 (hipcc processes side by side),
     each written atomically."""
     jobs = []
-    for lib, sources in ((LIB, SOURCES), (TWIN_LIB, TWIN_SOURCES)):
+    for lib, sources in ((LIB, SOURCES), (TWIN_LIB, TWIN_SOURCES), (GEN_LIB, GEN_SOURCES)):
         name = os.path.basename(lib)
-        fd, tmp = tempfile.mkstemp(prefix=f".{name}.", suffix=".tmp", dir=HERE)
+        fd, tmp = tempfile.mkstemp(prefix=f".{name}.", suffix=".tmp", dir=os.path.dirname(lib))
         os.close(fd)
-        cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, *sources, "-o", tmp]
+        cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, "-I", GEN_DIR, *sources, "-o", tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
@@ -120,6 +126,6 @@ def build(verbose: bool = False) -> str:
 
 def ensure_built() -> str:
     """Build only if a library is missing."""
-    if not (os.path.exists(LIB) and os.path.exists(TWIN_LIB)):
+    if not all(os.path.exists(p) for p in (LIB, TWIN_LIB, GEN_LIB)):
         build()
     return LIB

@@ -1,7 +1,9 @@
 """bench.py's host-side contract: one GPU only, its options, and the rule that
 the counter-derived traffic is reported only while the kernel sources match
 the digest the counters were taken on."""
+import json
 import os
+import re
 import subprocess
 import sys
 
@@ -62,3 +64,34 @@ def test_digest_ignores_comments_but_not_code():
     b = "int x = 1;   /* other words */\nint y = 2; // two"
     c = "int x = 1; int y = 3;"
     assert _build.code_text(a) == _build.code_text(b) != _build.code_text(c)
+
+
+STATS = os.path.join(ROOT, "profiles", "shard_step_kernel_llama3_8b_shard_stats.txt")
+
+
+def _fields(path):
+    text = open(path).read()
+    vals = dict(re.findall(r"^(\w+): (.+)$", text, re.M))
+    line = json.loads(vals.pop("bench_line"))
+    return vals, line
+
+
+def test_committed_profile_agrees_with_its_bench_line():
+    """The kernel-trace summary and the JSON line of the same profiled
+    bench.py run tell the same story: the timed kernel's average over the
+    timed dispatches is within 2 % of the line's HIP-event average, no
+    longer than the line's whole step, and the roofline fraction recomputed
+    from it is the one the summary states and within 0.02 of the line's."""
+    vals, line = _fields(STATS)
+    avg = float(vals["timed_kernel_average_ms"])
+    assert vals["timed_kernel"] == "ctl_step_kernel<8, true>"
+    assert int(vals["timed_dispatches"]) == line["steps"]
+    assert line["config"]["workload"] == "llama3_8b_shard"
+    n, bpp = int(vals["params"]), int(vals["bytes_per_param"])
+    assert n == line["config"]["shard_params"] and bpp == line["config"]["bytes_per_param_fused_step"]
+    fused = line["extra"]["fused_step_ms"]
+    assert abs(avg - fused) <= 0.02 * fused, (avg, fused)
+    assert avg <= line["ms_per_step"], (avg, line["ms_per_step"])
+    frac = bpp * n / (avg * 1e-3) / 1e9 / 8000.0
+    assert abs(frac - float(vals["roofline_frac_from_trace"].split()[0])) < 1e-4
+    assert abs(frac - line["roofline"]["frac"]) <= 0.02

@@ -5,8 +5,8 @@ of the step's arithmetic: it draws random numbers, scales them to the stated
 standard deviation and rounds fp16 arrays to binary16 on creation.  Both sides
 of every parity check take their inputs from here: the CPU oracle gets host
 arrays, the GPU path gets the same bits copied to the device (small cases), or
-the GPU draws its own and the oracle receives host copies of what it drew
-(full-size cases).
+the GPU draws its own with the HIP generator in csrc/zero_gen.hip and the
+oracle receives host copies of what it drew (full-size cases).
 
 Workloads (the rank's shard at its real shape; N replicas of the gradient
 shard stand in for the N ranks whose gradients are reduced onto this owner):
@@ -251,11 +251,13 @@ def exactly_summable_fp16(seed: int, n: int, bound_log2: int = 8) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Device (torch) generators for full-size workloads.  torch is used here only
-# to hold device memory and draw random numbers.
+# Device generators for full-size workloads: HIP kernels of their own
+# (workloads/csrc/zero_gen.hip, built into workloads/libzerogen.so) draw
+# Philox-4x32-10 normals straight into device memory; torch only allocates
+# the tensors and supplies the stream.
 # ---------------------------------------------------------------------------
 
-_PIECE = 1 << 27
+_GEN = None
 
 
 def _torch():
@@ -263,27 +265,60 @@ def _torch():
     return torch
 
 
-def device_generator(seed: int, device):
+def _gen():
+    """libzerogen.so, loaded on first use (after torch, whose HIP runtime it
+    shares)."""
+    global _GEN
+    if _GEN is None:
+        import ctypes
+        import os
+        _torch()
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzerogen.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+        lib.zero_gen_philox.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+        lib.zero_gen_normal.argtypes = [vp, i32, i64, u64, ctypes.c_float, i32, vp]
+        lib.zero_gen_to_fp16.argtypes = [vp, vp, i64, vp]
+        lib.zero_gen_scatter_fp16.argtypes = [vp, i64, vp, vp, i64, vp]
+        for name in ("zero_gen_philox", "zero_gen_normal", "zero_gen_to_fp16",
+                     "zero_gen_scatter_fp16"):
+            getattr(lib, name).restype = ctypes.c_int
+        _GEN = lib
+    return _GEN
+
+
+def _stream() -> int:
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _ok(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def device_philox(ctr_key, device):
+    """The four output words of Philox-4x32-10 for counter ctr_key[0:4] and
+    key ctr_key[4:6], computed on the device (for known-answer tests)."""
+    import ctypes
     torch = _torch()
-    g = torch.Generator(device=device)
-    g.manual_seed(seed)
-    return g
+    out = torch.zeros(4, dtype=torch.int32, device=device)
+    words = (ctypes.c_uint32 * 6)(*[int(x) & 0xFFFFFFFF for x in ctr_key])
+    _ok(_gen().zero_gen_philox(out.data_ptr(), words, _stream()), "zero_gen_philox")
+    return [int(x) & 0xFFFFFFFF for x in out.cpu().tolist()]
 
 
 def device_fill_normal(out, seed: int, sigma: float, absolute: bool = False):
-    """Fill ``out`` (fp32 or fp16 device tensor) with N(0, sigma) draws
-    (their absolute values if ``absolute``), rounded to out's dtype."""
+    """Fill ``out`` (contiguous fp32 or fp16 device tensor) with N(0, sigma)
+    draws of stream ``seed`` (their absolute values if ``absolute``), rounded
+    to out's dtype."""
     torch = _torch()
-    g = device_generator(seed, out.device)
-    n = out.numel()
-    flat = out.view(-1)
-    for off in range(0, n, _PIECE):
-        k = min(_PIECE, n - off)
-        z = torch.randn(k, generator=g, device=out.device, dtype=torch.float32)
-        if absolute:
-            z.abs_()
-        z.mul_(sigma)
-        flat[off:off + k].copy_(z)
+    if not out.is_contiguous() or out.dtype not in (torch.float32, torch.float16):
+        raise TypeError("out must be a contiguous fp32 or fp16 device tensor")
+    _ok(_gen().zero_gen_normal(out.data_ptr(), int(out.dtype == torch.float16), out.numel(),
+                               int(seed), float(sigma), int(bool(absolute)), _stream()),
+        "zero_gen_normal")
     return out
 
 
@@ -300,7 +335,9 @@ def device_state(w: ShardWorkload, device, n: int | None = None, offset_seed: in
         device_fill_normal(m, seed_of(*key, ARRAY_M), w.m_sigma, absolute=True)
     if w.v_sigma:
         device_fill_normal(v, seed_of(*key, ARRAY_V), w.v_sigma, absolute=True)
-    p16 = master.to(torch.float16)
+    p16 = torch.empty(n, dtype=torch.float16, device=device)
+    _ok(_gen().zero_gen_to_fp16(master.data_ptr(), p16.data_ptr(), n, _stream()),
+        "zero_gen_to_fp16")
     return dict(master=master, m=m, v=v, p16=p16)
 
 
@@ -335,6 +372,10 @@ def device_inject(chunks: Sequence, sites) -> None:
         sel = ci == c
         if not sel.any():
             continue
-        idx = torch.from_numpy(ei[sel]).to(chunks[c].device)
-        val = torch.from_numpy(vals[sel]).to(chunks[c].device)
-        chunks[c].index_copy_(0, idx, val)
+        idx = torch.from_numpy(np.ascontiguousarray(ei[sel])).to(chunks[c].device)
+        val = torch.from_numpy(np.ascontiguousarray(vals[sel]).view(np.int16)).to(
+            chunks[c].device)
+        _ok(_gen().zero_gen_scatter_fp16(chunks[c].data_ptr(), chunks[c].numel(),
+                                         idx.data_ptr(), val.data_ptr(), idx.numel(),
+                                         _stream()), "zero_gen_scatter_fp16")
+        torch.cuda.current_stream().synchronize()   # idx and val are freed on return
