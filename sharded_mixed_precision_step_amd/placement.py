@@ -135,9 +135,11 @@ def place_groups(arrays: Sequence[torch.Tensor], groups, timed: Callable[[list],
     if stream is None:
         stream = torch.cuda.current_stream()
     rng = random.Random(seed)
-    work = list(arrays)
+    # the search's list is reachable only through `holder` until _search takes
+    # it: a kept trial then drops the last reference to the group it replaced
+    holder = [list(arrays)]
     arrays.clear()
-    dev = work[0].device
+    dev = holder[0][0].device
     t_start = time.perf_counter()
     turn = [0]
 
@@ -160,11 +162,10 @@ def place_groups(arrays: Sequence[torch.Tensor], groups, timed: Callable[[list],
         return new
 
     with torch.cuda.stream(stream):
-        saved = {i: work[i].cpu() for i in restore}
+        saved = {i: holder[0][i].cpu() for i in restore}
         best_set, initial, best, done, kept = _search(
-            work, timed, make_set, torch.cuda.empty_cache, trials=trials,
+            holder.pop(), timed, make_set, torch.cuda.empty_cache, trials=trials,
             budget_s=budget_s, min_gain=min_gain)
-        del work
         for i, host in saved.items():
             best_set[i].copy_(host)
         del saved

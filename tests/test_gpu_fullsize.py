@@ -5,7 +5,9 @@ seconds on the host's cores, and by properties that hold at any size
 elsewhere.
 
 * Llama-3-8B shard (1,003,750,000 params, N = 8): every element, for the
-  device-controlled single pass and for the two-pass step.
+  device-controlled single pass and for the two-pass step; and the
+  page-literal split (the fp16 mean, its folds one, two and four arrivals at
+  a time, the one-chunk update from it).
 * Overflow (125,468,750 params, 100,375 injected inf/NaN): the step is
   skipped, the scale halves, the state stays bit-identical; then a clean
   step at the halved scale matches the oracle everywhere.
@@ -98,6 +100,62 @@ def test_llama3_8b_shard_full():
     print("case: full llama3_8b_shard, two-pass step vs oracle", flush=True)
     assert int(fl2.item()) == 0 and rel_close(float(sq2.item()), want_sq)
     compare_with_expected(cur, expected, label="two-pass ")
+
+
+def test_llama3_8b_page_literal_full():
+    """The page-literal split at the Llama-3-8B shard: the fp16 mean of the 8
+    replicas against the oracle's at every element (with its flag and norm);
+    the same mean folded arrival by arrival, in pairs and in quads equal to
+    it bit for bit; then the one-chunk update from it against the oracle at
+    every element."""
+    dev = device()
+    w = wl.LLAMA3_8B_SHARD
+    N, n, S = w.n_replicas, w.n, w.loss_scale
+    print(f"case: full {w.name} page-literal split n={n} N={N}", flush=True)
+    d = wl.device_shard(w, dev)
+    mean = torch.empty(n, dtype=torch.float16, device=dev)
+    fl, sq = flags(dev)
+    zs.zero_reduce_mean_fp16(d["chunks"], mean, S, fl, sq)
+    torch.cuda.synchronize()
+    piece = 1 << 24
+
+    def check_mean(k):
+        a, b = k * piece, min(n, (k + 1) * piece)
+        want = ozs.replica_mean_fp16([c[a:b].cpu().numpy() for c in d["chunks"]])
+        got = mean[a:b].cpu().numpy()
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), (a, b)
+        g = ozs.unscale(ozs.widen(want), S)
+        return ozs.nonfinite(g), ozs.grad_sqnorm(g)
+
+    with ThreadPoolExecutor(threads()) as ex:
+        res = list(ex.map(check_mean, range((n + piece - 1) // piece)))
+    assert not any(r[0] for r in res) and int(fl.item()) == 0
+    assert rel_close(float(sq.item()), float(np.sum([r[1] for r in res])))
+    acc = torch.empty(n, dtype=torch.float32, device=dev)
+    for groups in ([1] * N, [2] * (N // 2), [4] * (N // 4)):
+        print(f"case: full page-literal fold in groups {groups}", flush=True)
+        folded = torch.full((n,), float("nan"), dtype=torch.float16, device=dev)
+        first = 0
+        for g in groups:
+            last = first + g == N
+            if g == 1:
+                zs.zero_accumulate_chunk(d["chunks"][first], first, N, acc,
+                                         folded if last else None)
+            else:
+                zs.zero_accumulate_chunks(d["chunks"][first:first + g], first, N, acc,
+                                          folded if last else None)
+            first += g
+        torch.cuda.synchronize()
+        assert torch.equal(folded.view(torch.int16), mean.view(torch.int16)), groups
+        del folded
+    del acc
+    cur = (d["master"], d["m"], d["v"], d["p16"])
+    out = tuple(torch.empty_like(t) for t in cur)
+    zs.zero_shard_step_out([mean], S, *cur[:3], *out, zs.adamw_params(w.hyper))
+    torch.cuda.synchronize()
+    print("case: full page-literal one-chunk step vs oracle", flush=True)
+    overflow, _, _ = compare_with_oracle([mean], cur, out, w.hyper, S, label="split ")
+    assert not overflow
 
 
 def test_overflow_workload_full():
