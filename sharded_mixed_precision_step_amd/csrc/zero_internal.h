@@ -41,15 +41,18 @@ constexpr unsigned step_lds_reserve() { return NC > 0 ? kStepLdsReserve : 0u; }
 // a middle one 6.2-6.6 %.  Two per CU match four on a middle arrival but run
 // the first 20 % and the last 14 % slower than eight.
 constexpr unsigned kFoldLdsReserve = 36 * 1024;
-// The bucket flatten (a copy of each tensor into its slot) likewise runs
-// four blocks per CU; with streaming loads of the source tensors, the
-// ZeRO-2 rank's 160 buckets flatten 5.0-5.2 % faster on MI355X than with
-// plain loads and the registers' own limit (each alone: +2.1 % and +1 %).
-constexpr unsigned kFlattenLdsReserve = 36 * 1024;
+// The bucket flatten (a copy of each tensor into its slot) runs one pack per
+// lane with streaming loads of the source tensors and no cap on blocks per
+// CU.  The ZeRO-2 rank's 160 buckets flattened in batched launches (64 slots
+// each) on MI355X, same arrays, alternating launches: 4.96 ms, against
+// 5.40 ms with four packs per lane at four blocks per CU, 5.04 with two
+// packs at four per CU, and the same 4.96-4.97 ms with one pack at 8, 10 or
+// 16 blocks per CU; plain source loads cost 2 %.
+constexpr unsigned kFlattenLdsReserve = 0;
 constexpr int kMeanSpan = 4;       // packs per lane in an fp16-mean tile
 constexpr int kMeanTilePacks = kBlock * kMeanSpan;  // packs per fp16-mean tile (one block)
 constexpr int kFlattenBatch = 64;  // tensor slots per flatten launch (kernel-argument table)
-constexpr int kFlattenSpan = 4;    // packs per lane in a flatten tile
+constexpr int kFlattenSpan = 1;    // packs per lane in a flatten tile
 constexpr int64_t kFlattenTile = static_cast<int64_t>(kBlock) * kFlattenSpan * kPack;  // elements
 constexpr int64_t kMaxGridBlocks = 0x7fffffff;  // blocks in one launch's x dimension
 constexpr int kMaxBucketsPerLaunch = 32;  // bucket slices per multi-bucket step launch

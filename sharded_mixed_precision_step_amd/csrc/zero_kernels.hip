@@ -766,7 +766,7 @@ __global__ __launch_bounds__(kBlock) void fold_group_kernel(ChunkTable chunks, i
 // arguments), so one launch covers many slots of any lengths with no idle
 // blocks.  Within a tile: wave w the kFlattenSpan * 64 packs from
 // w * kFlattenSpan * 64, lane l the packs l, l + 64, ..., all loads before the
-// stores.
+// stores (with one pack per lane, each wave copies 1 KiB).
 __global__ __launch_bounds__(kBlock) void bucket_flatten_kernel(FlattenTable t) {
     const int64_t b = blockIdx.x;
     int lo = 0, hi = t.count - 1;  // the last slot whose first tile is <= b
