@@ -610,6 +610,8 @@ def bench_streamed(args, dev):
     assert zs.control_read(ctl).error == 0
     k1_bytes = w.bytes_per_param_step() * n
     k1_gbps = k1_bytes / (upd_ms * 1e-3) / 1e9
+    ceilings = copy_ceiling(dev, stream)
+    log("bench: stream ceilings " + ", ".join(f"{k} {v:.0f}" for k, v in ceilings.items()))
     log(f"bench: streamed device single pass {ms_per_step:.3f} ms/step, {len(w.buckets)} "
         f"bucket updates {upd_ms:.3f} ms ({k1_gbps:.0f} GB/s), skipped {c.skipped_steps}; "
         f"over two side streams {ms_2s:.3f} ms/step")
@@ -645,6 +647,8 @@ def bench_streamed(args, dev):
             "bucket_updates_pct_peak": 100 * k1_gbps / HBM_PEAK_GBPS,
             "step_gbps": k1_bytes / (ms_per_step * 1e-3) / 1e9,
             "skipped_steps": c.skipped_steps,
+            **ceilings,
+            "bucket_updates_pct_fma_ceiling": 100 * k1_gbps / ceilings["fma_ceiling_gbps"],
         },
     }
     if args.calibrate_copy:
@@ -656,7 +660,7 @@ def place_streamed(zs, w, arrays, n_buf, stream, args):
     """The lean placement search for a shard whose two state copies leave no
     room for a second set: trials alternate between re-placing the copy the
     first timing step writes together with the two chunk buffers, and the
-    copy it reads (contents copied over).  Each trial is timed as one
+    copy it reads (contents copied over in both).  Each trial is timed as one
     streamed step in each direction between the copies; the state's copy 0
     is saved to host memory before the search and written back after."""
     import torch
@@ -688,7 +692,9 @@ def place_streamed(zs, w, arrays, n_buf, stream, args):
         assert zs.control_read(ctl).error == 0
         return sum(sorted(a.elapsed_time(b) for a, b in t)[len(t) // 2] for t in times)
 
-    groups = [(list(range(4, 8 + 2 * n_buf)), False), (list(range(0, 4)), True)]
+    # the chunk buffers' contents are the seeded gradients and are copied
+    # over; the spare copy's are overwritten before they are read
+    groups = [(list(range(4, 8 + 2 * n_buf)), True), (list(range(0, 4)), True)]
     # spacers of up to 1 GiB: a trial of the first group allocates 36 arrays
     # (and a spacer before each) beside the 137 GB already resident
     arrays, rep = placement.place_groups(
@@ -1342,6 +1348,8 @@ def copy_ceiling(dev, stream, reps: int = 5):
       copy 1:1    torch's elementwise dst = -src
       add 2:1     torch's elementwise c = a + b (two arrays read, one written:
                   the step's mix at N = 8 is 28 bytes read to 14 written)
+      fma 3:1     torch's elementwise c = a + b * d (three read, one written:
+                  the step's mix at N = 16 is 44 bytes read to 14 written)
     Each figure is bytes moved over time."""
     import torch
 
@@ -1349,8 +1357,10 @@ def copy_ceiling(dev, stream, reps: int = 5):
     a = torch.empty(1 << 30, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     c = torch.empty_like(a)
+    d = torch.empty_like(a)
     a.fill_(1.0)
     b.fill_(2.0)
+    d.fill_(0.5)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     nb = a.numel() * 4
 
@@ -1369,8 +1379,9 @@ def copy_ceiling(dev, stream, reps: int = 5):
         "write_ceiling_gbps": timed(lambda: c.fill_(3.0), nb),
         "copy_ceiling_gbps": timed(lambda: torch.neg(a, out=c), 2 * nb),
         "add_ceiling_gbps": timed(lambda: torch.add(a, b, out=c), 3 * nb),
+        "fma_ceiling_gbps": timed(lambda: torch.addcmul(a, b, d, out=c), 4 * nb),
     }
-    del a, b, c
+    del a, b, c, d
     return out
 
 
