@@ -381,8 +381,10 @@ int zero_accumulate_chunks(const void* const* chunks, int32_t k, int64_t n, int3
  * n_chunks, acc, mean_fp16, stream) does, with acc the library's
  * accumulator: a file-scope device array of ZERO_FOLD_SCRATCH_ELEMS fp32
  * values (32 MiB) that each GPU the library runs on holds until the process
- * ends.  The call allocates and frees nothing; the first call on a device
- * looks up that device's copy of the array.  Every call on one GPU shares
+ * ends.  The call allocates and frees nothing.  The array used is the copy on
+ * the device `stream` belongs to (the current device for the null stream); the
+ * first call on a device looks its address up, making that device current for
+ * the lookup and then restoring the caller's.  Every call on one GPU shares
  * that GPU's array and it keeps the last call's contents, so the N calls of
  * one fold (index 0 .. N-1) must run in order and no other fold may run on
  * that GPU between them: folds that overlap in time on one GPU race.  Nothing

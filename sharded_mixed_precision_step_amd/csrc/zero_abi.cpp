@@ -728,7 +728,7 @@ int zero_accumulate_chunk_noalloc(const void* chunk, int64_t n, int32_t index, i
     }
     float* acc = nullptr;
     if (uses_acc) {
-        const hipError_t e = zero::fold_scratch(&acc);
+        const hipError_t e = zero::fold_scratch(static_cast<hipStream_t>(stream), &acc);
         if (e != hipSuccess) return hip_fail(e, "zero_accumulate_chunk_noalloc: scratch address");
     }
     zero::ChunkTable unused;

@@ -184,10 +184,10 @@ hipError_t launch_reduce_mean(const ChunkTable& chunks, int n_chunks, int64_t n,
                               const GradScalars& gs, uint16_t* mean16, int32_t* d_overflow,
                               double* d_sqnorm, hipStream_t stream);
 
-// The current device's address of the library's own fold accumulator
-// (ZERO_FOLD_SCRATCH_ELEMS fp32, zero_accumulate_chunk_noalloc), looked up
-// once per device.
-hipError_t fold_scratch(float** ptr);
+// The address of the library's own fold accumulator (ZERO_FOLD_SCRATCH_ELEMS
+// fp32, zero_accumulate_chunk_noalloc) on the device `stream` launches on,
+// looked up once per device.
+hipError_t fold_scratch(hipStream_t stream, float** ptr);
 
 // mode 0: acc = x; 1: acc += x; 2: mean16 = fp16((acc + x) / N); 3: mean16 = fp16(x)
 hipError_t launch_accumulate(const uint16_t* chunk, int64_t n, int mode, const GradScalars& gs,

@@ -823,12 +823,18 @@ constexpr int kMaxScratchDevices = 64;
 std::atomic<float*> g_scratch_ptr[kMaxScratchDevices];
 std::mutex g_scratch_mutex;
 
-// Compute units of the current device, asked of the runtime at each launch
-// that sizes a resident grid (the runtime answers from its own device
-// table; nothing is kept here).
-int current_cus() {
+// The device a launch on `stream` runs on: the stream's own device, or the
+// current device for the null stream.
+hipError_t stream_device(hipStream_t stream, int* dev) {
+    return stream ? hipStreamGetDevice(stream, dev) : hipGetDevice(dev);
+}
+
+// Compute units of the device `stream` launches on, asked of the runtime at
+// each launch that sizes a resident grid (the runtime answers from its own
+// device table; nothing is kept here).
+int stream_cus(hipStream_t stream) {
     int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
+    if (stream_device(stream, &dev) != hipSuccess ||
         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         v <= 0)
         return 256;
@@ -839,9 +845,9 @@ int current_cus() {
 int64_t step_grid(int64_t n) { return step_tiles(n); }
 
 // Check: a resident grid (grid-stride loop), no larger than the packs need.
-int64_t check_grid(int64_t n) {
+int64_t check_grid(int64_t n, hipStream_t stream) {
     const int64_t want = (n / kPack + kBlock - 1) / kBlock;
-    const int64_t resident = static_cast<int64_t>(kCheckBlocksPerCU) * current_cus();
+    const int64_t resident = static_cast<int64_t>(kCheckBlocksPerCU) * stream_cus(stream);
     const int64_t g = want < resident ? want : resident;
     return g < 1 ? 1 : g;
 }
@@ -913,7 +919,7 @@ hipError_t check_ctl_impl(const ChunkTable& chunks, int n_chunks, int64_t n,
 template <int NC>
 hipError_t check_impl(const ChunkTable& chunks, int n_chunks, int64_t n, const GradScalars& gs,
                       int32_t* d_overflow, double* d_sqnorm, hipStream_t stream) {
-    const int64_t grid = check_grid(n);
+    const int64_t grid = check_grid(n, stream);
     hipLaunchKernelGGL((overflow_check_kernel<NC, false>), dim3(static_cast<unsigned>(grid)),
                        dim3(kBlock), 0, stream, chunks, n_chunks, n, gs, d_overflow, d_sqnorm,
                        nullptr);
@@ -1003,9 +1009,9 @@ hipError_t launch_reduce_mean(const ChunkTable& chunks, int n_chunks, int64_t n,
 #undef ZERO_CASE
 }
 
-hipError_t fold_scratch(float** ptr) {
+hipError_t fold_scratch(hipStream_t stream, float** ptr) {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    hipError_t e = stream_device(stream, &dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
     float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
@@ -1013,8 +1019,17 @@ hipError_t fold_scratch(float** ptr) {
         std::lock_guard<std::mutex> lock(g_scratch_mutex);
         p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
         if (p == nullptr) {
+            // the symbol's address is per device: look it up with `dev`
+            // current, then give the caller's thread its device back
+            int prev = 0;
+            if ((e = hipGetDevice(&prev)) != hipSuccess) return e;
+            if (prev != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
             void* addr = nullptr;
             e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (prev != dev) {
+                const hipError_t back = hipSetDevice(prev);
+                if (e == hipSuccess) e = back;
+            }
             if (e != hipSuccess) return e;
             if (addr == nullptr) return hipErrorInvalidSymbol;
             p = static_cast<float*>(addr);

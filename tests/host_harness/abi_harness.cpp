@@ -160,7 +160,7 @@ hipError_t launch_fold_group(const ChunkTable&, int k, int64_t, bool read_acc, b
 }
 
 // the library's own accumulator, at a fake device address
-hipError_t fold_scratch(float** ptr) {
+hipError_t fold_scratch(hipStream_t, float** ptr) {
     ++g_scratch_lookups;
     *ptr = static_cast<float*>(fake(0x600000000000ull));
     return hipSuccess;
