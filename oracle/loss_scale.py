@@ -12,8 +12,11 @@ after ``growth_interval`` clean steps in a row the scale is multiplied by the
 growth factor (2) up to a ceiling.  The scale is an fp32 value.
 
 Pins: the halving on overflow and the untouched state are fixed by the
-overflow workload; growth, floor and ceiling are parity unpinned beyond the
-closed form of this state machine on forced flag sequences.
+overflow workload.  The growth rule and the restart of the clean run are
+checked against torch's GradScaler on forced sequences; that is a library
+with the same reading, not the pages, so growth stays a reading.  The floor
+and ceiling are parity unpinned beyond the closed form of this state machine
+on forced flag sequences.
 """
 from __future__ import annotations
 

@@ -513,6 +513,35 @@ def pin_scaler():
     assert s.scale == 2.0 and s.good_steps == 1
 
 
+def pin_scaler_grad_scaler():
+    """The reading of the scaler is the usual dynamic loss scaling, which
+    torch's GradScaler (torch.amp, on the CPU) implements: driven by the same
+    forced sequences of clean and overflowing steps (an inf gradient forces
+    the overflow), it skips the same steps and walks the same scales and
+    clean-step counts, for growth intervals 1, 2, 3 and 7, with the floor and
+    ceiling out of reach."""
+    import torch
+    rng = np.random.default_rng(7)
+    for interval in (1, 2, 3, 7):
+        flags = rng.random(60) < 0.3
+        ref = torch.amp.GradScaler("cpu", init_scale=1024.0, growth_factor=2.0,
+                                   backoff_factor=0.5, growth_interval=interval)
+        p = torch.nn.Parameter(torch.zeros(4))
+        opt = torch.optim.SGD([p], lr=1.0)
+        s = ls.ScalerState(scale=1024.0, growth_interval=interval, min_scale=2.0 ** -100,
+                           max_scale=2.0 ** 100)
+        for k, flag in enumerate(flags):
+            ref.scale(torch.ones(()))
+            before = p.detach().clone()
+            p.grad = torch.full((4,), float("inf") if flag else 1.0)
+            ref.step(opt)
+            ref.update()
+            skipped = torch.equal(before, p.detach())
+            assert ls.update_loss_scale(s, bool(flag)) == skipped, (interval, k)
+            assert s.scale == ref.get_scale(), (interval, k, s.scale, ref.get_scale())
+            assert s.good_steps == ref._get_growth_tracker(), (interval, k)
+
+
 def pin_flatten_layouts():
     for case in _golden("flatten_layouts.json")["cases"]:
         got = fl.bucket_layout(case["numels"], case["align"], case["pad_multiple"])

@@ -100,6 +100,16 @@ def _scaler_no_reset(s, overflow):
     return _orig_scaler(s, overflow)
 
 
+def _scaler_grows_late(s, overflow):
+    if overflow:
+        return _orig_scaler(s, overflow)
+    s.good_steps += 1
+    if s.good_steps > s.growth_interval:
+        s.scale = float(min(F32(s.scale) * F32(s.growth_factor), F32(s.max_scale)))
+        s.good_steps = 0
+    return False
+
+
 def _layout_unaligned(numels, align, pad_multiple):
     offs, end = [], 0
     for k in numels:
@@ -133,6 +143,7 @@ MUTATIONS = {
                            lambda g, start=0.0: float(np.sum(np.square(g.astype(np.float64))))),
     "scaler_grows_on_overflow": (ls, "update_loss_scale", _scaler_grow_on_overflow),
     "scaler_keeps_clean_run": (ls, "update_loss_scale", _scaler_no_reset),
+    "scaler_grows_one_step_late": (ls, "update_loss_scale", _scaler_grows_late),
     "layout_unaligned_starts": (fl, "bucket_layout", _layout_unaligned),
     "layout_no_padding": (fl, "bucket_layout", _layout_no_pad),
 }
