@@ -2,8 +2,8 @@
 zero_accumulate_chunk with a caller-owned accumulator: the same fp16 mean,
 bit for bit, over two folds in a row on one GPU, the second over fewer
 elements than the first (the library's accumulator keeps the first fold's
-contents, which the second must not see), and for a one-replica fold.  The
-calls go through the C ABI."""
+contents, which the second must not see), for a one-replica fold, and in a
+HIP graph replayed with new contents.  The calls go through the C ABI."""
 import ctypes
 
 import numpy as np
@@ -71,3 +71,37 @@ def test_noalloc_single_replica_and_refusals():
     with pytest.raises(zs.ZeroStepError) as e:
         zs.zero_accumulate_chunk_noalloc(big, 0, 2, None)
     assert e.value.code == zs.ZERO_ERANGE
+
+
+def test_noalloc_fold_replays_in_a_hip_graph():
+    """Code under HIP graph capture is among the callers the allocation-free
+    fold is for: the N calls of one fold captured once and replayed three
+    times, the chunks' contents redrawn eagerly between replays (with device
+    synchronisations and unrelated eager work in between), every replay's
+    fp16 mean equal, bit for bit, to the fold with an accumulator of the same
+    contents."""
+    dev = device()
+    n, N = 70_001, 4
+    chunks = _chunks(n, N, 300, dev)
+    got = torch.empty(n, dtype=torch.float16, device=dev)
+    want = torch.empty(n, dtype=torch.float16, device=dev)
+    _fold_noalloc(chunks, got)          # the device's accumulator looked up before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    print(f"case: allocation-free fold n={n} N={N} captured in a HIP graph", flush=True)
+    with torch.cuda.graph(graph):
+        _fold_noalloc(chunks, got)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for c, f in zip(chunks, _chunks(n, N, 301 + r, dev)):
+            c.copy_(f)
+        got.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device=dev).sum()      # unrelated eager work
+        _fold_with_acc(chunks, want)
+        torch.cuda.synchronize()
+        print(f"case: allocation-free fold, graph replay {r}", flush=True)
+        assert torch.isfinite(junk)
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
