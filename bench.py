@@ -11,19 +11,23 @@ update (replica sum, mean, unscale, inf/NaN flag, squared norm, moments,
 fp32 master, fp16 params) from the current copy of the state into the other
 copy; then decide on the device (skip, loss-scale move, t, and commit of the
 written copy if the step is clean).  Nothing is read back between steps.
-The host-decided single pass (flag read-back, host loss scale, swap) is
-timed afterwards and reported under "extra".  The two-pass form (overflow check, then the in-place update) and
-the page-literal split (the gradient mean stored as fp16, then the update
-from it) are timed afterwards on the same state and reported under "extra",
-and so is the step's traffic twin (the same loads and stores with XORs for
-arithmetic), whose rate is the ceiling of the step's access pattern on the
-device at hand.
+
+Timed afterwards on the same state and reported under "extra": the
+host-decided single pass (flag read-back, host loss scale, swap); the
+two-pass form (overflow check, then the in-place update), host- and
+device-decided; the page-literal split (the gradient mean stored as fp16,
+then the update from it) and the arrival folds; the step's traffic twin (the
+same loads and stores with XORs for arithmetic); plain read, write, copy
+and 2:1 and 3:1 streams on the same device; one bucket flatten; and the tiny
+workload's launch-bound step, eager and in HIP graphs.
 
 Before timing, the shard's 16 arrays go through the placement search of
-sharded_mixed_precision_step_amd.placement (each array re-allocated and kept
-where the step runs faster; contents unchanged), as a training run would do
-once at start-up.  `extra.placement` gives the two-direction step time before
-and after; `--no-placement` times the arrays where torch put them.
+sharded_mixed_precision_step_amd.placement (whole new sets of the arrays,
+each behind random spacer allocations, timed in turn; the fastest set is
+kept, contents unchanged), as a training run would do once at start-up.
+`extra.placement` gives the two-direction step time before and after, and
+the fused step is also timed where torch first put the arrays;
+`--no-placement` skips the search.
 
 Prints one JSON line.  `value` is params/s of the whole step.  `roofline`
 rates the fused update kernel, the dominant one, by its algorithmic bytes
