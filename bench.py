@@ -489,11 +489,34 @@ def bench_zero2(args, dev):
           (("device_step", device_step), ("device_streamed", device_streamed),
            ("device_streamed_2s", device_streamed_2s),
            ("multi_bucket", multi), ("per_bucket", per_bucket), ("whole_shard", whole))}
+    # the table update of the whole step alone (its launches between begin
+    # and decide), timed with HIP events on the launch stream
+    events = []
+    for k in range(args.steps + 2):
+        stepper._rebase()
+        zs.zero_control_begin(ctl, stepper.hp, stream=stream)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        zs.zero_shard_step_buckets_ctl(table, copies, stepper.hp, ctl, stream=stream)
+        e[1].record(stream)
+        zs.zero_control_decide(ctl, 0.0, True, stream=stream)
+        stepper.since_base += 1
+        if k >= 2:
+            events.append(e)
+    torch.cuda.synchronize()
+    update_ms = sum(a.elapsed_time(b) for a, b in events) / len(events)
     for c in (ctl, ctl_s, ctl_2s):
         assert zs.control_read(c).error == 0
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_buckets(w, arrivals, cur, (0, 40, 80, 120, 159), piece=1 << 20)
+        log(f"bench: cpu oracle {cpu['value']:.3e} params/s on {cpu['cores']} threads "
+            f"({cpu['seconds']:.1f} s for {cpu['params']} params)")
     step_bytes = w.bytes_per_param_step() * w.n
+    update_gbps = step_bytes / (update_ms * 1e-3) / 1e9
     log("bench: " + ", ".join(f"{k} {v:.3f} ms" for k, v in ms.items()) +
-        f", flatten {flat_ms:.3f} ms (one batch call), {flat_each_ms:.3f} ms (a call per bucket)")
+        f", table update {update_ms:.3f} ms (events), flatten {flat_ms:.3f} ms (one batch "
+        f"call), {flat_each_ms:.3f} ms (a call per bucket)")
     out_line = {
         "metric": METRIC,
         "value": w.n / (ms["device_step"] * 1e-3),
@@ -510,7 +533,15 @@ def bench_zero2(args, dev):
         "config": {"workload": w.name, "buckets": len(plan), "shard_params": w.n,
                    "replicas": N, "rank": r, "bytes_per_param_fused_step":
                    w.bytes_per_param_step()},
+        "roofline": {"bound": "hbm", "achieved": update_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": update_gbps / HBM_PEAK_GBPS, "traffic": None},
+        "cpu_baseline": cpu,
         "extra": {
+            "path": "single pass under the device control block over the bucket table: "
+                    "zero_control_begin, zero_shard_step_buckets_ctl (5 launches), "
+                    "zero_control_decide",
+            "table_update_ms": update_ms,
+            "table_update_gbps": update_gbps,
             **{f"{k}_ms": v for k, v in ms.items()},
             **{f"{k}_gbps": step_bytes / (v * 1e-3) / 1e9 for k, v in ms.items()},
             "flatten_own_buckets_ms": flat_ms,
@@ -934,43 +965,42 @@ def bench_replica_sweep(args, dev):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_buckets(w, items, state, sampled):
-    """The CPU oracle as it stands on whole buckets of a streamed shard (host
-    copies of their device chunks and state slices), in 2^22-param slices
-    over a thread pool, one bucket at a time."""
+def cpu_baseline_buckets(w, items, state, sampled, piece: int = 1 << 22):
+    """The CPU oracle as it stands on whole buckets of a shard (host copies of
+    their device chunks and state slices), in slices of `piece` params over
+    one thread pool for all the sampled buckets together."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle.zero_step as ozs
 
-    piece = 1 << 22
     threads = oracle_threads()
-    seconds, params = 0.0, 0
+    work, params = [], 0
     for b in sampled:
         chunks, off = items[b]
         nb = chunks[0].numel()
         ch = [c.cpu().numpy() for c in chunks]
         stt = [t[off:off + nb].cpu().numpy() for t in state]
-
-        def run(k):
-            sl = slice(k * piece, min((k + 1) * piece, nb))
-            return ozs.shard_step([c[sl] for c in ch], *(t[sl] for t in stt), w.hyper,
-                                  w.loss_scale)
-
-        t0 = time.perf_counter()
-        with ThreadPoolExecutor(threads) as ex:
-            results = list(ex.map(run, range((nb + piece - 1) // piece)))
-        seconds += time.perf_counter() - t0
+        work += [(ch, stt, slice(k, min(k + piece, nb))) for k in range(0, nb, piece)]
         params += nb
-        assert not any(r.overflow for r in results)
-        del ch, stt, results
+
+    def run(item):
+        ch, stt, sl = item
+        return ozs.shard_step([c[sl] for c in ch], *(t[sl] for t in stt), w.hyper, w.loss_scale)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        results = list(ex.map(run, work))
+    seconds = time.perf_counter() - t0
+    assert not any(r.overflow for r in results)
+    del work, results
     rate = params / seconds
     return {"value": rate, "unit": "params/s", "cores": threads, "kind": "oracle",
             **host_cpus(), "seconds": seconds, "params": params,
             "extrapolated_whole_shard_seconds": w.n / rate,
             "sample": (f"buckets {', '.join(map(str, sampled))} of the {w.name} shard "
-                       f"({params} params, N={w.n_replicas} replicas, 2^22-param slices): "
-                       f"overflow check and AdamW update; the whole-shard time is "
-                       f"extrapolated at this rate")}
+                       f"({params} params, N={w.n_replicas} replicas, slices of {piece} "
+                       f"params over one thread pool): overflow check and AdamW update; the "
+                       f"whole-shard time is extrapolated at this rate")}
 
 
 def fused_step_median(zs, chunks, cur, nxt, w, stream, reps: int = 9) -> float:
