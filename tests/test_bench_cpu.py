@@ -59,6 +59,19 @@ def test_committed_counter_summary_matches_the_sources():
     assert bench.read_traffic(_build.kernel_digest(), 1003750000) is not None
 
 
+def test_every_committed_counter_summary_was_taken_on_these_kernels():
+    """Each hardware-counter summary under profiles/ records the digest of
+    the kernel sources it was taken on, and that is the digest of the
+    sources as they are."""
+    import glob
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_pmc.txt")))
+    assert paths
+    digest = _build.kernel_digest()
+    for path in paths:
+        m = re.search(r"^kernel_digest_sha256:\s*([0-9a-f]+)", open(path).read(), re.M)
+        assert m and m.group(1) == digest, os.path.basename(path)
+
+
 def test_digest_ignores_comments_but_not_code():
     a = "int x = 1; // one\n/* block */ int y = 2;"
     b = "int x = 1;   /* other words */\nint y = 2; // two"
