@@ -369,6 +369,46 @@ def test_graph_of_one_step_replays_like_eager_calls():
                 assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
+def test_graph_of_clipped_two_pass_steps_replays_like_eager_calls():
+    """The two-pass flow with clipping (begin, check, decide with the clip
+    factor, update in place) captured once in a HIP graph and replayed four
+    times, with eager work and synchronisations between replays: after every
+    replay the state and the whole control block equal those of the same
+    steps run eagerly, bit for bit (this flow's norm is reduced in a fixed
+    order)."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=917)
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+
+    def fresh():
+        a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+        ctl = zs.control_new(_scaler()[0], w.hyper.step, dev)
+        return a, ctl, zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+
+    g_state, g_ctl, g_st = fresh()
+    e_state, e_ctl, e_st = fresh()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_st.two_pass(chunks, *g_state, max_grad_norm=2e-3)
+    torch.cuda.synchronize()
+    assert zs.control_read(g_ctl).step == w.hyper.step       # capture runs nothing
+    for r in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        e_st.two_pass(chunks, *e_state, max_grad_norm=2e-3)
+        junk = torch.randn(1 << 20, device=dev).sum()      # unrelated eager work
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        gc, ec = zs.control_read(g_ctl), zs.control_read(e_ctl)
+        print(f"case: two-pass graph replay {r}: t={gc.step} clip={gc.clip_coef}", flush=True)
+        assert bytes(gc) == bytes(ec)
+        assert gc.step == w.hyper.step + r + 1 and gc.clip_coef < 1.0
+        for x, y in zip(g_state, e_state):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
 def test_bucket_table_single_pass_matches_oracle():
     """ZeRO-2 slices (ragged, tiling the shard) stepped by one call per step
     under the control block: the skip decision covers every slice, and the
