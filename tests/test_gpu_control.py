@@ -409,6 +409,62 @@ def test_graph_of_clipped_two_pass_steps_replays_like_eager_calls():
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
+@pytest.mark.parametrize("flow", ["bucket_table", "two_pass_buckets"])
+def test_graph_of_a_bucketed_step_replays_like_eager_calls(flow):
+    """A ZeRO-2 step over ragged bucket slices, captured once in a HIP graph
+    and replayed four times with eager work in between: the single pass over
+    a bucket table (its update launches between begin and decide), or the
+    two-pass flow over the buckets (a check per bucket, the decision with a
+    clip factor, an in-place update per bucket).  After every replay the
+    state equals that of the eager steps bit for bit, and so does the control
+    block (the squared norm to 1e-12 where per-block atomics sum it)."""
+    dev = device()
+    w = _workload()
+    h = wl.host_shard(w, n=n, offset_seed=918)
+    chunks = [torch.from_numpy(c).to(dev) for c in h["chunks"]]
+    sizes = [8 * 1000, 8 * 1001, n - 8 * 2001]
+    offs = [0, 8 * 1000, 8 * 2001]
+    buckets = [([c[o:o + sz] for c in chunks], o) for o, sz in zip(offs, sizes)]
+    table = zs.BucketSlices(buckets)
+
+    def fresh():
+        a = tuple(torch.from_numpy(h[k]).to(dev) for k in ("master", "m", "v", "p16"))
+        copies = (a, tuple(torch.full_like(x, float("nan")) for x in a))
+        ctl = zs.control_new(_scaler()[0], w.hyper.step, dev)
+        return copies, ctl, zs.DeviceStepper(ctl, zs.adamw_params(w.hyper))
+
+    def step(st, copies):
+        if flow == "bucket_table":
+            st.single_pass_buckets(table, copies)
+        else:
+            st.two_pass_buckets(buckets, *copies[0], max_grad_norm=2e-3)
+
+    g_copies, g_ctl, g_st = fresh()
+    e_copies, e_ctl, e_st = fresh()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_st, g_copies)
+    torch.cuda.synchronize()
+    assert zs.control_read(g_ctl).step == w.hyper.step       # capture runs nothing
+    for r in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_st, e_copies)
+        junk = torch.randn(1 << 20, device=dev).sum()      # unrelated eager work
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        gc, ec = zs.control_read(g_ctl), zs.control_read(e_ctl)
+        print(f"case: {flow} graph replay {r}: t={gc.step} cur={gc.cur}", flush=True)
+        for name in _KEPT + ("skip", "overflow", "error", "clip_coef", "step_used"):
+            assert getattr(gc, name) == getattr(ec, name), (r, name)
+        assert abs(gc.sqnorm - ec.sqnorm) <= 1e-12 * ec.sqnorm
+        assert gc.step == w.hyper.step + r + 1
+        for cp_g, cp_e in zip(g_copies, e_copies):
+            for x, y in zip(cp_g, cp_e):
+                assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
 def test_bucket_table_single_pass_matches_oracle():
     """ZeRO-2 slices (ragged, tiling the shard) stepped by one call per step
     under the control block: the skip decision covers every slice, and the
