@@ -1,6 +1,6 @@
 """Placement search for a shard's long-lived device arrays.
 
-The fused step streams 2N + 6 arrays at once (N gradient chunks, three fp32
+The fused step streams N + 7 arrays at once (N gradient chunks, three fp32
 state arrays read and three written, the fp16 params).  On MI355X its
 bandwidth depends on where those arrays sit in physical HBM, not only on
 their virtual layout.  At the Llama-3-8B shard (n = 1,003,750,000, N = 8) the
@@ -183,7 +183,7 @@ def place_shard(chunks: Sequence[torch.Tensor], copies, hp, loss_scale: float, *
 
     chunks: the N fp16 gradient-chunk buffers; copies: two (master, exp_avg,
     exp_avg_sq, param_fp16) tuples, copy 0 holding the state.  Each trial
-    allocates a complete new set of the 2N + 8 arrays, with spacer
+    allocates a complete new set of the N + 8 arrays, with spacer
     allocations of random size (up to `max_spacer` bytes) before each array
     so that the set lands somewhere new, copies the contents over, and times
     the step in both directions.  The set with the lowest time is kept (a
