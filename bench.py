@@ -300,6 +300,7 @@ def main():
         "step_gbps": k1_bytes / (ms_per_step * 1e-3) / 1e9,
         "skipped_steps": skipped,
         "placement": placed if placed is not None else "allocation as made (--no-placement)",
+        "fused_step_counter_gbps": (traffic / (k1_ms * 1e-3) / 1e9) if traffic else None,
         "unplaced_fused_step_median_ms": unplaced,
         "unplaced_fused_step_pct_peak":
             100 * w.bytes_per_param_step() * n / (unplaced * 1e-3) / 1e9 / HBM_PEAK_GBPS,
