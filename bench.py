@@ -125,20 +125,18 @@ def host_cpus() -> dict:
 
 def cpu_baseline(dev_shard, w, slices: int):
     """The CPU oracle as it stands, on the first `slices` x 2^22 params of the
-    shard (host copies of the device inputs), over a thread pool.  A shard
-    too small to give every thread a few 2^22-param slices is cut into
-    slices of at least 2^16 params instead."""
+    shard (host copies of the device inputs), over a thread pool."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle.zero_step as ozs
 
-    threads = oracle_threads()
-    total = min(slices << 22, w.n) if slices > 0 else w.n
-    piece = min(1 << 22, max(1 << 16, -(-total // (4 * threads))))
+    piece = 1 << 22
+    total = min(slices * piece, w.n) if slices > 0 else w.n
     host = dict(chunks=[c[:total].cpu().numpy() for c in dev_shard["chunks"]],
                 master=dev_shard["master"][:total].cpu().numpy(),
                 m=dev_shard["m"][:total].cpu().numpy(), v=dev_shard["v"][:total].cpu().numpy(),
                 p16=dev_shard["p16"][:total].cpu().numpy())
+    threads = oracle_threads()
 
     def run(k):
         sl = slice(k * piece, min((k + 1) * piece, total))
@@ -162,10 +160,9 @@ def cpu_baseline(dev_shard, w, slices: int):
     return {"value": total / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
             **host_cpus(), "seconds": dt,
             "single_core_value": n1 / dt1,
-            "single_core_sample": f"the first {n1} params ({single} slices of {piece}), "
-                                  f"one thread",
+            "single_core_sample": f"the first {n1} params ({single} slices of 2^22), one thread",
             "sample": (f"{'whole' if total == w.n else 'first ' + str(total) + ' params of the'} "
-                       f"{w.name} shard ({total} params, {count} slices of {piece}, "
+                       f"{w.name} shard ({total} params, {count} slices of 2^22, "
                        f"N={w.n_replicas} replicas): overflow check and AdamW update")}
 
 
