@@ -157,8 +157,9 @@ def cpu_baseline(dev_shard, w, slices: int):
         run(k)
     dt1 = time.perf_counter() - t0
     n1 = min(single * piece, total)
-    return {"value": total / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
-            **host_cpus(), "seconds": dt,
+    # a pool of `threads` on `count` slices keeps at most `count` of them busy
+    return {"value": total / dt, "unit": "params/s", "cores": min(threads, count),
+            "kind": "oracle", **host_cpus(), "pool_threads": threads, "seconds": dt,
             "single_core_value": n1 / dt1,
             "single_core_sample": f"the first {n1} params ({single} slices of 2^22), one thread",
             "sample": (f"{'whole' if total == w.n else 'first ' + str(total) + ' params of the'} "
