@@ -123,14 +123,18 @@ def host_cpus() -> dict:
                           f"GPU's share of the host"}
 
 
-def cpu_baseline(dev_shard, w, slices: int):
+ORACLE_PIECE = 1 << 22
+
+
+def cpu_baseline(dev_shard, w, slices: int, keep: list | None = None):
     """The CPU oracle as it stands, on the first `slices` x 2^22 params of the
-    shard (host copies of the device inputs), over a thread pool."""
+    shard (host copies of the device inputs), over a thread pool.  With
+    `keep`, the oracle's result for each 2^22-param slice is appended to it."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle.zero_step as ozs
 
-    piece = 1 << 22
+    piece = ORACLE_PIECE
     total = min(slices * piece, w.n) if slices > 0 else w.n
     host = dict(chunks=[c[:total].cpu().numpy() for c in dev_shard["chunks"]],
                 master=dev_shard["master"][:total].cpu().numpy(),
@@ -157,6 +161,8 @@ def cpu_baseline(dev_shard, w, slices: int):
         run(k)
     dt1 = time.perf_counter() - t0
     n1 = min(single * piece, total)
+    if keep is not None:
+        keep.extend(results)
     # a pool of `threads` on `count` slices keeps at most `count` of them busy
     return {"value": total / dt, "unit": "params/s", "cores": min(threads, count),
             "kind": "oracle", **host_cpus(), "pool_threads": threads, "seconds": dt,
@@ -165,6 +171,52 @@ def cpu_baseline(dev_shard, w, slices: int):
             "sample": (f"{'whole' if total == w.n else 'first ' + str(total) + ' params of the'} "
                        f"{w.name} shard ({total} params, {count} slices of 2^22, "
                        f"N={w.n_replicas} replicas): overflow check and AdamW update")}
+
+
+def ulp_line(x, sbits):
+    """IEEE floats (sign and magnitude) mapped to integers in value order, one
+    step per representable value: the distance of two maps is the ulp
+    distance of the floats (+0 and -0 map to 0)."""
+    import numpy as np
+    i = x.view(sbits).astype(np.int64)
+    mag = i & ((1 << (8 * x.itemsize - 1)) - 1)
+    return np.where(i < 0, -mag, mag)
+
+
+def parity_of_step(zs, d, spare, w, results, stream) -> dict:
+    """One fused step on the device (zero_shard_step_out) from the shard's
+    inputs into the spare copy, against the oracle's results for the same
+    inputs (kept from the CPU baseline, 2^22-param slices from the start of
+    the shard): bit equality per array, and the largest distance in fp32 ulps
+    (master, m, v) and fp16 ulps (params) where the bits differ."""
+    import numpy as np
+    import torch
+
+    hp = zs.adamw_params(w.hyper)
+    flag = torch.zeros(1, dtype=torch.int32, device=spare[0].device)
+    zs.zero_shard_step_out(d["chunks"], w.loss_scale, d["master"], d["m"], d["v"], *spare, hp,
+                           flag, None, stream=stream)
+    torch.cuda.synchronize()
+
+    worst = {"master": 0, "m": 0, "v": 0, "p16": 0}
+    elements = 0
+    for k, r in enumerate(results):
+        a = k * ORACLE_PIECE
+        b = a + r.master.size
+        for name, t, ref in zip(("master", "m", "v", "p16"), spare,
+                                (r.master, r.m, r.v, r.p16)):
+            got = t[a:b].cpu().numpy()
+            bits = np.uint16 if ref.dtype == np.float16 else np.uint32
+            if not np.array_equal(got.view(bits), ref.view(bits)):
+                sbits = np.int16 if ref.dtype == np.float16 else np.int32
+                d_ulp = np.abs(ulp_line(got, sbits) - ulp_line(ref, sbits))
+                worst[name] = max(worst[name], int(d_ulp.max()))
+        elements = b
+    return {"elements": elements, "overflow": int(flag.item()),
+            "bit_exact": all(v == 0 for v in worst.values()),
+            "max_ulp_master": worst["master"], "max_ulp_m": worst["m"],
+            "max_ulp_v": worst["v"], "max_ulp_p16_fp16": worst["p16"],
+            "against": "the oracle's step of the same inputs (the CPU baseline's results)"}
 
 
 def main():
@@ -201,13 +253,18 @@ def main():
     log(f"bench: inputs drawn on device in {time.perf_counter() - t0:.1f} s")
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(d, w, args.cpu_sample_slices)
-        log(f"bench: cpu oracle {cpu['value']:.3e} params/s on {cpu['cores']} threads "
-            f"({cpu['seconds']:.1f} s)")
-
     stream = torch.cuda.current_stream()
     spare = tuple(torch.empty_like(d[k]) for k in ("master", "m", "v", "p16"))
+    parity = None
+    if not args.no_cpu_baseline:
+        oracle_results = []
+        cpu = cpu_baseline(d, w, args.cpu_sample_slices, keep=oracle_results)
+        log(f"bench: cpu oracle {cpu['value']:.3e} params/s on {cpu['cores']} threads "
+            f"({cpu['seconds']:.1f} s)")
+        parity = parity_of_step(zs, d, spare, w, oracle_results, stream)
+        del oracle_results
+        log(f"bench: one device step against the oracle over {parity['elements']} params: "
+            f"bit-exact {parity['bit_exact']}")
     unplaced = fused_step_median(zs, d["chunks"], (d["master"], d["m"], d["v"], d["p16"]),
                                  spare, w, stream)
     log(f"bench: fused step where torch allocated the arrays: median {unplaced:.3f} ms")
@@ -342,6 +399,7 @@ def main():
                      "unit": "GB/s", "frac": k1_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "parity": parity,
         "extra": extra,
     }
     print(json.dumps(out), flush=True)

@@ -72,6 +72,22 @@ def test_every_committed_counter_summary_was_taken_on_these_kernels():
         assert m and m.group(1) == digest, os.path.basename(path)
 
 
+def test_ulp_line_counts_representable_values():
+    import numpy as np
+    one, m1 = np.float32(1.0), np.float32(-1.0)
+    a = np.array([one, m1, 0.0, -0.0, one, 2.0], np.float32)
+    b = np.array([np.nextafter(one, np.float32(2)), np.nextafter(m1, np.float32(0)),
+                  np.float32(1e-45), np.float32(-1e-45), one, np.nextafter(np.float32(2), 0,
+                                                                             dtype=np.float32)],
+                 np.float32)
+    d = np.abs(bench.ulp_line(a, np.int32) - bench.ulp_line(b, np.int32))
+    assert list(d) == [1, 1, 1, 1, 0, 1]
+    assert bench.ulp_line(np.array([0.0, -0.0], np.float32), np.int32).tolist() == [0, 0]
+    h = np.array([1.0, -2.0, 65504.0], np.float16)
+    g = np.array([np.nextafter(np.float16(1), np.float16(2)), -2.0, np.inf], np.float16)
+    assert list(np.abs(bench.ulp_line(h, np.int16) - bench.ulp_line(g, np.int16))) == [1, 0, 1]
+
+
 def test_digest_ignores_comments_but_not_code():
     a = "int x = 1; // one\n/* block */ int y = 2;"
     b = "int x = 1;   /* other words */\nint y = 2; // two"
