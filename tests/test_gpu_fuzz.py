@@ -97,3 +97,102 @@ def test_random_configuration_matches_oracle(case):
         for name, x, ref in zip(("master", "m", "v", "p16"), d,
                                 (want.master, want.m, want.v, want.p16)):
             assert _same(x, ref), name
+
+
+GUARD = 0x7E01          # a NaN pattern no flatten writes
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_flatten_batch_matches_oracle(case):
+    """A batch of 1-9 buckets of 0-12 tensors each (0-30,000 elements, some
+    sources only 2-byte aligned), with align in 1..1024 and pad_multiple
+    0 or a multiple of align: each bucket equals the oracle's flatten bit for
+    bit, and nothing past its padded end is written; one call per bucket
+    gives the same buckets."""
+    import oracle.flatten as ofl
+    dev = device()
+    rng = np.random.default_rng(8000 + case)
+    align = int(rng.integers(1, 1025))
+    pad = 0 if rng.random() < 0.25 else align * int(rng.integers(1, 17))
+    specs = [[rng.standard_normal(int(rng.integers(0, 30_001))).astype(np.float16)
+              for _ in range(int(rng.integers(0, 13)))] for _ in range(int(rng.integers(1, 10)))]
+    print(f"case: flatten fuzz {case}: {len(specs)} buckets align={align} pad={pad}", flush=True)
+    pairs, wants, singles = [], [], []
+    for ts in specs:
+        want, want_offs = ofl.flatten(ts, align, pad)
+        srcs = []
+        for t in ts:
+            flat = torch.from_numpy(t.view(np.int16)).to(dev)
+            if rng.random() < 0.4 and flat.numel():
+                big = torch.empty(flat.numel() + 1, dtype=torch.int16, device=dev)
+                big[1:].copy_(flat)
+                flat = big[1:]
+            srcs.append(flat.view(torch.float16))
+        bucket = torch.full((want.size + 64,), GUARD, dtype=torch.int16,
+                            device=dev).view(torch.float16)
+        single = torch.full_like(bucket, 0).view(torch.int16).fill_(GUARD).view(torch.float16)
+        pairs.append((srcs, bucket))
+        singles.append(single)
+        wants.append((want, want_offs))
+    offs = zs.zero_bucket_flatten_batch(pairs, align=align, pad_multiple=pad)
+    for (srcs, _), single in zip(pairs, singles):
+        zs.zero_bucket_flatten(srcs, single, align, pad)
+    torch.cuda.synchronize()
+    for b, ((_, bucket), single, (want, want_offs)) in enumerate(zip(pairs, singles, wants)):
+        assert offs[b] == want_offs, b
+        got = bucket.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got[:want.size], want.view(np.uint16)), b
+        assert np.all(got[want.size:] == GUARD), b
+        assert torch.equal(single.view(torch.int16), bucket.view(torch.int16)), b
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_bucket_table_matches_oracle(case):
+    """A shard tiled by 1-70 slices of random lengths (multiples of 8 apart,
+    the last ragged), N in 1..20, in the multi-bucket call and under the
+    control block: the state is the oracle's step of the whole shard, bit for
+    bit, and the flag is the oracle's."""
+    dev = device()
+    rng = np.random.default_rng(9000 + case)
+    N = int(rng.integers(1, 21))
+    k = int(rng.integers(1, 71))
+    sizes = [8 * int(x) for x in rng.integers(0, 700, k - 1)]
+    sizes.append(int(rng.integers(1, 5000)))
+    n = sum(sizes)
+    S = float(2.0 ** int(rng.integers(0, 17)))
+    hyper = wl.AdamWHyper(step=int(rng.integers(1, 5000)))
+    chunks_h = [(rng.standard_normal(n, dtype=np.float32) * np.float32(1e-4 * S))
+                .astype(np.float16) for _ in range(N)]
+    if rng.random() < 0.2:
+        chunks_h[int(rng.integers(0, N))][int(rng.integers(0, n))] = np.float16(np.nan)
+    master = rng.standard_normal(n, dtype=np.float32) * np.float32(0.02)
+    m = rng.standard_normal(n, dtype=np.float32) * np.float32(1e-4)
+    v = np.abs(rng.standard_normal(n, dtype=np.float32)) * np.float32(1e-8)
+    p16 = master.astype(np.float16)
+    print(f"case: bucket table fuzz {case}: {k} slices n={n} N={N} S={S}", flush=True)
+    want = ozs.shard_step(chunks_h, master, m, v, p16, hyper, S)
+    chunks = [torch.from_numpy(x).to(dev) for x in chunks_h]
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(int)
+    table = zs.BucketSlices([([c[o:o + sz] for c in chunks], int(o))
+                             for o, sz in zip(offs, sizes)])
+    state = (master, m, v, p16)
+    # host-pointer table call
+    a = tuple(torch.from_numpy(x).to(dev) for x in state)
+    b = tuple(torch.empty_like(x) for x in a)
+    fl, sq = flags(dev)
+    zs.zero_shard_step_buckets(table, S, *a[:3], *b, zs.adamw_params(hyper), fl, sq)
+    torch.cuda.synchronize()
+    assert int(fl.item()) == int(want.overflow)
+    if not want.overflow:
+        for name, x, ref in zip(("master", "m", "v", "p16"), b,
+                                (want.master, want.m, want.v, want.p16)):
+            assert _same(x, ref), name
+    # under the control block
+    ctl = zs.control_new(zs.LossScaler.create(scale=S), hyper.step, dev)
+    zs.DeviceStepper(ctl, zs.adamw_params(hyper)).single_pass_buckets(table, (a, b))
+    c = zs.control_read(ctl)
+    assert c.error == 0 and c.overflow == int(want.overflow)
+    got = (a, b)[c.cur]
+    for name, x, ref in zip(("master", "m", "v", "p16"), got,
+                            state if want.overflow else (want.master, want.m, want.v, want.p16)):
+        assert _same(x, ref), name
